@@ -1,0 +1,274 @@
+"""Benchmark of the NVFP4 dense MLP on one MI355X.
+
+A step is one whole MLP forward (quantize -> fused gate_up + SwiGLU + NVFP4
+re-quant -> down_proj) over one batch of synthetic input, with inputs and
+packed weights resident in HBM. The weights are rotated over several copies
+(>= 1 GB in total) so the 256 MB Infinity Cache cannot serve them, as the
+distinct weights of successive layers would not be cached either.
+
+Prints one JSON line. `value` is algorithmic bytes (decode workloads, GB/s)
+or algorithmic flops (prefill, TFLOP/s) per second of wall clock over the
+timed steps; `roofline` reports the dominant kernel (the fused gate_up
+kernel) timed with HIP events on the stream it runs on; `cpu_baseline` is
+the CPU oracle timed on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import nvfp4_quantized_dense_amd as nv  # noqa: E402
+import nvfp4_synth as synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense f16/bf16 MFMA
+NVFP4_BYTES = 0.5625           # per element: 4-bit code + 1/16 of a scale byte
+
+WORKLOADS = {
+    # name: (M, H, I, mode, outliers, n_seeds, default steps, default warmup)
+    "decode_w4a4": (1, 5120, 17408, "w4a4", True, 1000, 1000, 50),
+    "smallbatch_w4a4": (16, 7168, 18432, "w4a4", False, 64, 500, 50),
+    "prefill_w4a4": (8192, 7168, 18432, "w4a4", False, 2, 20, 3),
+    "w4a16": (16, 5120, 17408, "w4a16", False, 64, 500, 50),
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def bf16_tensor(bits: np.ndarray, dev):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def algorithmic(M, H, I, mode, out_bytes):
+    """Compulsory bytes and real flops of one forward, per kernel."""
+    w_gu = 2 * I * H * NVFP4_BYTES
+    w_d = H * I * NVFP4_BYTES
+    if mode == "w4a4":
+        quant = M * H * 2 + M * H * NVFP4_BYTES
+        fused = w_gu + M * H * NVFP4_BYTES + M * I * NVFP4_BYTES
+        down = w_d + M * I * NVFP4_BYTES + M * H * out_bytes
+    else:
+        quant = 0.0
+        fused = w_gu + M * H * 2 + M * I * 2
+        down = w_d + M * I * 2 + M * H * out_bytes
+    flops_fused = 2.0 * M * (2 * I) * H
+    flops_down = 2.0 * M * H * I
+    return dict(quant=quant, fused=fused, down=down, total=quant + fused + down,
+                flops_fused=flops_fused, flops=flops_fused + flops_down)
+
+
+def prepare_weights(H, I, dev, copies):
+    """fp32 synthetic weights -> GPU calibrate + quantize + repack (the library's
+    own one-time weight preparation), replicated `copies` times."""
+    out = []
+    gs = []
+    for tid, R, C, kind in [(synth.TENSOR_W_GATE_UP, 2 * I, H, nv.REPACK_SWIGLU),
+                            (synth.TENSOR_W_DOWN, H, I, nv.REPACK_PLAIN)]:
+        w = torch.from_numpy(synth.weights(0, R, C, tid)).to(dev)
+        g, g_inv = nv.nvfp4_calibrate(w)
+        c, s = nv.nvfp4_quantize(w, g_inv)
+        del w
+        p = nv.nvfp4_repack_weight(kind, c, s)
+        del c, s
+        out.append([p] + [p.clone() for _ in range(copies - 1)])
+        gs.append(g)
+    torch.cuda.synchronize()
+    return out[0], out[1], gs[0], gs[1]
+
+
+def cpu_baseline(M, H, I, mode, outliers, per_step_bytes, per_step_flops, budget_s, use_flops):
+    """The CPU oracle on a bounded sample of the workload's steps."""
+    import oracle
+    wgu = synth.weights(0, 2 * I, H, synth.TENSOR_W_GATE_UP)
+    g_gu, gi_gu = oracle.global_scale(wgu)
+    c_gu, s_gu = oracle.quantize(wgu, gi_gu)
+    del wgu
+    wd = synth.weights(0, H, I, synth.TENSOR_W_DOWN)
+    g_d, gi_d = oracle.global_scale(wd)
+    c_d, s_d = oracle.quantize(wd, gi_d)
+    del wd
+    rows = min(M, 8)
+    x0 = synth.activations(0, M, H, outliers=outliers)[:rows]
+    if mode == "w4a4":
+        g1, g1_inv = oracle.global_scale(x0)
+        a_gu = oracle.alpha(g1, g_gu)
+        h = oracle.swiglu(oracle.gemm_w4a4(*oracle.quantize(x0, g1_inv), c_gu, s_gu, a_gu))
+        g2, g2_inv = oracle.global_scale(h)
+        a_d = oracle.alpha(g2, g_d)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        x = synth.activations(n, M, H, outliers=outliers)[:rows]
+        if mode == "w4a4":
+            oracle.mlp_w4a4(x, c_gu, s_gu, a_gu, c_d, s_d, a_d, g1_inv, g2_inv)
+        else:
+            oracle.mlp_w4a16(x, c_gu, s_gu, g_gu, c_d, s_d, g_d)
+        n += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    frac = rows / M  # the oracle ran `rows` of the M tokens per step
+    step_s = dt / n / frac
+    if use_flops:
+        value, unit = per_step_flops / step_s / 1e12, "TFLOP/s"
+    else:
+        value, unit = per_step_bytes / step_s / 1e9, "GB/s"
+    return {"value": value, "unit": unit, "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{n} steps of {rows} of {M} token rows each, full MLP forward, "
+                      f"{dt:.1f} s, scaled to whole steps"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--workload", default="decode_w4a4", choices=list(WORKLOADS))
+    ap.add_argument("--M", type=int, default=None, help="override the token count")
+    ap.add_argument("--copies", type=int, default=None, help="weight copies rotated (default >= 1 GB)")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--path", type=int, default=0, help="kernel class override (0 = auto)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path; see the sharding notes in DESIGN.md)")
+        sys.exit(2)
+
+    M, H, I, mode, outliers, n_seeds, d_steps, d_warm = WORKLOADS[args.workload]
+    if args.M is not None:
+        M = args.M
+        n_seeds = max(2, min(n_seeds, (1 << 22) // max(1, M * H)))
+    steps = args.steps if args.steps is not None else d_steps
+    warmup = args.warmup if args.warmup is not None else d_warm
+    dev = torch.device("cuda:0")
+    nv.set_path(args.path)
+    out_dtype = torch.bfloat16
+    alg = algorithmic(M, H, I, mode, 2)
+    weight_bytes = 3 * H * I * NVFP4_BYTES
+    copies = args.copies or max(1, int(np.ceil(1.0e9 / weight_bytes)))
+    prefill = M >= 256
+    log(f"[bench] workload {args.workload} M={M} H={H} I={I} mode={mode} copies={copies} "
+        f"steps={steps} warmup={warmup}")
+
+    t = time.perf_counter()
+    p_gu, p_d, g_gu, g_d = prepare_weights(H, I, dev, copies)
+    log(f"[bench] weights ready in {time.perf_counter() - t:.1f}s")
+    xs = [bf16_tensor(synth.activations(s, M, H, outliers=outliers), dev) for s in range(n_seeds)]
+
+    # Static activation scales, calibrated on the seed-0 input: g1 from x,
+    # g2 from the fused kernel's own fp32 h for that x.
+    ws = torch.empty(max(1, nv.mlp_workspace_bytes(0 if mode == "w4a4" else 1, M, H, I)),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty((M, H), dtype=out_dtype, device=dev)
+    if mode == "w4a4":
+        g1, g1_inv = nv.nvfp4_calibrate(xs[0])
+        a_gu = torch.tensor([np.float32(g1.item()) * np.float32(g_gu.item())], device=dev)
+        xq, xsc = nv.nvfp4_quantize(xs[0], g1_inv)
+        h = nv.gemm_swiglu(0, xq, xsc, p_gu[0], I, H, a_gu, h_dtype=torch.float32)
+        g2, g2_inv = nv.nvfp4_calibrate(h)
+        a_d = torch.tensor([np.float32(g2.item()) * np.float32(g_d.item())], device=dev)
+        del h
+        xq = torch.empty((M, H // 2), dtype=torch.uint8, device=dev)
+        xsc = torch.empty((M, H // 16), dtype=torch.uint8, device=dev)
+        hq = torch.empty((M, I // 2), dtype=torch.uint8, device=dev)
+        hsc = torch.empty((M, I // 16), dtype=torch.uint8, device=dev)
+    else:
+        a_gu, a_d = g_gu, g_d
+        hb = torch.empty((M, I), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+
+    def step(i, timed):
+        x = xs[i % n_seeds]
+        r = i % copies
+        if mode == "w4a4":
+            nv.nvfp4_quantize(x, g1_inv, xq, xsc, stream=stream)
+            if timed:
+                ev[i][0].record(stream)
+            nv.gemm_swiglu_nvfp4_quant(xq, xsc, p_gu[r], I, H, a_gu, g2_inv, hq, hsc, stream=stream)
+            if timed:
+                ev[i][1].record(stream)
+            nv.nvfp4_gemm(0, hq, hsc, p_d[r], H, I, a_d, out=out, stream=stream)
+        else:
+            if timed:
+                ev[i][0].record(stream)
+            nv.gemm_swiglu(1, x, None, p_gu[r], I, H, a_gu, h=hb, stream=stream)
+            if timed:
+                ev[i][1].record(stream)
+            nv.nvfp4_gemm(1, hb, None, p_d[r], H, I, a_d, out=out, stream=stream)
+
+    for i in range(warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+    log("[bench] warmup done")
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i, True)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    log(f"[bench] timed {steps} steps in {dt:.3f}s")
+
+    fused_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    ms_per_step = dt * 1e3 / steps
+    if prefill:
+        value = alg["flops"] / (ms_per_step * 1e-3) / 1e12
+        unit = "TFLOP/s"
+        achieved = alg["flops_fused"] / (fused_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / MFMA_F16_PEAK_TFLOPS, "traffic": None}
+    else:
+        value = alg["total"] / (ms_per_step * 1e-3) / 1e9
+        unit = "GB/s"
+        achieved = alg["fused"] / (fused_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": None}
+    roof["kernel"] = "gemm_swiglu_nvfp4_quant" if mode == "w4a4" else "gemm_swiglu(w4a16, bf16 h)"
+    roof["kernel_us"] = fused_ms * 1e3
+    roof["algorithmic_bytes"] = alg["fused"]
+    roof["algorithmic_flops"] = alg["flops_fused"]
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle")
+        cpu = cpu_baseline(M, H, I, mode, outliers, alg["total"], alg["flops"], args.cpu_budget, prefill)
+
+    res = {
+        "metric": "NVFP4 MLP TFLOPS + GB/s (% roofline), decode M=1..16 and prefill M=8192",
+        "value": value,
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16" if mode == "w4a4" else "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload} M={M} H={H} I={I}", "M": M, "hidden": H,
+                   "intermediate": I, "mode": mode, "seeds": n_seeds, "weight_copies": copies,
+                   "out_dtype": "bf16", "tflops": alg["flops"] / (ms_per_step * 1e-3) / 1e12,
+                   "gbs": alg["total"] / (ms_per_step * 1e-3) / 1e9},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,207 @@
+/*
+ * nvfp4.h -- C ABI of the MI355X (gfx950) NVFP4 dense-MLP library.
+ *
+ * The hot path of an NVFP4-quantized dense MLP in LLM inference:
+ *   activation quantize -> gate_up GEMM -> SiLU(gate) * up -> NVFP4
+ *   re-quantize -> down_proj GEMM,
+ * plus a W4A16 variant (bf16 activations against NVFP4 weights) and a
+ * one-time weight repack. The call sequence follows the fused MLP forward of
+ * sglang PR #26626 ("fuse NVFP4 gate_up_gemm + Swish + output quant", key
+ * source snippets: DeepseekV2MLP.forward) and the W4A16 dense path of the
+ * PR #35120 report ("add FlashInfer CuTe DSL NVFP4 W4A16 mode", key source
+ * snippets: fp4_gemm).
+ *
+ * Formats (all row-major, little-endian):
+ *   bf16      uint16 bit patterns.
+ *   NVFP4     codes  uint8 [rows, K/2]: two 4-bit E2M1 codes per byte, element
+ *                    2i in the low nibble; bit 3 of a code is the sign, bits
+ *                    0..2 index {0, 0.5, 1, 1.5, 2, 3, 4, 6}.
+ *             scales uint8 [rows, K/16]: one E4M3FN byte per 16 consecutive
+ *                    elements of a row (the pages' `float8_e4m3fn` view with
+ *                    K/16 scales per row, PR #35120 report, key source
+ *                    snippets, flashinfer_cutedsl.py).
+ *             value  = E2M1(code) * E4M3(scale) * g, with g the tensor's fp32
+ *                    global scale.
+ *   packed    an opaque weight buffer written by nvfp4_repack_weight; the same
+ *             bytes as codes + scales, permuted for the kernels' loads.
+ *
+ * Scalars g_inv, alpha, g2_inv are 1-element fp32 arrays in DEVICE memory
+ * (like `input_scale_inv` and `alpha` tensors on the pages), so a call never
+ * synchronizes with the host.
+ *
+ * Ownership and execution: the caller allocates every buffer (inputs,
+ * outputs, packed weights sized by nvfp4_packed_bytes, workspace sized by
+ * mlp_workspace_bytes) and keeps it alive until the work on `stream` has
+ * finished. Calls are asynchronous on `stream` (a hipStream_t; NULL is the
+ * default stream). The library never allocates, frees, synchronizes or reads
+ * the environment. Device pointers must be 16-byte aligned. Calls that share
+ * no output buffer may run concurrently on different streams.
+ *
+ * Errors: every entry point returns NVFP4_OK or a negative code and leaves a
+ * thread-local message for nvfp4_last_error(). Argument checks come before
+ * any HIP call, so a rejected call has no effect on the device. There is no
+ * fallback path: an unsupported device or combination is an error.
+ */
+#ifndef NVFP4_MI355X_H_
+#define NVFP4_MI355X_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NVFP4_OK 0
+#define NVFP4_ERR_INVALID_ARG (-1) /* null/misaligned pointer, bad size or enum */
+#define NVFP4_ERR_UNSUPPORTED (-2) /* device is not gfx950, or mode/dtype combination not offered */
+#define NVFP4_ERR_HIP (-3)         /* a HIP runtime call or kernel launch failed */
+
+/* Element types of dense buffers. */
+#define NVFP4_DTYPE_BF16 0
+#define NVFP4_DTYPE_F32 1
+
+/* GEMM / MLP quantization modes (the pages' `quant_mode` "w4a4" | "w4a16",
+ * PR #35120 report, implementation breakdown item 1). */
+#define NVFP4_MODE_W4A4 0  /* NVFP4 activations x NVFP4 weights */
+#define NVFP4_MODE_W4A16 1 /* bf16 activations x NVFP4 weights */
+
+/* Repack kinds. */
+#define NVFP4_REPACK_PLAIN 0  /* any [R, C] weight, e.g. down_proj */
+#define NVFP4_REPACK_SWIGLU 1 /* merged gate_up [2I, C], rows [gate; up] */
+
+/* Kernel-class override for tests and benchmarks (process-wide). */
+#define NVFP4_PATH_AUTO 0    /* choose by M */
+#define NVFP4_PATH_GEMV 1    /* weight-streaming VALU GEMV, no MFMA (M <= 4) */
+#define NVFP4_PATH_STREAM 2  /* weight-streaming MFMA kernel (any M, sized for M <= 64) */
+#define NVFP4_PATH_TILED 3   /* LDS-tiled MFMA GEMM (any M) */
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* nvfp4_last_error(void);
+
+/*
+ * Per-tensor calibration of the global scale (static scales, like the
+ * `input_scale` / `input_scale_inv` layer attributes on the pages):
+ *   amax = max |x|,  g = fl(amax / 2688),  g_inv = fl(1 / g)
+ * where 2688 = 6 * 448 maps amax onto the largest element times the largest
+ * scale. x: n elements of x_dtype (bf16 or f32, finite, amax > 0).
+ * g, g_inv: 1-element fp32 device outputs (g's memory is also used as the
+ * reduction cell while the call runs).
+ */
+int nvfp4_calibrate(const void* x, int x_dtype, int64_t n, float* g, float* g_inv,
+                    void* stream);
+
+/*
+ * NVFP4 quantize, `fp4_quantize(x, input_scale_inv)` of PR #26626
+ * (DeepseekV2MLP.forward). For each 16-element block of a row:
+ *   amax = max |x_k|;  sv = fl(fl(amax * g_inv) / 6);
+ *   s = E4M3(sv) rounded to nearest, ties to even, saturating at 448;
+ *   r = fl(g_inv / s) (0 if s == 0);  code_k = E2M1(fl(x_k * r)) rounded to
+ *   nearest, ties to the even code, saturating at 6, sign kept (-0 -> 0x8).
+ * x: [M, K] of x_dtype (bf16 activations, or f32 e.g. for weights); K % 16 == 0.
+ * codes: [M, K/2] out; scales: [M, K/16] out. Bit-exact with the oracle.
+ */
+int nvfp4_quantize(const void* x, int x_dtype, int64_t M, int64_t K, const float* g_inv,
+                   uint8_t* codes, uint8_t* scales, void* stream);
+
+/*
+ * Bytes of the packed weight for an [R, C] NVFP4 matrix: R * C * 9 / 16
+ * (the codes and scales, permuted). R % 16 == 0 and C % 256 == 0; kind
+ * SWIGLU also needs (R / 2) % 16 == 0. Returns 0 for invalid arguments.
+ */
+size_t nvfp4_packed_bytes(int kind, int64_t R, int64_t C);
+
+/*
+ * One-time weight repack (the pages' load-time interleave of gate/up rows and
+ * block-scale swizzle in process_weights_after_loading, PR #26626 key source
+ * snippets, modelopt_quant.py; and the W4A16 prepack of the PR #35120 report,
+ * implementation breakdown item 2). The layout is this library's own:
+ *   tiles of 16 rows x 256 columns, 2304 bytes each, ordered
+ *   (row group, column tile); inside a tile, lane l = 0..63 owns codes bytes
+ *   [16l, 16l+16) and [1024+16l, 1024+16l+16) = row (l % 16), columns
+ *   256t + 128c + 32(l / 16) + [0, 32) for c = 0, 1, and scale bytes
+ *   [2048+4l, 2048+4l+4) = the scales of those four 16-column blocks.
+ *   kind SWIGLU takes rows [gate (I rows); up (I rows)] and orders row groups
+ *   gate 0, up 0, gate 1, up 1, ... (groups of 16), so a pair of adjacent
+ *   groups holds the gate and up rows of 16 consecutive outputs.
+ * codes [R, C/2], scales [R, C/16] in; packed out (nvfp4_packed_bytes bytes).
+ * Deterministic; the inputs may be freed afterwards.
+ */
+int nvfp4_repack_weight(int kind, const uint8_t* codes, const uint8_t* scales, int64_t R,
+                        int64_t C, void* packed, void* stream);
+
+/* Inverse of nvfp4_repack_weight (for verification and export). */
+int nvfp4_unpack_weight(int kind, const void* packed, int64_t R, int64_t C, uint8_t* codes,
+                        uint8_t* scales, void* stream);
+
+/*
+ * NVFP4 GEMM, `fp4_gemm(input, weight, input_sf, weight_sf, alpha, out_dtype,
+ * quant_mode)` of the PR #35120 report (key source snippets):
+ *   out[m, n] = alpha * sum_k A[m, k] * W[n, k]
+ * mode W4A4:  a = activation codes [M, K/2], a_scales = [M, K/16];
+ *             W4A4 alpha = g_a * g_w.
+ * mode W4A16: a = bf16 activations [M, K], a_scales must be NULL (the pages'
+ *             optional `input_sf`); alpha = g_w (weight dequant factor only).
+ * w_packed: PLAIN packed weight of [N, K]. K % 256 == 0, N % 16 == 0, M >= 0.
+ * out: [M, N] of out_dtype (f32 or bf16, round to nearest even).
+ * Accumulation is fp32; the order is fixed per (M, path), so results are
+ * deterministic.
+ */
+int nvfp4_gemm(int mode, const void* a, const uint8_t* a_scales, const void* w_packed,
+               int64_t M, int64_t N, int64_t K, const float* alpha, void* out, int out_dtype,
+               void* stream);
+
+/*
+ * Fused gate_up GEMM + SiLU(gate) * up + NVFP4 re-quantization,
+ * `nvfp4_gemm_swiglu_nvfp4_quant(x_fp4, x_scale, W_il, S_il, alpha,
+ * down_proj.input_scale_inv)` of PR #26626 (DeepseekV2MLP.forward). W4A4 only,
+ * as on the pages (PR #35120 report, implementation breakdown item 5).
+ *   gate/up[m, j] = alpha * (A @ W^T) for rows j and I + j of [gate; up],
+ *   h = SiLU(gate) * up in fp32, then quantized with g2_inv as nvfp4_quantize
+ *   does; h never reaches memory in another form.
+ * a_codes [M, K/2], a_scales [M, K/16]; w_gu_packed: SWIGLU packed [2I, K];
+ * I % 16 == 0, K % 256 == 0. h_codes [M, I/2], h_scales [M, I/16] out.
+ */
+int gemm_swiglu_nvfp4_quant(const uint8_t* a_codes, const uint8_t* a_scales,
+                            const void* w_gu_packed, int64_t M, int64_t I, int64_t K,
+                            const float* alpha, const float* g2_inv, uint8_t* h_codes,
+                            uint8_t* h_scales, void* stream);
+
+/*
+ * gate_up GEMM + SiLU(gate) * up to a dense h [M, I] of h_dtype (bf16: the
+ * W4A16 chain's activation; f32: calibration of g2 and checks of the
+ * re-quantization). mode and a/a_scales as in nvfp4_gemm. Uses the same
+ * accumulation as gemm_swiglu_nvfp4_quant for the same (M, path).
+ */
+int gemm_swiglu(int mode, const void* a, const uint8_t* a_scales, const void* w_gu_packed,
+                int64_t M, int64_t I, int64_t K, const float* alpha, void* h, int h_dtype,
+                void* stream);
+
+/* Workspace bytes mlp_forward needs: W4A4 holds x and h in NVFP4; W4A16
+ * holds h in bf16. Each region starts 256-byte aligned. */
+size_t mlp_workspace_bytes(int mode, int64_t M, int64_t H, int64_t I);
+
+/*
+ * Dense MLP forward, the pages' fused path (PR #26626, DeepseekV2MLP.forward):
+ *   W4A4:  x -> nvfp4_quantize(g1_inv) -> gemm_swiglu_nvfp4_quant(alpha_gu,
+ *          g2_inv) -> nvfp4_gemm(alpha_d) -> out
+ *   W4A16: x -> gemm_swiglu(bf16 h, alpha_gu = g_wgu) -> nvfp4_gemm(W4A16,
+ *          alpha_d = g_wd) -> out; g1_inv and g2_inv must be NULL.
+ * x bf16 [M, H]; w_gu_packed: SWIGLU packed [2I, H]; w_d_packed: PLAIN packed
+ * [H, I]; H % 256 == 0, I % 256 == 0. out [M, H] of out_dtype.
+ */
+int mlp_forward(int mode, const uint16_t* x, int64_t M, int64_t H, int64_t I,
+                const void* w_gu_packed, const float* alpha_gu, const void* w_d_packed,
+                const float* alpha_d, const float* g1_inv, const float* g2_inv, void* ws,
+                size_t ws_bytes, void* out, int out_dtype, void* stream);
+
+/* Select the kernel class used by the GEMM entry points (NVFP4_PATH_*).
+ * Process-wide; meant for tests and benchmarks. Returns the previous value,
+ * or NVFP4_ERR_INVALID_ARG. */
+int nvfp4_set_path(int path);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_MI355X_H_ */

@@ -1,0 +1,301 @@
+// api.cpp -- the extern "C" entry points declared in include/nvfp4.h:
+// argument validation (always before any HIP call), the gfx950 device check,
+// the choice of kernel class by token count, and the launches.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/nvfp4.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+std::atomic<int> g_path{NVFP4_PATH_AUTO};
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Largest GEMM dimension accepted: keeps every index of the 32-bit grid
+// arithmetic and the 64-bit byte offsets far from overflow.
+constexpr int64_t kMaxDim = int64_t(1) << 24;
+
+bool dim_ok(int64_t v) { return v >= 0 && v <= kMaxDim; }
+
+// gfx950 check, cached per device.
+int check_device() {
+  static std::mutex mu;
+  static int cached[64];
+  static bool init = false;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(NVFP4_ERR_HIP, "hipGetDevice failed");
+  if (dev < 0 || dev >= 64) return fail(NVFP4_ERR_UNSUPPORTED, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!init) {
+    for (int& c : cached) c = -1;
+    init = true;
+  }
+  if (cached[dev] < 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+      return fail(NVFP4_ERR_HIP, "hipGetDeviceProperties failed");
+    cached[dev] = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 0;
+    if (!cached[dev]) {
+      fail(NVFP4_ERR_UNSUPPORTED, "device %d is %s; this library runs on gfx950 (MI355X) only", dev,
+           prop.gcnArchName);
+    }
+  }
+  if (cached[dev] != 1)
+    return fail(NVFP4_ERR_UNSUPPORTED, "device %d is not gfx950 (MI355X); no other path exists", dev);
+  return NVFP4_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(NVFP4_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  g_err[0] = '\0';
+  return NVFP4_OK;
+}
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// Kernel class for a GEMM of M tokens.
+int choose_path(int64_t M) {
+  int p = g_path.load();
+  if (p != NVFP4_PATH_AUTO) return p;
+  if (M <= 1) return NVFP4_PATH_GEMV;
+  if (M <= 64) return NVFP4_PATH_STREAM;
+  return NVFP4_PATH_TILED;
+}
+
+hipError_t run_gemm(int path, int mode, int epi, const nvfp4::GemmArgs& a, hipStream_t s) {
+  switch (path) {
+    case NVFP4_PATH_GEMV: return nvfp4::launch_valu_gemv(mode, epi, a, s);
+    case NVFP4_PATH_STREAM: return nvfp4::launch_stream_gemm(mode, epi, a, s);
+    default: return nvfp4::launch_tiled_gemm(mode, epi, a, s);
+  }
+}
+
+// Shared checks of the GEMM entry points. N is the packed row count.
+int check_gemm(int mode, const void* a, const uint8_t* a_scales, const void* w, int64_t M,
+               int64_t N, int64_t K, const float* alpha, const void* out) {
+  if (mode != NVFP4_MODE_W4A4 && mode != NVFP4_MODE_W4A16)
+    return fail(NVFP4_ERR_INVALID_ARG, "unsupported quant mode %d (W4A4=0, W4A16=1)", mode);
+  if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K)) return fail(NVFP4_ERR_INVALID_ARG, "dimension out of range");
+  if (K <= 0 || K % 256 != 0) return fail(NVFP4_ERR_INVALID_ARG, "K=%lld must be a positive multiple of 256", (long long)K);
+  if (N <= 0 || N % 16 != 0) return fail(NVFP4_ERR_INVALID_ARG, "N=%lld must be a positive multiple of 16", (long long)N);
+  if (M > 0) {
+    if (!a || !w || !alpha || !out) return fail(NVFP4_ERR_INVALID_ARG, "null pointer argument");
+    if (!aligned16(a) || !aligned16(w) || !aligned16(out))
+      return fail(NVFP4_ERR_INVALID_ARG, "activation, weight and output must be 16-byte aligned");
+    if (mode == NVFP4_MODE_W4A4 && !a_scales)
+      return fail(NVFP4_ERR_INVALID_ARG, "W4A4 needs activation scales");
+  }
+  if (mode == NVFP4_MODE_W4A16 && a_scales)
+    return fail(NVFP4_ERR_INVALID_ARG, "W4A16 takes bf16 activations: a_scales must be NULL");
+  return NVFP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* nvfp4_last_error(void) { return g_err; }
+
+int nvfp4_set_path(int path) {
+  if (path < NVFP4_PATH_AUTO || path > NVFP4_PATH_TILED)
+    return fail(NVFP4_ERR_INVALID_ARG, "unknown path %d", path);
+  return g_path.exchange(path);
+}
+
+int nvfp4_calibrate(const void* x, int x_dtype, int64_t n, float* g, float* g_inv, void* stream) {
+  if (x_dtype != NVFP4_DTYPE_BF16 && x_dtype != NVFP4_DTYPE_F32)
+    return fail(NVFP4_ERR_INVALID_ARG, "x_dtype must be BF16 or F32");
+  if (n <= 0 || n > (int64_t(1) << 40)) return fail(NVFP4_ERR_INVALID_ARG, "n must be positive");
+  if (!x || !g || !g_inv) return fail(NVFP4_ERR_INVALID_ARG, "null pointer argument");
+  if (reinterpret_cast<uintptr_t>(g) % 4 || reinterpret_cast<uintptr_t>(g_inv) % 4)
+    return fail(NVFP4_ERR_INVALID_ARG, "g and g_inv must be 4-byte aligned");
+  if (g == g_inv) return fail(NVFP4_ERR_INVALID_ARG, "g and g_inv must differ");
+  int st = check_device();
+  if (st) return st;
+  return hip_status(nvfp4::launch_calibrate(x, x_dtype == NVFP4_DTYPE_F32, n, g, g_inv, as_stream(stream)),
+                    "calibrate launch");
+}
+
+int nvfp4_quantize(const void* x, int x_dtype, int64_t M, int64_t K, const float* g_inv,
+                   uint8_t* codes, uint8_t* scales, void* stream) {
+  if (x_dtype != NVFP4_DTYPE_BF16 && x_dtype != NVFP4_DTYPE_F32)
+    return fail(NVFP4_ERR_INVALID_ARG, "x_dtype must be BF16 or F32");
+  if (!dim_ok(M) || K < 0 || K > (int64_t(1) << 30) || K % 16 != 0)
+    return fail(NVFP4_ERR_INVALID_ARG, "need 0 <= M and K a multiple of 16 (M=%lld K=%lld)",
+                (long long)M, (long long)K);
+  if (M * K == 0) { g_err[0] = '\0'; return NVFP4_OK; }
+  if (!x || !g_inv || !codes || !scales) return fail(NVFP4_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(x) || !aligned16(codes))
+    return fail(NVFP4_ERR_INVALID_ARG, "x and codes must be 16-byte aligned");
+  int st = check_device();
+  if (st) return st;
+  return hip_status(nvfp4::launch_quantize(x, x_dtype == NVFP4_DTYPE_F32, M, K, g_inv, codes, scales,
+                                           as_stream(stream)),
+                    "quantize launch");
+}
+
+size_t nvfp4_packed_bytes(int kind, int64_t R, int64_t C) {
+  if (kind != NVFP4_REPACK_PLAIN && kind != NVFP4_REPACK_SWIGLU) return 0;
+  if (R <= 0 || C <= 0 || R % 16 != 0 || C % 256 != 0 || R > kMaxDim || C > kMaxDim) return 0;
+  if (kind == NVFP4_REPACK_SWIGLU && (R / 2) % 16 != 0) return 0;
+  return static_cast<size_t>(R) * static_cast<size_t>(C) / 16 * 9;
+}
+
+static int repack_common(int kind, const uint8_t* codes, const uint8_t* scales, int64_t R, int64_t C,
+                         const void* packed, bool unpack, uint8_t* oc, uint8_t* os, void* stream) {
+  if (nvfp4_packed_bytes(kind, R, C) == 0)
+    return fail(NVFP4_ERR_INVALID_ARG,
+                "repack needs kind PLAIN/SWIGLU, R %% 16 == 0 (SWIGLU: R/2 %% 16 == 0), C %% 256 == 0 "
+                "(kind=%d R=%lld C=%lld)", kind, (long long)R, (long long)C);
+  if (!packed) return fail(NVFP4_ERR_INVALID_ARG, "null packed pointer");
+  if (unpack ? (!oc || !os) : (!codes || !scales)) return fail(NVFP4_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(packed) || !aligned16(unpack ? oc : codes))
+    return fail(NVFP4_ERR_INVALID_ARG, "packed and codes must be 16-byte aligned");
+  int st = check_device();
+  if (st) return st;
+  return hip_status(nvfp4::launch_repack(kind, codes, scales, R, C,
+                                         const_cast<uint8_t*>(static_cast<const uint8_t*>(packed)), unpack,
+                                         oc, os, as_stream(stream)),
+                    "repack launch");
+}
+
+int nvfp4_repack_weight(int kind, const uint8_t* codes, const uint8_t* scales, int64_t R, int64_t C,
+                        void* packed, void* stream) {
+  return repack_common(kind, codes, scales, R, C, packed, false, nullptr, nullptr, stream);
+}
+
+int nvfp4_unpack_weight(int kind, const void* packed, int64_t R, int64_t C, uint8_t* codes,
+                        uint8_t* scales, void* stream) {
+  return repack_common(kind, nullptr, nullptr, R, C, packed, true, codes, scales, stream);
+}
+
+int nvfp4_gemm(int mode, const void* a, const uint8_t* a_scales, const void* w_packed, int64_t M,
+               int64_t N, int64_t K, const float* alpha, void* out, int out_dtype, void* stream) {
+  int st = check_gemm(mode, a, a_scales, w_packed, M, N, K, alpha, out);
+  if (st) return st;
+  if (out_dtype != NVFP4_DTYPE_F32 && out_dtype != NVFP4_DTYPE_BF16)
+    return fail(NVFP4_ERR_INVALID_ARG, "out_dtype must be F32 or BF16");
+  if (M == 0) { g_err[0] = '\0'; return NVFP4_OK; }
+  st = check_device();
+  if (st) return st;
+  nvfp4::GemmArgs ga{a, a_scales, static_cast<const uint8_t*>(w_packed), M, N, K, alpha, nullptr, out, nullptr};
+  const int epi = out_dtype == NVFP4_DTYPE_F32 ? nvfp4::kOutF32 : nvfp4::kOutBF16;
+  return hip_status(run_gemm(choose_path(M), mode, epi, ga, as_stream(stream)), "gemm launch");
+}
+
+int gemm_swiglu_nvfp4_quant(const uint8_t* a_codes, const uint8_t* a_scales, const void* w_gu_packed,
+                            int64_t M, int64_t I, int64_t K, const float* alpha, const float* g2_inv,
+                            uint8_t* h_codes, uint8_t* h_scales, void* stream) {
+  if (!dim_ok(I) || I <= 0 || I % 16 != 0)
+    return fail(NVFP4_ERR_INVALID_ARG, "I=%lld must be a positive multiple of 16", (long long)I);
+  int st = check_gemm(NVFP4_MODE_W4A4, a_codes, a_scales, w_gu_packed, M, 2 * I, K, alpha, h_codes);
+  if (st) return st;
+  if (M > 0 && (!g2_inv || !h_scales)) return fail(NVFP4_ERR_INVALID_ARG, "null pointer argument");
+  if (M == 0) { g_err[0] = '\0'; return NVFP4_OK; }
+  st = check_device();
+  if (st) return st;
+  nvfp4::GemmArgs ga{a_codes, a_scales, static_cast<const uint8_t*>(w_gu_packed), M, 2 * I, K, alpha, g2_inv,
+                     h_codes, h_scales};
+  return hip_status(run_gemm(choose_path(M), NVFP4_MODE_W4A4, nvfp4::kSwigluNvfp4, ga, as_stream(stream)),
+                    "gemm_swiglu_nvfp4_quant launch");
+}
+
+int gemm_swiglu(int mode, const void* a, const uint8_t* a_scales, const void* w_gu_packed, int64_t M,
+                int64_t I, int64_t K, const float* alpha, void* h, int h_dtype, void* stream) {
+  if (!dim_ok(I) || I <= 0 || I % 16 != 0)
+    return fail(NVFP4_ERR_INVALID_ARG, "I=%lld must be a positive multiple of 16", (long long)I);
+  int st = check_gemm(mode, a, a_scales, w_gu_packed, M, 2 * I, K, alpha, h);
+  if (st) return st;
+  if (h_dtype != NVFP4_DTYPE_F32 && h_dtype != NVFP4_DTYPE_BF16)
+    return fail(NVFP4_ERR_INVALID_ARG, "h_dtype must be F32 or BF16");
+  if (M == 0) { g_err[0] = '\0'; return NVFP4_OK; }
+  st = check_device();
+  if (st) return st;
+  nvfp4::GemmArgs ga{a, a_scales, static_cast<const uint8_t*>(w_gu_packed), M, 2 * I, K, alpha, nullptr, h, nullptr};
+  const int epi = h_dtype == NVFP4_DTYPE_F32 ? nvfp4::kSwigluF32 : nvfp4::kSwigluBF16;
+  return hip_status(run_gemm(choose_path(M), mode, epi, ga, as_stream(stream)), "gemm_swiglu launch");
+}
+
+size_t mlp_workspace_bytes(int mode, int64_t M, int64_t H, int64_t I) {
+  if (M < 0 || H <= 0 || I <= 0 || !dim_ok(M) || !dim_ok(H) || !dim_ok(I)) return 0;
+  const size_t m = static_cast<size_t>(M);
+  if (mode == NVFP4_MODE_W4A4) {
+    return align256(m * H / 2) + align256(m * H / 16) + align256(m * I / 2) + align256(m * I / 16);
+  }
+  if (mode == NVFP4_MODE_W4A16) return align256(m * I * 2);
+  return 0;
+}
+
+int mlp_forward(int mode, const uint16_t* x, int64_t M, int64_t H, int64_t I, const void* w_gu_packed,
+                const float* alpha_gu, const void* w_d_packed, const float* alpha_d, const float* g1_inv,
+                const float* g2_inv, void* ws, size_t ws_bytes, void* out, int out_dtype, void* stream) {
+  if (mode != NVFP4_MODE_W4A4 && mode != NVFP4_MODE_W4A16)
+    return fail(NVFP4_ERR_INVALID_ARG, "unsupported quant mode %d", mode);
+  if (!dim_ok(M) || !dim_ok(H) || !dim_ok(I)) return fail(NVFP4_ERR_INVALID_ARG, "dimension out of range");
+  if (H <= 0 || H % 256 != 0 || I <= 0 || I % 256 != 0)
+    return fail(NVFP4_ERR_INVALID_ARG, "H and I must be positive multiples of 256 (H=%lld I=%lld)",
+                (long long)H, (long long)I);
+  if (out_dtype != NVFP4_DTYPE_F32 && out_dtype != NVFP4_DTYPE_BF16)
+    return fail(NVFP4_ERR_INVALID_ARG, "out_dtype must be F32 or BF16");
+  if (mode == NVFP4_MODE_W4A16 && (g1_inv || g2_inv))
+    return fail(NVFP4_ERR_INVALID_ARG, "W4A16 takes no activation scales: g1_inv and g2_inv must be NULL");
+  if (M == 0) { g_err[0] = '\0'; return NVFP4_OK; }
+  if (!x || !w_gu_packed || !alpha_gu || !w_d_packed || !alpha_d || !out || !ws)
+    return fail(NVFP4_ERR_INVALID_ARG, "null pointer argument");
+  if (mode == NVFP4_MODE_W4A4 && (!g1_inv || !g2_inv))
+    return fail(NVFP4_ERR_INVALID_ARG, "W4A4 needs g1_inv and g2_inv");
+  if (!aligned16(x) || !aligned16(w_gu_packed) || !aligned16(w_d_packed) || !aligned16(out) || !aligned16(ws))
+    return fail(NVFP4_ERR_INVALID_ARG, "buffers must be 16-byte aligned");
+  const size_t need = mlp_workspace_bytes(mode, M, H, I);
+  if (ws_bytes < need)
+    return fail(NVFP4_ERR_INVALID_ARG, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  int st = check_device();
+  if (st) return st;
+  hipStream_t s = as_stream(stream);
+  const int path = choose_path(M);
+  const int epi_out = out_dtype == NVFP4_DTYPE_F32 ? nvfp4::kOutF32 : nvfp4::kOutBF16;
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  const size_t m = static_cast<size_t>(M);
+  hipError_t e;
+  if (mode == NVFP4_MODE_W4A4) {
+    uint8_t* xq = base;
+    uint8_t* xs = xq + align256(m * H / 2);
+    uint8_t* hq = xs + align256(m * H / 16);
+    uint8_t* hs = hq + align256(m * I / 2);
+    e = nvfp4::launch_quantize(x, false, M, H, g1_inv, xq, xs, s);
+    if (e != hipSuccess) return hip_status(e, "mlp_forward quantize");
+    nvfp4::GemmArgs g1{xq, xs, static_cast<const uint8_t*>(w_gu_packed), M, 2 * I, H, alpha_gu, g2_inv, hq, hs};
+    e = run_gemm(path, NVFP4_MODE_W4A4, nvfp4::kSwigluNvfp4, g1, s);
+    if (e != hipSuccess) return hip_status(e, "mlp_forward gate_up");
+    nvfp4::GemmArgs g2{hq, hs, static_cast<const uint8_t*>(w_d_packed), M, H, I, alpha_d, nullptr, out, nullptr};
+    e = run_gemm(path, NVFP4_MODE_W4A4, epi_out, g2, s);
+    return hip_status(e, "mlp_forward down");
+  }
+  uint8_t* hb = base;
+  nvfp4::GemmArgs g1{x, nullptr, static_cast<const uint8_t*>(w_gu_packed), M, 2 * I, H, alpha_gu, nullptr, hb, nullptr};
+  e = run_gemm(path, NVFP4_MODE_W4A16, nvfp4::kSwigluBF16, g1, s);
+  if (e != hipSuccess) return hip_status(e, "mlp_forward gate_up");
+  nvfp4::GemmArgs g2{hb, nullptr, static_cast<const uint8_t*>(w_d_packed), M, H, I, alpha_d, nullptr, out, nullptr};
+  e = run_gemm(path, NVFP4_MODE_W4A16, epi_out, g2, s);
+  return hip_status(e, "mlp_forward down");
+}
+
+}  // extern "C"

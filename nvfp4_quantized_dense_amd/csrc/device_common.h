@@ -1,0 +1,192 @@
+// device_common.h -- gfx950 device helpers shared by the NVFP4 kernels:
+// the E2M1/E4M3 encoders, in-register dequantization for the MFMA operands,
+// the packed-weight tile geometry and the GEMM epilogues.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+namespace nvfp4 {
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Packed weight tile: 16 rows x 256 columns. Lane l of a wave owns, for
+// c = 0, 1, the 16 code bytes at c * 1024 + 16 l (row l % 16, columns
+// 256 t + 128 c + 32 (l / 16) + [0, 32)) and 4 scale bytes at 2048 + 4 l
+// (blocks 16 t + 8 c + 2 (l / 16) + {0, 1}, ordered c0b0 c0b1 c1b0 c1b1).
+constexpr int kTileRows = 16;
+constexpr int kTileK = 256;
+constexpr int kTileCodeBytes = 2048;
+constexpr int kTileBytes = 2304;
+
+template <int E>
+struct EpiTraits {
+  static constexpr bool swiglu = (E == kSwigluNvfp4 || E == kSwigluBF16 || E == kSwigluF32);
+};
+
+// ---------------------------------------------------------------------------
+// Encoders (round to nearest, ties to even, saturating).
+// ---------------------------------------------------------------------------
+
+// Non-negative finite fp32 -> E4M3FN byte. Normal range: round the 23-bit
+// mantissa to 3 bits with the carry running into the exponent; below 2^-6 the
+// quantum is 2^-9, so rint(v * 512) is the subnormal mantissa (8 = 2^-6 is
+// byte 0x08 as well). Values at or above 448 saturate to 0x7E.
+__device__ __forceinline__ uint32_t e4m3_from_f32(float v) {
+  uint32_t u = __float_as_uint(v) & 0x7FFFFFFFu;
+  if (u >= 0x43E00000u) return 0x7Eu;  // >= 448
+  if (u < 0x3C800000u) {               // < 2^-6
+    return (uint32_t)__builtin_rintf(__uint_as_float(u) * 512.0f);
+  }
+  u += 0x7FFFFu + ((u >> 20) & 1u);
+  return (((u >> 23) - 120u) << 3) | ((u >> 20) & 7u);
+}
+
+// E4M3FN byte (selected byte of a dword) -> fp32, hardware OCP decode.
+template <int SEL>
+__device__ __forceinline__ float e4m3_to_f32(uint32_t dword) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)dword, SEL);
+}
+
+// fp32 -> 4-bit E2M1 code. The code magnitude counts the grid midpoints that
+// |y| has passed; the comparison at each midpoint (strict or not) sends ties
+// to the even neighbour. Bit 3 takes the sign bit of y.
+__device__ __forceinline__ uint32_t e2m1_from_f32(float y) {
+  float a = __builtin_fabsf(y);
+  uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+               (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+               (uint32_t)(a > 5.0f);
+  return c | ((__float_as_uint(y) >> 28) & 8u);
+}
+
+// One NVFP4 block: scale byte and the per-element multiplier r = g_inv / s.
+struct BlockScale {
+  uint32_t byte;
+  float r;
+};
+__device__ __forceinline__ BlockScale block_scale(float amax, float g_inv) {
+  float sv = (amax * g_inv) / 6.0f;
+  BlockScale b;
+  b.byte = e4m3_from_f32(sv);
+  float s = __builtin_amdgcn_cvt_f32_fp8((int)b.byte, 0);
+  b.r = (s != 0.0f) ? g_inv / s : 0.0f;
+  return b;
+}
+
+// ---------------------------------------------------------------------------
+// Dequantization of 8 E2M1 codes (one dword) into an MFMA operand.
+// The fp4 conversion instructions scale by a power of two only (the exponent
+// of their f32 scale operand), so the E4M3 block scale is applied separately:
+//  * f16: q converts exactly, then a packed f16 multiply by s; q * s has at
+//    most 6 significant bits and lies in [2^-10, 2688], so it is exact.
+//  * bf16: q * s through f32 (exact) and a round-to-nearest pack that keeps
+//    the exact value.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ f16x8 deq8_f16(uint32_t w, _Float16 s) {
+  f16x2 s2 = {s, s};
+  f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2;
+  f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2;
+  f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2;
+  f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2;
+  f16x8 r = {p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 deq8_bf16(uint32_t w, float s) {
+  f32x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+  f32x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+  f32x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+  f32x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+  bf16x8 r = {(__bf16)(p0[0] * s), (__bf16)(p0[1] * s), (__bf16)(p1[0] * s),
+              (__bf16)(p1[1] * s), (__bf16)(p2[0] * s), (__bf16)(p2[1] * s),
+              (__bf16)(p3[0] * s), (__bf16)(p3[1] * s)};
+  return r;
+}
+
+// Scale byte k (0..3) of a lane's scale dword as f16 / f32.
+template <int K>
+__device__ __forceinline__ _Float16 scale_f16(uint32_t sdw) {
+  return (_Float16)e4m3_to_f32<K>(sdw);
+}
+
+__device__ __forceinline__ f32x4 mfma16x16x32(const f16x8& a, const f16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
+
+// ---------------------------------------------------------------------------
+// Epilogues. The MFMA 16x16x32 result tile of a lane holds rows 4(l/16)+r,
+// r = 0..3, of one token column l % 16.
+// ---------------------------------------------------------------------------
+
+// Dense output: out[token, row0 + r] = alpha * acc[r].
+template <int E>
+__device__ __forceinline__ void store_dense(const f32x4& acc, float alpha, bool valid,
+                                            int64_t token, int64_t row0, int64_t N, void* out) {
+  if (!valid) return;
+  f32x4 v = {alpha * acc[0], alpha * acc[1], alpha * acc[2], alpha * acc[3]};
+  if constexpr (E == kOutF32) {
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + token * N + row0) = v;
+  } else {
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    bf16x4 b = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+    *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(out) + token * N + row0) = b;
+  }
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  float s = g / (1.0f + expf(-g));
+  return s * u;
+}
+
+// SwiGLU of matching gate/up tiles. Lane l holds outputs j = j0 + 4(l/16) + r
+// of token l % 16; j0 is a multiple of 16, so the 64 lanes of the wave hold
+// whole 16-element NVFP4 blocks of h (one per token column). All lanes of the
+// wave must call this (the block amax is a cross-lane reduction).
+template <int E>
+__device__ __forceinline__ void store_swiglu(const f32x4& gate, const f32x4& up, float alpha,
+                                             float g2_inv, bool valid, int64_t token, int64_t j0,
+                                             int lane, int64_t I, void* out, uint8_t* out_scales) {
+  const int q = lane >> 4;
+  float h[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) h[r] = silu_mul(alpha * gate[r], alpha * up[r]);
+  const int64_t j = j0 + 4 * q;
+  if constexpr (E == kSwigluF32) {
+    if (valid) {
+      f32x4 v = {h[0], h[1], h[2], h[3]};
+      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + token * I + j) = v;
+    }
+  } else if constexpr (E == kSwigluBF16) {
+    if (valid) {
+      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+      bf16x4 b = {(__bf16)h[0], (__bf16)h[1], (__bf16)h[2], (__bf16)h[3]};
+      *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(out) + token * I + j) = b;
+    }
+  } else {
+    float amax = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(h[0]), __builtin_fabsf(h[1])),
+                                 __builtin_fmaxf(__builtin_fabsf(h[2]), __builtin_fabsf(h[3])));
+    amax = __builtin_fmaxf(amax, __shfl_xor(amax, 16));
+    amax = __builtin_fmaxf(amax, __shfl_xor(amax, 32));
+    BlockScale bs = block_scale(amax, g2_inv);
+    uint32_t packed = e2m1_from_f32(h[0] * bs.r) | (e2m1_from_f32(h[1] * bs.r) << 4) |
+                      (e2m1_from_f32(h[2] * bs.r) << 8) | (e2m1_from_f32(h[3] * bs.r) << 12);
+    if (valid) {
+      uint8_t* codes = reinterpret_cast<uint8_t*>(out);
+      *reinterpret_cast<uint16_t*>(codes + token * (I / 2) + j / 2) = (uint16_t)packed;
+      if (q == 0) out_scales[token * (I / 16) + j0 / 16] = (uint8_t)bs.byte;
+    }
+  }
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,99 @@
+"""The C-ABI library on the CPU: it loads, exports every function that
+include/nvfp4.h declares, and rejects bad arguments before any HIP call
+(these calls never reach a device, so they run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import nvfp4_quantized_dense_amd as nv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "nvfp4.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:int|size_t|char\s*\*|const char\s*\*)\s*\**\s*"
+                                 r"([a-z_0-9]+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ["nvfp4_quantize", "nvfp4_gemm", "gemm_swiglu_nvfp4_quant", "mlp_forward",
+              "nvfp4_repack_weight", "nvfp4_packed_bytes", "nvfp4_last_error"]:
+        assert n in names, names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(nv.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    assert set(declared_functions()) == set(nv.SIGNATURES)
+
+
+def test_packed_and_workspace_sizes():
+    assert nv.nvfp4_packed_bytes(nv.REPACK_PLAIN, 5120, 17408) == 5120 * 17408 * 9 // 16
+    assert nv.nvfp4_packed_bytes(nv.REPACK_SWIGLU, 2 * 17408, 5120) == 2 * 17408 * 5120 * 9 // 16
+    assert nv.nvfp4_packed_bytes(nv.REPACK_PLAIN, 24, 256) == 0       # rows % 16
+    assert nv.nvfp4_packed_bytes(nv.REPACK_PLAIN, 16, 128) == 0       # cols % 256
+    assert nv.nvfp4_packed_bytes(nv.REPACK_SWIGLU, 48, 256) == 0      # half not % 16
+    assert nv.nvfp4_packed_bytes(7, 16, 256) == 0
+    w = nv.mlp_workspace_bytes(nv.MODE_W4A4, 1, 5120, 17408)
+    assert w >= 2560 + 320 + 8704 + 1088 and w % 256 == 0
+    assert nv.mlp_workspace_bytes(nv.MODE_W4A16, 4, 256, 512) == 4 * 512 * 2
+    assert nv.mlp_workspace_bytes(9, 1, 256, 512) == 0
+
+
+def _code(fn, *args):
+    return fn(*args)
+
+
+def test_invalid_arguments_are_rejected_on_the_host():
+    lib = nv.lib()
+    P = ctypes.c_void_p(0x100000)  # 16-byte aligned, never dereferenced
+    U = ctypes.c_void_p(0x100001)  # misaligned
+    N = None
+    INV = nv.NVFP4_ERR_INVALID_ARG
+    assert lib.nvfp4_quantize(P, 7, 4, 256, P, P, P, N) == INV                 # dtype
+    assert lib.nvfp4_quantize(P, 0, 4, 250, P, P, P, N) == INV                 # K % 16
+    assert lib.nvfp4_quantize(N, 0, 4, 256, P, P, P, N) == INV                 # null x
+    assert lib.nvfp4_quantize(U, 0, 4, 256, P, P, P, N) == INV                 # misaligned
+    assert b"aligned" in lib.nvfp4_last_error()
+    assert lib.nvfp4_quantize(N, 0, 0, 256, N, N, N, N) == nv.NVFP4_OK         # empty: no-op
+    assert lib.nvfp4_gemm(3, P, P, P, 4, 16, 256, P, P, 1, N) == INV           # mode
+    assert b"mode" in lib.nvfp4_last_error()
+    assert lib.nvfp4_gemm(0, P, P, P, 4, 16, 200, P, P, 1, N) == INV           # K % 256
+    assert lib.nvfp4_gemm(0, P, P, P, 4, 24, 256, P, P, 1, N) == INV           # N % 16
+    assert lib.nvfp4_gemm(0, P, N, P, 4, 16, 256, P, P, 1, N) == INV           # W4A4 needs scales
+    assert lib.nvfp4_gemm(1, P, P, P, 4, 16, 256, P, P, 1, N) == INV           # W4A16 takes none
+    assert lib.nvfp4_gemm(0, P, P, P, 4, 16, 256, P, P, 5, N) == INV           # out dtype
+    assert lib.nvfp4_gemm(0, P, P, P, -1, 16, 256, P, P, 1, N) == INV          # negative M
+    assert lib.nvfp4_gemm(0, P, P, P, 0, 16, 256, P, P, 1, N) == nv.NVFP4_OK   # M = 0: no-op
+    assert lib.gemm_swiglu_nvfp4_quant(P, P, P, 4, 24, 256, P, P, P, P, N) == INV  # I % 16
+    assert lib.gemm_swiglu_nvfp4_quant(P, P, P, 4, 32, 256, P, N, P, P, N) == INV  # null g2_inv
+    assert lib.gemm_swiglu(0, P, P, P, 4, 32, 256, P, P, 3, N) == INV          # h dtype
+    assert lib.nvfp4_repack_weight(0, P, P, 17, 256, P, N) == INV              # rows
+    assert lib.nvfp4_unpack_weight(1, P, 48, 256, P, P, N) == INV              # swiglu half
+    assert lib.nvfp4_calibrate(P, 0, 0, P, P, N) == INV                        # n
+    assert lib.nvfp4_calibrate(P, 0, 16, P, P, N) == INV                       # g == g_inv
+    ws = ctypes.c_size_t(1 << 20)
+    assert lib.mlp_forward(0, P, 4, 256, 500, P, P, P, P, P, P, P, ws, P, 1, N) == INV  # I % 256
+    assert lib.mlp_forward(1, P, 4, 256, 512, P, P, P, P, P, N, P, ws, P, 1, N) == INV  # W4A16 + g1
+    assert lib.mlp_forward(0, P, 4, 256, 512, P, P, P, P, N, P, P, ws, P, 1, N) == INV  # W4A4 no g1
+    assert lib.mlp_forward(0, P, 4, 256, 512, P, P, P, P, P, P, P, ctypes.c_size_t(16), P, 1, N) == INV
+    assert b"workspace" in lib.nvfp4_last_error()
+    assert lib.nvfp4_set_path(9) == INV
+
+
+def test_set_path_round_trip():
+    prev = nv.set_path(nv.PATH_TILED)
+    assert nv.set_path(prev) == nv.PATH_TILED
+
+
+def test_python_binding_raises_with_the_message():
+    import torch
+    x = torch.zeros((4, 250), dtype=torch.bfloat16)
+    with pytest.raises(nv.Nvfp4Error, match="multiple of 16"):
+        nv.nvfp4_quantize(x, torch.ones(1))

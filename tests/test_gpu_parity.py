@@ -1,0 +1,268 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Bit-exact where the result is integer/byte work (quantize codes and scale
+bytes, calibration, repack); within the fp32 tolerance for GEMM/MLP outputs;
+the one-step tie rule for re-quantized codes against the pure oracle, and
+bit-exact against the oracle's quantization of the kernel's own fp32 h.
+"""
+import numpy as np
+import pytest
+import torch
+
+import nvfp4_synth as synth
+import oracle
+from gpu_helpers import (calibrate_activation_scales, dev, gemm_close, mlp_weights, packed_weights,
+                         requant_check, scalar, to_dev, to_host)
+
+pytestmark = pytest.mark.gpu
+
+nv = None
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    global nv
+    import nvfp4_quantized_dense_amd as _nv
+    nv = _nv
+    nv.lib()
+    assert torch.cuda.is_available()
+    yield
+    nv.set_path(nv.PATH_AUTO)
+
+
+PATHS = {"gemv": 1, "stream": 2, "tiled": 3}
+
+
+@pytest.fixture(params=list(PATHS))
+def path(request):
+    prev = nv.set_path(PATHS[request.param])
+    yield request.param
+    nv.set_path(prev)
+
+
+def rand_nvfp4(rng, R, K, lo=0x28, hi=0x48):
+    return (rng.integers(0, 256, (R, K // 2), dtype=np.uint8),
+            rng.integers(lo, hi, (R, K // 16), dtype=np.uint8))
+
+
+# -- quantize / calibrate / repack (bit-exact) -------------------------------
+
+def _edge_rows(K, rng):
+    """Rows that hit ties, saturation, subnormal scales, zero blocks, -0."""
+    rows = []
+    tie = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5, 6, -0.25, -2.5, 0.5, 1, 1.5, 2, 3, 4],
+                   np.float32)
+    rows.append(np.tile(tie, K // 16))
+    rows.append(np.zeros(K, np.float32))
+    z = np.zeros(K, np.float32); z[::16] = -0.0; z[1::16] = -1e-38
+    rows.append(z)
+    rows.append(np.full(K, 3.0e4, np.float32) * np.sign(rng.standard_normal(K)).astype(np.float32))
+    rows.append((rng.standard_normal(K) * 1e-30).astype(np.float32))
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("M,K", [(1, 16), (3, 256), (64, 5120), (257, 7168), (5, 18432)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_quantize_bit_exact(M, K, dtype):
+    rng = np.random.default_rng(M * 7 + K)
+    x = (rng.standard_normal((M, K)) * np.exp(2 * rng.standard_normal((M, 1)))).astype(np.float32)
+    x = np.concatenate([x, _edge_rows(K, rng)])
+    xb = synth.f32_to_bf16_bits(x)
+    for gi in [np.float32(1.0), np.float32(0.37), np.float32(2.0e3)]:
+        if dtype == "bf16":
+            xin, xo = to_dev(xb), xb
+        else:
+            xin, xo = to_dev(x), x
+        c, s = nv.nvfp4_quantize(xin, scalar(gi))
+        oc, os_ = oracle.quantize(xo, gi)
+        assert np.array_equal(to_host(s), os_), f"scales differ (g_inv={gi})"
+        assert np.array_equal(to_host(c), oc), f"codes differ (g_inv={gi})"
+
+
+def test_quantize_exhaustive_bf16_slot():
+    """Every finite bf16 value beside a block max of 6 (s = 1, r = 1)."""
+    vals = synth.bf16_bits_to_f32(np.arange(65536, dtype=np.uint16))
+    vals = vals[np.isfinite(vals) & (np.abs(vals) <= 6)]
+    x = np.zeros((vals.size, 16), np.float32)
+    x[:, 0] = 6.0
+    x[:, 5] = vals
+    xb = synth.f32_to_bf16_bits(x)
+    c, s = nv.nvfp4_quantize(to_dev(xb), scalar(1.0))
+    oc, os_ = oracle.quantize(xb, np.float32(1.0))
+    assert np.array_equal(to_host(c), oc) and np.array_equal(to_host(s), os_)
+
+
+@pytest.mark.parametrize("n,dtype", [(1, "bf16"), (4097, "bf16"), (1 << 20, "f32")])
+def test_calibrate_bit_exact(n, dtype):
+    rng = np.random.default_rng(n)
+    x = (rng.standard_normal(n) * 3).astype(np.float32)
+    xo = synth.f32_to_bf16_bits(x) if dtype == "bf16" else x
+    g, gi = nv.nvfp4_calibrate(to_dev(xo))
+    og, ogi = oracle.global_scale(xo)
+    assert to_host(g)[0] == og and to_host(gi)[0] == ogi
+
+
+@pytest.mark.parametrize("kind,R,C", [(0, 16, 256), (0, 5120, 512), (1, 32, 256), (1, 1024, 768)])
+def test_repack_round_trip(kind, R, C):
+    rng = np.random.default_rng(R + C)
+    c, s = rand_nvfp4(rng, R, C, 0, 256)
+    p = nv.nvfp4_repack_weight(kind, to_dev(c), to_dev(s))
+    assert p.numel() == R * C * 9 // 16
+    c2, s2 = nv.nvfp4_unpack_weight(kind, p, R, C)
+    assert np.array_equal(to_host(c2), c) and np.array_equal(to_host(s2), s)
+    # the packed buffer is a permutation of the input bytes
+    assert np.array_equal(np.sort(to_host(p)), np.sort(np.concatenate([c.ravel(), s.ravel()])))
+
+
+# -- GEMM ---------------------------------------------------------------------
+
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 16, 17, 40, 64, 130])
+@pytest.mark.parametrize("mode", ["w4a4", "w4a16"])
+def test_gemm_matches_oracle(path, M, mode):
+    rng = np.random.default_rng(M)
+    N, K = 272, 768  # 17 row groups, 3 K tiles: ragged against every tile shape
+    wc, ws = rand_nvfp4(rng, N, K)
+    p = nv.nvfp4_repack_weight(0, to_dev(wc), to_dev(ws))
+    alpha = np.float32(0.0173)
+    if mode == "w4a4":
+        ac, as_ = rand_nvfp4(rng, M, K)
+        ref = oracle.gemm_w4a4(ac, as_, wc, ws, alpha)
+        y = nv.nvfp4_gemm(0, to_dev(ac), to_dev(as_), p, N, K, scalar(alpha))
+    else:
+        x = synth.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+        ref = oracle.gemm_w4a16(x, wc, ws, alpha)
+        y = nv.nvfp4_gemm(1, to_dev(x), None, p, N, K, scalar(alpha))
+    gemm_close(to_host(y), ref, f"{path} {mode} M={M}")
+    yb = nv.nvfp4_gemm(0 if mode == "w4a4" else 1, to_dev(ac if mode == "w4a4" else x),
+                       to_dev(as_) if mode == "w4a4" else None, p, N, K, scalar(alpha),
+                       out_dtype=torch.bfloat16)
+    assert np.array_equal(to_host(yb), synth.f32_to_bf16_bits(to_host(y)))
+
+
+@pytest.mark.parametrize("M", [1, 4, 33])
+def test_gemm_power_of_two_scales_bit_exact(path, M):
+    """All partial sums exactly representable: every path must be bit-exact."""
+    rng = np.random.default_rng(100 + M)
+    N, K = 64, 1024
+    ac = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
+    wc = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    pw = np.array([0x30, 0x38, 0x40], np.uint8)
+    as_, ws = rng.choice(pw, (M, K // 16)), rng.choice(pw, (N, K // 16))
+    p = nv.nvfp4_repack_weight(0, to_dev(wc), to_dev(ws))
+    y = nv.nvfp4_gemm(0, to_dev(ac), to_dev(as_), p, N, K, scalar(0.25))
+    assert np.array_equal(to_host(y), oracle.gemm_w4a4(ac, as_, wc, ws, np.float32(0.25)))
+    # W4A16 with bf16 activations that are small multiples of powers of two
+    x = synth.f32_to_bf16_bits((rng.integers(-8, 9, (M, K)) * 0.25).astype(np.float32))
+    y = nv.nvfp4_gemm(1, to_dev(x), None, p, N, K, scalar(0.5))
+    assert np.array_equal(to_host(y), oracle.gemm_w4a16(x, wc, ws, np.float32(0.5)))
+
+
+def test_gemm_deterministic_and_guarded(path):
+    rng = np.random.default_rng(5)
+    M, N, K = 37, 128, 512
+    wc, ws = rand_nvfp4(rng, N, K)
+    ac, as_ = rand_nvfp4(rng, M, K)
+    p = nv.nvfp4_repack_weight(0, to_dev(wc), to_dev(ws))
+    guard = torch.full((M * N + 64,), 12345.0, dtype=torch.float32, device=dev())
+    out = guard[16:16 + M * N].view(M, N)
+    nv.nvfp4_gemm(0, to_dev(ac), to_dev(as_), p, N, K, scalar(1.0), out=out)
+    y1 = to_host(out).copy()
+    nv.nvfp4_gemm(0, to_dev(ac), to_dev(as_), p, N, K, scalar(1.0), out=out)
+    assert np.array_equal(y1, to_host(out))
+    g = to_host(guard)
+    assert np.all(g[:16] == 12345.0) and np.all(g[16 + M * N:] == 12345.0)
+
+
+# -- fused gate_up + SwiGLU (+ NVFP4) ------------------------------------------
+
+@pytest.mark.parametrize("M", [1, 3, 16, 40, 129])
+def test_swiglu_fused_requant(path, M):
+    H, I = 512, 256
+    w = mlp_weights(H, I, 1)
+    p_gu, _ = packed_weights(H, I, 1)
+    x = synth.activations(3, M, H)
+    sc = calibrate_activation_scales(x, w)
+    xq, xs = oracle.quantize(x, sc["g1_inv"])
+    dxq, dxs = to_dev(xq), to_dev(xs)
+    # dense h in f32 against the oracle
+    h32 = nv.gemm_swiglu(0, dxq, dxs, p_gu, I, H, scalar(sc["a_gu"]), h_dtype=torch.float32)
+    gu = oracle.gemm_w4a4(xq, xs, w["c_gu"], w["s_gu"], sc["a_gu"])
+    h_ref = oracle.swiglu(gu)
+    gemm_close(to_host(h32), h_ref, f"{path} h M={M}")
+    # fused NVFP4: bit-exact against the oracle's quantization of the kernel's h
+    hc, hs = nv.gemm_swiglu_nvfp4_quant(dxq, dxs, p_gu, I, H, scalar(sc["a_gu"]), scalar(sc["g2_inv"]))
+    oc, os_ = oracle.quantize(to_host(h32), sc["g2_inv"])
+    assert np.array_equal(to_host(hs), os_) and np.array_equal(to_host(hc), oc)
+    # and within the tie rule against the pure oracle
+    requant_check(to_host(hc), to_host(hs), h_ref, sc["g2_inv"])
+    # bf16 h (W4A16 chain epilogue) is the rounding of the f32 one
+    hb = nv.gemm_swiglu(0, dxq, dxs, p_gu, I, H, scalar(sc["a_gu"]), h_dtype=torch.bfloat16)
+    assert np.array_equal(to_host(hb), synth.f32_to_bf16_bits(to_host(h32)))
+
+
+# -- MLP ------------------------------------------------------------------------
+
+def _run_mlp(mode, x, w, sc, p_gu, p_d):
+    if mode == "w4a4":
+        return nv.mlp_forward(0, to_dev(x), p_gu, scalar(sc["a_gu"]), p_d, scalar(sc["a_d"]), w["I"],
+                              g1_inv=scalar(sc["g1_inv"]), g2_inv=scalar(sc["g2_inv"]))
+    return nv.mlp_forward(1, to_dev(x), p_gu, scalar(w["g_gu"]), p_d, scalar(w["g_d"]), w["I"])
+
+
+def _check_mlp(mode, M, H, I, seed=0, outliers=False, rows=None):
+    w = mlp_weights(H, I, 0)
+    p_gu, p_d = packed_weights(H, I, 0)
+    x = synth.activations(seed, M, H, outliers=outliers)
+    sc = calibrate_activation_scales(x[:min(M, 64)], w) if mode == "w4a4" else None
+    y = to_host(_run_mlp(mode, x, w, sc, p_gu, p_d))
+    torch.cuda.synchronize()
+    sel = np.arange(M) if rows is None else rows
+    xs_ = x[sel]
+    if mode == "w4a4":
+        r = oracle.mlp_w4a4(xs_, w["c_gu"], w["s_gu"], sc["a_gu"], w["c_d"], w["s_d"], sc["a_d"],
+                            sc["g1_inv"], sc["g2_inv"])
+    else:
+        r = oracle.mlp_w4a16(xs_, w["c_gu"], w["s_gu"], w["g_gu"], w["c_d"], w["s_d"], w["g_d"])
+    gemm_close(y[sel], r["out"], f"mlp {mode} M={M} H={H} I={I}")
+    return y
+
+
+@pytest.mark.parametrize("mode", ["w4a4", "w4a16"])
+def test_mlp_tiny_workload(path, mode):
+    """M=4, hidden 256, intermediate 512, seed 0 (the tiny NVFP4 MLP)."""
+    _check_mlp(mode, 4, 256, 512)
+
+
+@pytest.mark.parametrize("M", [1, 7, 64, 200])
+def test_mlp_auto_dispatch(M):
+    nv.set_path(nv.PATH_AUTO)
+    _check_mlp("w4a4", M, 512, 768, seed=M)
+    _check_mlp("w4a16", M, 512, 768, seed=M)
+
+
+def test_mlp_decode_full_size():
+    """Decode W4A4: M=1, hidden 5120, intermediate 17408, outliers, three seeds."""
+    nv.set_path(nv.PATH_AUTO)
+    for seed in (0, 1, 999):
+        _check_mlp("w4a4", 1, 5120, 17408, seed=seed, outliers=True)
+
+
+@pytest.mark.parametrize("M", [1, 4, 16, 64])
+def test_mlp_small_batch_full_size(M):
+    """Fused W4A4 MLP, hidden 7168, intermediate 18432."""
+    nv.set_path(nv.PATH_AUTO)
+    _check_mlp("w4a4", M, 7168, 18432, rows=np.arange(min(M, 16)))
+
+
+def test_mlp_prefill_full_size_sampled_rows():
+    """Prefill W4A4: M=8192 on the GPU, 64 seeded rows checked by the oracle."""
+    nv.set_path(nv.PATH_AUTO)
+    rows = np.sort(np.random.default_rng(8192).choice(8192, 64, replace=False))
+    _check_mlp("w4a4", 8192, 7168, 18432, rows=rows)
+
+
+@pytest.mark.parametrize("M", [1, 16, 256, 4096])
+def test_mlp_w4a16_full_size(M):
+    nv.set_path(nv.PATH_AUTO)
+    rows = np.arange(M) if M <= 16 else np.sort(np.random.default_rng(M).choice(M, 32, replace=False))
+    _check_mlp("w4a16", M, 5120, 17408, rows=rows)
