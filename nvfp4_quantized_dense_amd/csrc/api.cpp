@@ -80,12 +80,30 @@ int choose_path(int64_t M) {
   return NVFP4_PATH_TILED;
 }
 
+// Kernels that address their operands with 32-bit buffer offsets: the packed
+// weight and the activation rows (including one tile of padding past M) must
+// stay below 2^31 bytes.
+bool fits_buffers(const nvfp4::GemmArgs& a, int mode) {
+  const int64_t lim = int64_t(1) << 31;
+  const int64_t row = mode == NVFP4_MODE_W4A4 ? a.K / 2 : a.K * 2;
+  return a.N * a.K / 16 * 9 < lim && (a.M + 256) * row < lim;
+}
+
 hipError_t run_gemm(int path, int mode, int epi, const nvfp4::GemmArgs& a, hipStream_t s) {
+  const bool fits = fits_buffers(a, mode);
   switch (path) {
-    case NVFP4_PATH_GEMV: return nvfp4::launch_valu_gemv(mode, epi, a, s);
-    case NVFP4_PATH_STREAM: return nvfp4::launch_stream_gemm(mode, epi, a, s);
-    default: return nvfp4::launch_tiled_gemm(mode, epi, a, s);
+    case NVFP4_PATH_GEMV:
+      if (fits) return nvfp4::launch_valu_gemv(mode, epi, a, s);
+      break;
+    case NVFP4_PATH_STREAM:
+      if (fits) return nvfp4::launch_stream_gemm(mode, epi, a, s);
+      break;
+    default:
+      if (mode == NVFP4_MODE_W4A4 && fits) return nvfp4::launch_tiled2_gemm(epi, a, s);
+      break;
   }
+  // Beyond 2^31-byte operands only the 64-bit-addressed tiled kernel runs.
+  return nvfp4::launch_tiled_gemm(mode, epi, a, s);
 }
 
 // Shared checks of the GEMM entry points. N is the packed row count.
@@ -102,6 +120,8 @@ int check_gemm(int mode, const void* a, const uint8_t* a_scales, const void* w, 
       return fail(NVFP4_ERR_INVALID_ARG, "activation, weight and output must be 16-byte aligned");
     if (mode == NVFP4_MODE_W4A4 && !a_scales)
       return fail(NVFP4_ERR_INVALID_ARG, "W4A4 needs activation scales");
+    if (mode == NVFP4_MODE_W4A4 && !aligned16(a_scales))
+      return fail(NVFP4_ERR_INVALID_ARG, "activation scales must be 16-byte aligned");
   }
   if (mode == NVFP4_MODE_W4A16 && a_scales)
     return fail(NVFP4_ERR_INVALID_ARG, "W4A16 takes bf16 activations: a_scales must be NULL");

@@ -125,6 +125,35 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
 
 // ---------------------------------------------------------------------------
+// Raw buffer loads (device pass only: the resource type is a GPU type). The
+// per-lane offset is range-checked against the resource's byte count and an
+// out-of-range load returns zeros without touching memory, so ragged token
+// rows and the "no next tile" case of a software pipeline need no branch.
+// ---------------------------------------------------------------------------
+#if defined(__HIP_DEVICE_COMPILE__)
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr uint32_t kOutOfRange = 0x80000000u;  // a lane offset past any buffer used here
+
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+// `nt`: streamed once (the packed weights), with a wave-uniform scalar base
+// `soff`; plain: re-read data, keep cached.
+__device__ __forceinline__ u32x4 bload16_nt(Rsrc r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 2);
+}
+__device__ __forceinline__ uint32_t bload4_nt(Rsrc r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 2);
+}
+__device__ __forceinline__ u32x4 bload16(Rsrc r, uint32_t voff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0);
+}
+__device__ __forceinline__ uint32_t bload2(Rsrc r, uint32_t voff) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, 0, 0);
+}
+#endif
+
+// ---------------------------------------------------------------------------
 // Epilogues. The MFMA 16x16x32 result tile of a lane holds rows 4(l/16)+r,
 // r = 0..3, of one token column l % 16.
 // ---------------------------------------------------------------------------

@@ -1,4 +1,4 @@
-// gemv.hip -- VALU GEMV for the smallest token counts (M <= 4), no MFMA.
+// gemv.hip -- VALU GEMV for the smallest token counts (decode), no MFMA.
 //
 // The decode fast path streams the packed weight with 16-byte loads and
 // does the arithmetic on the vector ALU with packed dot products: codes are
@@ -10,13 +10,20 @@
 // itself, of 16 products of grid values, is exact.
 //
 // Lane l owns row l % 16 of each row group and columns 32 (l / 16) + [0, 32)
-// of each 128-column half tile (the packed layout's lane order); the four
-// lanes of a row and the NW waves (which divide the K tiles) are summed at
-// the end in a fixed order.
+// of each 128-column half tile (the packed layout's lane order). NW waves
+// divide a row group's K tiles; each wave keeps the next tile's loads in
+// flight while it computes the current one (two register sets, no branch
+// around the prefetch: past the last tile it loads from out of range, which
+// returns zeros without a memory access). Token rows past M are out of range
+// of the activation buffers as well and read as zeros. The four lanes of a
+// row and the NW waves are summed at the end in a fixed order.
 #include "device_common.h"
 #include "kernels.h"
 
 namespace nvfp4 {
+
+#if defined(__HIP_DEVICE_COMPILE__)
+namespace {
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -31,23 +38,170 @@ __device__ __forceinline__ float dot2_bf16(bf16x2 w, uint32_t x, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(w, __builtin_bit_cast(bf16x2, x), acc, false);
 }
 
+template <int MODE, int MT>
+struct GemvSrc {
+  Rsrc w, a, s;
+  uint32_t a_row[MT];  // lane offset of each token row in the activation codes (W4A4) or bf16 (W4A16)
+  uint32_t s_row[MT];  // lane offset of each token row in the activation scales (W4A4)
+};
+
+// Loads of one K tile for one wave: NG weight tiles and (W4A4) the NVFP4
+// activation slices of MT tokens.
+template <int MODE, int NG, int MT>
+struct GemvTile {
+  u32x4 wc[NG][2];
+  uint32_t wsd[NG];
+  u32x4 xc[MODE == kW4A4 ? MT : 1][2];
+  uint32_t xsd[MODE == kW4A4 ? MT : 1];
+};
+
+template <int MODE, int NG, int MT>
+__device__ __forceinline__ void gemv_load(GemvTile<MODE, NG, MT>& d, const GemvSrc<MODE, MT>& src,
+                                          int64_t rg0, int64_t T, int64_t t, int lane) {
+  const int q = lane >> 4;
+  const bool in = t < T;
+  const uint32_t tw = in ? (uint32_t)(t * kTileBytes) : kOutOfRange;
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const uint32_t gbase = (uint32_t)((rg0 + g) * T * kTileBytes);
+    d.wc[g][0] = bload16_nt(src.w, tw + 16 * lane, gbase);
+    d.wc[g][1] = bload16_nt(src.w, tw + 1024 + 16 * lane, gbase);
+    d.wsd[g] = bload4_nt(src.w, tw + kTileCodeBytes + 4 * lane, gbase);
+  }
+  if constexpr (MODE == kW4A4) {
+    const uint32_t ta = in ? (uint32_t)(t * 128 + q * 16) : kOutOfRange;
+    const uint32_t ts = in ? (uint32_t)(t * 16 + q * 2) : kOutOfRange;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      d.xc[m][0] = bload16(src.a, src.a_row[m] + ta);
+      d.xc[m][1] = bload16(src.a, src.a_row[m] + ta + 64);
+      d.xsd[m] = bload2(src.s, src.s_row[m] + ts) | (bload2(src.s, src.s_row[m] + ts + 8) << 16);
+    }
+  }
+}
+
+template <int MODE, int NG, int MT>
+__device__ __forceinline__ void gemv_compute(float (&acc)[NG][MT], const GemvTile<MODE, NG, MT>& d,
+                                             const GemvSrc<MODE, MT>& src, int64_t t, int lane) {
+  float ws[NG][4];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    ws[g][0] = e4m3_to_f32<0>(d.wsd[g]); ws[g][1] = e4m3_to_f32<1>(d.wsd[g]);
+    ws[g][2] = e4m3_to_f32<2>(d.wsd[g]); ws[g][3] = e4m3_to_f32<3>(d.wsd[g]);
+  }
+  if constexpr (MODE == kW4A4) {
+    float xs[MT][4];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      xs[m][0] = e4m3_to_f32<0>(d.xsd[m]); xs[m][1] = e4m3_to_f32<1>(d.xsd[m]);
+      xs[m][2] = e4m3_to_f32<2>(d.xsd[m]); xs[m][3] = e4m3_to_f32<3>(d.xsd[m]);
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        f16x2 xp[MT][8];  // activation pairs of this block, unscaled
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+          for (int uu = 0; uu < 2; ++uu) {
+            const uint32_t v = d.xc[m][c][2 * blk + uu];
+            xp[m][4 * uu + 0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 0);
+            xp[m][4 * uu + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 1);
+            xp[m][4 * uu + 2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 2);
+            xp[m][4 * uu + 3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 3);
+          }
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+          float bs[MT];
+#pragma unroll
+          for (int m = 0; m < MT; ++m) bs[m] = 0.0f;
+#pragma unroll
+          for (int uu = 0; uu < 2; ++uu) {
+            const uint32_t v = d.wc[g][c][2 * blk + uu];
+            const f16x2 w0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 0);
+            const f16x2 w1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 1);
+            const f16x2 w2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 2);
+            const f16x2 w3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 3);
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+              bs[m] = __builtin_amdgcn_fdot2(w0, xp[m][4 * uu + 0], bs[m], false);
+              bs[m] = __builtin_amdgcn_fdot2(w1, xp[m][4 * uu + 1], bs[m], false);
+              bs[m] = __builtin_amdgcn_fdot2(w2, xp[m][4 * uu + 2], bs[m], false);
+              bs[m] = __builtin_amdgcn_fdot2(w3, xp[m][4 * uu + 3], bs[m], false);
+            }
+          }
+#pragma unroll
+          for (int m = 0; m < MT; ++m)
+            acc[g][m] = __builtin_fmaf(bs[m], ws[g][2 * c + blk] * xs[m][2 * c + blk], acc[g][m]);
+        }
+      }
+  } else {
+    const int q = lane >> 4;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      u32x4 xv[MT][4];
+      const uint32_t tx = (uint32_t)((t * kTileK + c * 128 + q * 32) * 2);
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) xv[m][u] = bload16(src.a, src.a_row[m] + tx + 16 * u);
+#pragma unroll
+      for (int g = 0; g < NG; ++g)
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+          float bs[MT];
+#pragma unroll
+          for (int m = 0; m < MT; ++m) bs[m] = 0.0f;
+#pragma unroll
+          for (int uu = 0; uu < 2; ++uu) {
+            const int u = 2 * blk + uu;
+            const uint32_t v = d.wc[g][c][u];
+            bf16x2 w[4];
+            w[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, 0);
+            w[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, 1);
+            w[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, 2);
+            w[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, 3);
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+              for (int p = 0; p < 4; ++p) bs[m] = dot2_bf16(w[p], xv[m][u][p], bs[m]);
+          }
+#pragma unroll
+          for (int m = 0; m < MT; ++m) acc[g][m] = __builtin_fmaf(bs[m], ws[g][2 * c + blk], acc[g][m]);
+        }
+    }
+  }
+}
+
+}  // namespace
+#endif  // __HIP_DEVICE_COMPILE__
+
 template <int MODE, int EPI, int MT, int NW>
 __global__ __launch_bounds__(NW * 64) void k_valu_gemv(GemmArgs args) {
+#if defined(__HIP_DEVICE_COMPILE__)
   constexpr int NG = EpiTraits<EPI>::swiglu ? 2 : 1;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int q = lane >> 4;
-  const int64_t K = args.K;
-  const int64_t T = K / kTileK;
+  const int64_t K = args.K, T = K / kTileK;
   const int64_t rg0 = (int64_t)blockIdx.x * NG;
   const int64_t tok0 = (int64_t)blockIdx.y * MT;
 
-  int64_t trow[MT];
-  bool tvalid[MT];
+  GemvSrc<MODE, MT> src;
+  src.w = make_rsrc(args.w, (uint32_t)(args.N / kTileRows * T * kTileBytes));
+  if constexpr (MODE == kW4A4) {
+    src.a = make_rsrc(args.a, (uint32_t)(args.M * (K / 2)));
+    src.s = make_rsrc(args.a_scales, (uint32_t)(args.M * (K / 16)));
+  } else {
+    src.a = make_rsrc(args.a, (uint32_t)(args.M * K * 2));
+    src.s = src.a;
+  }
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
-    tvalid[m] = tok0 + m < args.M;
-    trow[m] = tvalid[m] ? tok0 + m : 0;  // rows past M read row 0, then zeroed
+    // rows past M start past the end of the buffer: they read as zeros
+    src.a_row[m] = (uint32_t)((tok0 + m) * (MODE == kW4A4 ? K / 2 : K * 2));
+    src.s_row[m] = (uint32_t)((tok0 + m) * (K / 16));
   }
 
   float acc[NG][MT];
@@ -56,122 +210,18 @@ __global__ __launch_bounds__(NW * 64) void k_valu_gemv(GemmArgs args) {
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[g][m] = 0.0f;
 
-  for (int64_t t = wave; t < T; t += NW) {
-    u32x4 wc[NG][2];
-    uint32_t wsd[NG];
-#pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      const uint8_t* tp = args.w + ((rg0 + g) * T + t) * kTileBytes;
-      wc[g][0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(tp + 16 * lane));
-      wc[g][1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(tp + 1024 + 16 * lane));
-      wsd[g] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(tp + kTileCodeBytes + 4 * lane));
-    }
-    float ws[NG][4];
-#pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      ws[g][0] = e4m3_to_f32<0>(wsd[g]); ws[g][1] = e4m3_to_f32<1>(wsd[g]);
-      ws[g][2] = e4m3_to_f32<2>(wsd[g]); ws[g][3] = e4m3_to_f32<3>(wsd[g]);
-    }
-    if constexpr (MODE == kW4A4) {
-      const uint8_t* ac = reinterpret_cast<const uint8_t*>(args.a);
-      u32x4 xc[MT][2];
-      float xs[MT][4];
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        const uint8_t* row = ac + trow[m] * (K / 2) + t * 128 + q * 16;
-        u32x4 c0 = *reinterpret_cast<const u32x4*>(row);
-        u32x4 c1 = *reinterpret_cast<const u32x4*>(row + 64);
-        const uint8_t* srow = args.a_scales + trow[m] * (K / 16) + t * 16 + q * 2;
-        uint32_t sd = (uint32_t)*reinterpret_cast<const uint16_t*>(srow) |
-                      ((uint32_t)*reinterpret_cast<const uint16_t*>(srow + 8) << 16);
-        const u32x4 z = {0, 0, 0, 0};
-        xc[m][0] = tvalid[m] ? c0 : z;
-        xc[m][1] = tvalid[m] ? c1 : z;
-        sd = tvalid[m] ? sd : 0u;
-        xs[m][0] = e4m3_to_f32<0>(sd); xs[m][1] = e4m3_to_f32<1>(sd);
-        xs[m][2] = e4m3_to_f32<2>(sd); xs[m][3] = e4m3_to_f32<3>(sd);
-      }
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-          // activation pairs of this block, unscaled
-          f16x2 xp[MT][8];
-#pragma unroll
-          for (int m = 0; m < MT; ++m)
-#pragma unroll
-            for (int uu = 0; uu < 2; ++uu) {
-              const uint32_t d = xc[m][c][2 * blk + uu];
-              xp[m][4 * uu + 0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 0);
-              xp[m][4 * uu + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 1);
-              xp[m][4 * uu + 2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 2);
-              xp[m][4 * uu + 3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 3);
-            }
-#pragma unroll
-          for (int g = 0; g < NG; ++g) {
-            float bs[MT];
-#pragma unroll
-            for (int m = 0; m < MT; ++m) bs[m] = 0.0f;
-#pragma unroll
-            for (int uu = 0; uu < 2; ++uu) {
-              const uint32_t d = wc[g][c][2 * blk + uu];
-              f16x2 w0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 0);
-              f16x2 w1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 1);
-              f16x2 w2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 2);
-              f16x2 w3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 3);
-#pragma unroll
-              for (int m = 0; m < MT; ++m) {
-                bs[m] = __builtin_amdgcn_fdot2(w0, xp[m][4 * uu + 0], bs[m], false);
-                bs[m] = __builtin_amdgcn_fdot2(w1, xp[m][4 * uu + 1], bs[m], false);
-                bs[m] = __builtin_amdgcn_fdot2(w2, xp[m][4 * uu + 2], bs[m], false);
-                bs[m] = __builtin_amdgcn_fdot2(w3, xp[m][4 * uu + 3], bs[m], false);
-              }
-            }
-#pragma unroll
-            for (int m = 0; m < MT; ++m)
-              acc[g][m] = __builtin_fmaf(bs[m], ws[g][2 * c + blk] * xs[m][2 * c + blk], acc[g][m]);
-          }
-        }
-    } else {
-      const uint16_t* xa = reinterpret_cast<const uint16_t*>(args.a);
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        u32x4 xv[MT][4];
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-          const u32x4* row = reinterpret_cast<const u32x4*>(xa + trow[m] * K + t * kTileK + c * 128 + q * 32);
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            u32x4 v = row[u];
-            xv[m][u] = tvalid[m] ? v : u32x4{0, 0, 0, 0};
-          }
-        }
-#pragma unroll
-        for (int g = 0; g < NG; ++g)
-#pragma unroll
-          for (int blk = 0; blk < 2; ++blk) {
-            float bs[MT];
-#pragma unroll
-            for (int m = 0; m < MT; ++m) bs[m] = 0.0f;
-#pragma unroll
-            for (int uu = 0; uu < 2; ++uu) {
-              const int u = 2 * blk + uu;
-              const uint32_t d = wc[g][c][u];
-              bf16x2 w[4];
-              w[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, 1.0f, 0);
-              w[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, 1.0f, 1);
-              w[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, 1.0f, 2);
-              w[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, 1.0f, 3);
-#pragma unroll
-              for (int m = 0; m < MT; ++m)
-#pragma unroll
-                for (int p = 0; p < 4; ++p) bs[m] = dot2_bf16(w[p], xv[m][u][p], bs[m]);
-            }
-#pragma unroll
-            for (int m = 0; m < MT; ++m) acc[g][m] = __builtin_fmaf(bs[m], ws[g][2 * c + blk], acc[g][m]);
-          }
-      }
-    }
+  // Tiles t = wave, wave + NW, ...; two register sets alternate.
+  int64_t t = wave;
+  GemvTile<MODE, NG, MT> ta, tb;
+  gemv_load<MODE, NG, MT>(ta, src, rg0, T, t, lane);
+  while (t < T) {
+    gemv_load<MODE, NG, MT>(tb, src, rg0, T, t + NW, lane);
+    gemv_compute<MODE, NG, MT>(acc, ta, src, t, lane);
+    t += NW;
+    if (t >= T) break;
+    gemv_load<MODE, NG, MT>(ta, src, rg0, T, t + NW, lane);
+    gemv_compute<MODE, NG, MT>(acc, tb, src, t, lane);
+    t += NW;
   }
 
   // Sum the four lanes of each row (xor 16, then 32), then the waves.
@@ -216,15 +266,29 @@ __global__ __launch_bounds__(NW * 64) void k_valu_gemv(GemmArgs args) {
   } else {
     store_dense<EPI>(res[0], alpha, lvalid, token, rg0 * kTileRows + 4 * q, args.N, args.out);
   }
+#endif  // __HIP_DEVICE_COMPILE__
 }
 
-template <int MODE, int EPI, int MT>
-static hipError_t launch_mt(const GemmArgs& a, hipStream_t s) {
+template <int MODE, int EPI, int MT, int NW>
+static hipError_t launch_mt_nw(const GemmArgs& a, hipStream_t s) {
   constexpr int NG = EpiTraits<EPI>::swiglu ? 2 : 1;
-  constexpr int NW = 4;
   dim3 grid((unsigned)(a.N / kTileRows / NG), (unsigned)((a.M + MT - 1) / MT));
   k_valu_gemv<MODE, EPI, MT, NW><<<grid, NW * 64, 0, s>>>(a);
   return hipGetLastError();
+}
+
+// Waves per workgroup: enough that the grid keeps about 16 waves per CU
+// streaming (small grids such as down_proj's get 16-wave workgroups).
+// (16-wave workgroups only where the tile fits 128 VGPRs per lane.)
+template <int MODE, int EPI, int MT>
+static hipError_t launch_mt(const GemmArgs& a, hipStream_t s) {
+  constexpr int NG = EpiTraits<EPI>::swiglu ? 2 : 1;
+  const int64_t wgs = a.N / kTileRows / NG * ((a.M + MT - 1) / MT);
+  if (wgs >= 1024) return launch_mt_nw<MODE, EPI, MT, 4>(a, s);
+  if constexpr (MT <= 2) {
+    if (wgs < 512) return launch_mt_nw<MODE, EPI, MT, 16>(a, s);
+  }
+  return launch_mt_nw<MODE, EPI, MT, 8>(a, s);
 }
 
 template <int MODE, int EPI>
@@ -234,6 +298,8 @@ static hipError_t launch_me(const GemmArgs& a, hipStream_t s) {
   return launch_mt<MODE, EPI, 4>(a, s);
 }
 
+// Needs the packed weight and the activations below 2^31 bytes (32-bit
+// buffer offsets); the caller checks.
 hipError_t launch_valu_gemv(int mode, int epi, const GemmArgs& a, hipStream_t s) {
   if (a.M == 0) return hipSuccess;
   if (mode == kW4A4) {

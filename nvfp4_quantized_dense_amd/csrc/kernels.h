@@ -41,5 +41,7 @@ struct GemmArgs {
 hipError_t launch_stream_gemm(int mode, int epi, const GemmArgs& a, hipStream_t s);
 hipError_t launch_valu_gemv(int mode, int epi, const GemmArgs& a, hipStream_t s);
 hipError_t launch_tiled_gemm(int mode, int epi, const GemmArgs& a, hipStream_t s);
+// W4A4 only; packed weight, activation codes and scales each < 2^31 bytes.
+hipError_t launch_tiled2_gemm(int epi, const GemmArgs& a, hipStream_t s);
 
 }  // namespace nvfp4

@@ -1,40 +1,160 @@
 // stream.hip -- weight-streaming MFMA GEMM for small token counts.
 //
-// Decode-sized GEMMs are bound by HBM reads of the packed weight (0.5625
+// Small-batch GEMMs are bound by HBM reads of the packed weight (0.5625
 // bytes per element), so each workgroup streams whole packed tiles with
 // 16-byte loads and spends the MFMA unit only on the contraction: the weight
 // rows are the 16-row A operand of v_mfma_f32_16x16x32 (f16 for W4A4, bf16
-// for W4A16) and up to four groups of 16 tokens are the B operand. Tokens
-// beyond M are zero columns. Activations are read from global memory (they
-// are tiny and stay in L2) in their NVFP4 or bf16 form and dequantized in
-// registers exactly like the weights.
+// for W4A16) and up to four groups of 16 tokens are the B operand. Token rows
+// past M lie out of range of the activation buffers and read as zeros.
+// Activations are read from global memory (they are small and stay in L2) in
+// their NVFP4 or bf16 form and dequantized in registers like the weights.
 //
 // Work split: a workgroup owns NG packed row groups (2 for the SwiGLU pair
-// gate/up) and NW waves divide the K tiles between them; the partial sums
-// are combined through LDS in a fixed order, so results are deterministic.
+// gate/up) and NW waves divide the K tiles between them; each wave keeps the
+// next tile's loads in flight while it multiplies the current one (two
+// register sets, branch-free prefetch). Partial sums are combined through LDS
+// in a fixed order (deterministic).
 #include "device_common.h"
 #include "kernels.h"
 
 namespace nvfp4 {
 
+#if defined(__HIP_DEVICE_COMPILE__)
+namespace {
+
+template <int MODE, int NT>
+struct StreamSrc {
+  Rsrc w, a, s;
+  uint32_t a_row[NT];  // lane offset of this lane's token row, per token group
+  uint32_t s_row[NT];
+};
+
+template <int MODE, int NG, int NT>
+struct StreamTile {
+  u32x4 wc[NG][2];
+  uint32_t wsd[NG];
+  u32x4 xc[MODE == kW4A4 ? NT : 1][2];
+  uint32_t xsd[MODE == kW4A4 ? NT : 1];
+};
+
+template <int MODE, int NG, int NT>
+__device__ __forceinline__ void stream_load(StreamTile<MODE, NG, NT>& d, const StreamSrc<MODE, NT>& src,
+                                            int64_t rg0, int64_t T, int64_t t, int lane) {
+  const int q = lane >> 4;
+  const bool in = t < T;
+  const uint32_t tw = in ? (uint32_t)(t * kTileBytes) : kOutOfRange;
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const uint32_t gbase = (uint32_t)((rg0 + g) * T * kTileBytes);
+    d.wc[g][0] = bload16_nt(src.w, tw + 16 * lane, gbase);
+    d.wc[g][1] = bload16_nt(src.w, tw + 1024 + 16 * lane, gbase);
+    d.wsd[g] = bload4_nt(src.w, tw + kTileCodeBytes + 4 * lane, gbase);
+  }
+  if constexpr (MODE == kW4A4) {
+    const uint32_t ta = in ? (uint32_t)(t * 128 + q * 16) : kOutOfRange;
+    const uint32_t ts = in ? (uint32_t)(t * 16 + q * 2) : kOutOfRange;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      d.xc[j][0] = bload16(src.a, src.a_row[j] + ta);
+      d.xc[j][1] = bload16(src.a, src.a_row[j] + ta + 64);
+      d.xsd[j] = bload2(src.s, src.s_row[j] + ts) | (bload2(src.s, src.s_row[j] + ts + 8) << 16);
+    }
+  }
+}
+
+template <int MODE, int NG, int NT>
+__device__ __forceinline__ void stream_compute(f32x4 (&acc)[NG][NT], const StreamTile<MODE, NG, NT>& d,
+                                               const StreamSrc<MODE, NT>& src, int64_t t, int lane) {
+  if constexpr (MODE == kW4A4) {
+    _Float16 ws[NG][4], xs[NT][4];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      ws[g][0] = scale_f16<0>(d.wsd[g]); ws[g][1] = scale_f16<1>(d.wsd[g]);
+      ws[g][2] = scale_f16<2>(d.wsd[g]); ws[g][3] = scale_f16<3>(d.wsd[g]);
+    }
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      xs[j][0] = scale_f16<0>(d.xsd[j]); xs[j][1] = scale_f16<1>(d.xsd[j]);
+      xs[j][2] = scale_f16<2>(d.xsd[j]); xs[j][3] = scale_f16<3>(d.xsd[j]);
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int sb = 2 * c + (u >> 1);
+        f16x8 A[NG], B[NT];
+#pragma unroll
+        for (int g = 0; g < NG; ++g) A[g] = deq8_f16(d.wc[g][c][u], ws[g][sb]);
+#pragma unroll
+        for (int j = 0; j < NT; ++j) B[j] = deq8_f16(d.xc[j][c][u], xs[j][sb]);
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+#pragma unroll
+          for (int j = 0; j < NT; ++j) acc[g][j] = mfma16x16x32(A[g], B[j], acc[g][j]);
+      }
+  } else {
+    const int q = lane >> 4;
+    float ws[NG][4];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      ws[g][0] = e4m3_to_f32<0>(d.wsd[g]); ws[g][1] = e4m3_to_f32<1>(d.wsd[g]);
+      ws[g][2] = e4m3_to_f32<2>(d.wsd[g]); ws[g][3] = e4m3_to_f32<3>(d.wsd[g]);
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      u32x4 xv[NT][4];
+      const uint32_t tx = (uint32_t)((t * kTileK + c * 128 + q * 32) * 2);
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) xv[j][u] = bload16(src.a, src.a_row[j] + tx + 16 * u);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int sb = 2 * c + (u >> 1);
+        bf16x8 A[NG];
+#pragma unroll
+        for (int g = 0; g < NG; ++g) A[g] = deq8_bf16(d.wc[g][c][u], ws[g][sb]);
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+#pragma unroll
+          for (int j = 0; j < NT; ++j) acc[g][j] = mfma16x16x32(A[g], as_bf16x8(xv[j][u]), acc[g][j]);
+      }
+    }
+  }
+}
+
+}  // namespace
+#endif  // __HIP_DEVICE_COMPILE__
+
 template <int MODE, int EPI, int NT, int NW>
 __global__ __launch_bounds__(NW * 64) void k_stream(GemmArgs args) {
+#if defined(__HIP_DEVICE_COMPILE__)
   constexpr int NG = EpiTraits<EPI>::swiglu ? 2 : 1;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int q = lane >> 4;
   const int tl = lane & 15;
-  const int64_t K = args.K;
-  const int64_t T = K / kTileK;
+  const int64_t K = args.K, T = K / kTileK;
   const int64_t rg0 = (int64_t)blockIdx.x * NG;
   const int64_t tok0 = (int64_t)blockIdx.y * 16 * NT;
 
+  StreamSrc<MODE, NT> src;
+  src.w = make_rsrc(args.w, (uint32_t)(args.N / kTileRows * T * kTileBytes));
+  if constexpr (MODE == kW4A4) {
+    src.a = make_rsrc(args.a, (uint32_t)(args.M * (K / 2)));
+    src.s = make_rsrc(args.a_scales, (uint32_t)(args.M * (K / 16)));
+  } else {
+    src.a = make_rsrc(args.a, (uint32_t)(args.M * K * 2));
+    src.s = src.a;
+  }
   int64_t tok[NT];
   bool tvalid[NT];
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
     tok[j] = tok0 + 16 * j + tl;
     tvalid[j] = tok[j] < args.M;
+    src.a_row[j] = (uint32_t)(tok[j] * (MODE == kW4A4 ? K / 2 : K * 2));  // past M: out of range
+    src.s_row[j] = (uint32_t)(tok[j] * (K / 16));
   }
 
   f32x4 acc[NG][NT];
@@ -43,98 +163,17 @@ __global__ __launch_bounds__(NW * 64) void k_stream(GemmArgs args) {
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[g][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const uint8_t* wbase = args.w;
-  for (int64_t t = wave; t < T; t += NW) {
-    // Weight tiles: two 16-byte code chunks and one scale dword per lane.
-    u32x4 wc[NG][2];
-    uint32_t wsd[NG];
-#pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      const uint8_t* tp = wbase + ((rg0 + g) * T + t) * kTileBytes;
-      wc[g][0] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(tp + 16 * lane));
-      wc[g][1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(tp + 1024 + 16 * lane));
-      wsd[g] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(tp + kTileCodeBytes + 4 * lane));
-    }
-    if constexpr (MODE == kW4A4) {
-      const uint8_t* ac = reinterpret_cast<const uint8_t*>(args.a);
-      u32x4 xc[NT][2];
-      uint32_t xsd[NT];
-#pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        // Rows past M read row 0 (always present) and are zeroed: no address
-        // beyond the activation is ever formed.
-        const int64_t trow = tvalid[j] ? tok[j] : 0;
-        const uint8_t* row = ac + trow * (K / 2) + t * 128 + q * 16;
-        u32x4 c0 = *reinterpret_cast<const u32x4*>(row);
-        u32x4 c1 = *reinterpret_cast<const u32x4*>(row + 64);
-        const uint8_t* srow = args.a_scales + trow * (K / 16) + t * 16 + q * 2;
-        uint32_t lo = *reinterpret_cast<const uint16_t*>(srow);
-        uint32_t hi = *reinterpret_cast<const uint16_t*>(srow + 8);
-        const u32x4 z = {0, 0, 0, 0};
-        xc[j][0] = tvalid[j] ? c0 : z;
-        xc[j][1] = tvalid[j] ? c1 : z;
-        xsd[j] = tvalid[j] ? (lo | (hi << 16)) : 0u;
-      }
-      _Float16 ws[NG][4], xs[NT][4];
-#pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        ws[g][0] = scale_f16<0>(wsd[g]); ws[g][1] = scale_f16<1>(wsd[g]);
-        ws[g][2] = scale_f16<2>(wsd[g]); ws[g][3] = scale_f16<3>(wsd[g]);
-      }
-#pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        xs[j][0] = scale_f16<0>(xsd[j]); xs[j][1] = scale_f16<1>(xsd[j]);
-        xs[j][2] = scale_f16<2>(xsd[j]); xs[j][3] = scale_f16<3>(xsd[j]);
-      }
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int sb = 2 * c + (u >> 1);
-          f16x8 A[NG], B[NT];
-#pragma unroll
-          for (int g = 0; g < NG; ++g) A[g] = deq8_f16(wc[g][c][u], ws[g][sb]);
-#pragma unroll
-          for (int j = 0; j < NT; ++j) B[j] = deq8_f16(xc[j][c][u], xs[j][sb]);
-#pragma unroll
-          for (int g = 0; g < NG; ++g)
-#pragma unroll
-            for (int j = 0; j < NT; ++j) acc[g][j] = mfma16x16x32(A[g], B[j], acc[g][j]);
-        }
-    } else {
-      const uint16_t* xa = reinterpret_cast<const uint16_t*>(args.a);
-      float ws[NG][4];
-#pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        ws[g][0] = e4m3_to_f32<0>(wsd[g]); ws[g][1] = e4m3_to_f32<1>(wsd[g]);
-        ws[g][2] = e4m3_to_f32<2>(wsd[g]); ws[g][3] = e4m3_to_f32<3>(wsd[g]);
-      }
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        u32x4 xv[NT][4];
-#pragma unroll
-        for (int j = 0; j < NT; ++j) {
-          const int64_t trow = tvalid[j] ? tok[j] : 0;
-          const u32x4* row = reinterpret_cast<const u32x4*>(xa + trow * K + t * kTileK + c * 128 + q * 32);
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            u32x4 v = row[u];
-            xv[j][u] = tvalid[j] ? v : u32x4{0, 0, 0, 0};
-          }
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int sb = 2 * c + (u >> 1);
-          bf16x8 A[NG];
-#pragma unroll
-          for (int g = 0; g < NG; ++g) A[g] = deq8_bf16(wc[g][c][u], ws[g][sb]);
-#pragma unroll
-          for (int g = 0; g < NG; ++g)
-#pragma unroll
-            for (int j = 0; j < NT; ++j) acc[g][j] = mfma16x16x32(A[g], as_bf16x8(xv[j][u]), acc[g][j]);
-        }
-      }
-    }
+  int64_t t = wave;
+  StreamTile<MODE, NG, NT> ta, tb;
+  stream_load<MODE, NG, NT>(ta, src, rg0, T, t, lane);
+  while (t < T) {
+    stream_load<MODE, NG, NT>(tb, src, rg0, T, t + NW, lane);
+    stream_compute<MODE, NG, NT>(acc, ta, src, t, lane);
+    t += NW;
+    if (t >= T) break;
+    stream_load<MODE, NG, NT>(ta, src, rg0, T, t + NW, lane);
+    stream_compute<MODE, NG, NT>(acc, tb, src, t, lane);
+    t += NW;
   }
 
   // Combine the waves' partial sums in wave order.
@@ -154,7 +193,7 @@ __global__ __launch_bounds__(NW * 64) void k_stream(GemmArgs args) {
       for (int g = 0; g < NG; ++g)
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
-          f32x4 p = red[w][g * NT + j][lane];
+          const f32x4 p = red[w][g * NT + j][lane];
           acc[g][j] = f32x4{acc[g][j][0] + p[0], acc[g][j][1] + p[1], acc[g][j][2] + p[2],
                             acc[g][j][3] + p[3]};
         }
@@ -177,15 +216,34 @@ __global__ __launch_bounds__(NW * 64) void k_stream(GemmArgs args) {
         store_dense<EPI>(acc[g][j], alpha, tvalid[j], tok[j], (rg0 + g) * kTileRows + 4 * q, args.N,
                          args.out);
   }
+#endif  // __HIP_DEVICE_COMPILE__
 }
 
-template <int MODE, int EPI, int NT>
-static hipError_t launch_nt(const GemmArgs& a, hipStream_t s) {
+template <int MODE, int EPI, int NT, int NW>
+static hipError_t launch_nt_nw(const GemmArgs& a, hipStream_t s) {
   constexpr int NG = EpiTraits<EPI>::swiglu ? 2 : 1;
-  constexpr int NW = 4;
   dim3 grid((unsigned)(a.N / kTileRows / NG), (unsigned)((a.M + 16 * NT - 1) / (16 * NT)));
   k_stream<MODE, EPI, NT, NW><<<grid, NW * 64, 0, s>>>(a);
   return hipGetLastError();
+}
+
+// Waves per workgroup: enough that the grid keeps about 16 waves per CU,
+// capped where two register sets of NT token groups would not fit the
+// per-lane register budget of larger workgroups (16 waves: 128 VGPRs).
+template <int MODE, int EPI, int NT>
+static hipError_t launch_nt(const GemmArgs& a, hipStream_t s) {
+  constexpr int NG = EpiTraits<EPI>::swiglu ? 2 : 1;
+  const int64_t wgs = a.N / kTileRows / NG * ((a.M + 16 * NT - 1) / (16 * NT));
+  if constexpr (NT >= 3) {
+    return launch_nt_nw<MODE, EPI, NT, 4>(a, s);
+  } else if constexpr (NT == 2) {
+    if (wgs >= 1024) return launch_nt_nw<MODE, EPI, NT, 4>(a, s);
+    return launch_nt_nw<MODE, EPI, NT, 8>(a, s);
+  } else {
+    if (wgs >= 1024) return launch_nt_nw<MODE, EPI, NT, 4>(a, s);
+    if (wgs >= 512) return launch_nt_nw<MODE, EPI, NT, 8>(a, s);
+    return launch_nt_nw<MODE, EPI, NT, 16>(a, s);
+  }
 }
 
 template <int MODE, int EPI>
@@ -197,6 +255,8 @@ static hipError_t launch_mode_epi(const GemmArgs& a, hipStream_t s) {
   return launch_nt<MODE, EPI, 4>(a, s);
 }
 
+// Needs the packed weight and the activations below 2^31 bytes (32-bit
+// buffer offsets); the caller checks.
 hipError_t launch_stream_gemm(int mode, int epi, const GemmArgs& a, hipStream_t s) {
   if (a.M == 0) return hipSuccess;
   if (mode == kW4A4) {

@@ -266,3 +266,67 @@ def test_mlp_w4a16_full_size(M):
     nv.set_path(nv.PATH_AUTO)
     rows = np.arange(M) if M <= 16 else np.sort(np.random.default_rng(M).choice(M, 32, replace=False))
     _check_mlp("w4a16", M, 5120, 17408, rows=rows)
+
+
+# -- every kernel instantiation: waves per workgroup (16, 8, 4) x token tiles --
+
+# 17, 513 and 1025 row groups select 16-, 8- and 4-wave workgroups.
+WAVE_N = [272, 8208, 16400]
+M_FOR = {"gemv": [1, 2, 3], "stream": [5, 20, 40, 60]}
+
+
+@pytest.mark.parametrize("kpath", ["gemv", "stream"])
+@pytest.mark.parametrize("N", WAVE_N)
+@pytest.mark.parametrize("mode", ["w4a4", "w4a16"])
+def test_gemm_wave_variants(kpath, N, mode):
+    prev = nv.set_path(PATHS[kpath])
+    try:
+        rng = np.random.default_rng(N)
+        K = 512
+        wc, ws = rand_nvfp4(rng, N, K)
+        p = nv.nvfp4_repack_weight(0, to_dev(wc), to_dev(ws))
+        for M in M_FOR[kpath]:
+            if mode == "w4a4":
+                ac, as_ = rand_nvfp4(rng, M, K)
+                ref = oracle.gemm_w4a4(ac, as_, wc, ws, np.float32(0.5))
+                y = nv.nvfp4_gemm(0, to_dev(ac), to_dev(as_), p, N, K, scalar(0.5))
+            else:
+                x = synth.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+                ref = oracle.gemm_w4a16(x, wc, ws, np.float32(0.5))
+                y = nv.nvfp4_gemm(1, to_dev(x), None, p, N, K, scalar(0.5))
+            gemm_close(to_host(y), ref, f"{kpath} {mode} N={N} M={M}")
+    finally:
+        nv.set_path(prev)
+
+
+@pytest.mark.parametrize("kpath", ["gemv", "stream"])
+@pytest.mark.parametrize("I", [256, 8208, 16400])
+def test_swiglu_wave_variants(kpath, I):
+    """SwiGLU epilogues (f32, bf16, NVFP4) at 16-, 8- and 4-wave workgroups."""
+    prev = nv.set_path(PATHS[kpath])
+    try:
+        rng = np.random.default_rng(I)
+        H = 512
+        wc, ws = rand_nvfp4(rng, 2 * I, H)
+        p = nv.nvfp4_repack_weight(1, to_dev(wc), to_dev(ws))
+        for M in M_FOR[kpath]:
+            ac, as_ = rand_nvfp4(rng, M, H)
+            alpha = np.float32(0.01)
+            h_ref = oracle.swiglu(oracle.gemm_w4a4(ac, as_, wc, ws, alpha))
+            h32 = nv.gemm_swiglu(0, to_dev(ac), to_dev(as_), p, I, H, scalar(alpha), h_dtype=torch.float32)
+            gemm_close(to_host(h32), h_ref, f"{kpath} swiglu I={I} M={M}")
+            _, g2_inv = oracle.global_scale(h_ref)
+            hc, hs = nv.gemm_swiglu_nvfp4_quant(to_dev(ac), to_dev(as_), p, I, H, scalar(alpha), scalar(g2_inv))
+            oc, os_ = oracle.quantize(to_host(h32), g2_inv)
+            assert np.array_equal(to_host(hc), oc) and np.array_equal(to_host(hs), os_)
+            hb = nv.gemm_swiglu(0, to_dev(ac), to_dev(as_), p, I, H, scalar(alpha), h_dtype=torch.bfloat16)
+            assert np.array_equal(to_host(hb), synth.f32_to_bf16_bits(to_host(h32)))
+            # W4A16 with the same weights
+            x = synth.f32_to_bf16_bits(rng.standard_normal((M, H)).astype(np.float32))
+            h_ref16 = oracle.swiglu(oracle.gemm_w4a16(x, wc, ws, alpha))
+            for dt in (torch.float32, torch.bfloat16):
+                hh = nv.gemm_swiglu(1, to_dev(x), None, p, I, H, scalar(alpha), h_dtype=dt)
+                gemm_close(to_host(hh).astype(np.float32) if dt == torch.float32 else
+                           synth.bf16_bits_to_f32(to_host(hh)), h_ref16, f"{kpath} w4a16 swiglu I={I} M={M}")
+    finally:
+        nv.set_path(prev)
