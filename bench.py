@@ -15,6 +15,8 @@ run of that kernel on the stream it runs on; `cpu_baseline` is the CPU
 oracle timed on a bounded sample of the same workload.
 """
 import argparse
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -67,6 +69,31 @@ def algorithmic(M, H, I, mode, out_bytes):
     flops_down = 2.0 * M * H * I
     return dict(quant=quant, fused=fused, down=down, total=quant + fused + down,
                 flops_fused=flops_fused, flops=flops_fused + flops_down)
+
+
+def kernel_source_hash() -> str:
+    """sha256[:16] over the kernel sources, as recorded in profiles/*.md."""
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "nvfp4_quantized_dense_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str, M: int):
+    """HBM bytes per launch of the dominant kernel from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, if the kernels are unchanged
+    since those counters were taken; else None."""
+    src = kernel_source_hash()
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        with open(path) as fh:
+            for line in fh:
+                if not line.startswith("bench-traffic:"):
+                    continue
+                kv = dict(t.split("=", 1) for t in line.split()[1:] if "=" in t)
+                if kv.get("workload") == workload and kv.get("M") == str(M) and kv.get("src") == src:
+                    return float(kv["bytes_per_launch"])
+    return None
 
 
 def prepare_weights(H, I, dev, copies):
@@ -143,7 +170,19 @@ def main():
     ap.add_argument("--path", type=int, default=0, help="kernel class override (0 = auto)")
     ap.add_argument("--sweep", default=None,
                     help="comma-separated token counts: one JSON line per M on the same weights")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run 5 device-to-device copies of BYTES bytes (a plain copy kernel of "
+                         "known size, to scale the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        n = args.copy_calibration
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 5}))
+        return
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
@@ -253,6 +292,7 @@ def run_one(args, dev, M, H, I, mode, outliers, n_seeds, steps, warmup, copies, 
         achieved = alg["fused"] / (fused_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "traffic": None}
+    roof["traffic"] = recorded_traffic(args.workload, M)
     roof["kernel"] = "gemm_swiglu_nvfp4_quant" if mode == "w4a4" else "gemm_swiglu(w4a16, bf16 h)"
     roof["kernel_us"] = fused_ms * 1e3
     roof["launches_timed"] = n_k
