@@ -72,7 +72,8 @@ extern "C" {
 
 /* Kernel-class override for tests and benchmarks (process-wide). */
 #define NVFP4_PATH_AUTO 0    /* choose by M */
-#define NVFP4_PATH_GEMV 1    /* weight-streaming VALU GEMV, no MFMA (M <= 4) */
+#define NVFP4_PATH_GEMV 1    /* decode GEMV sized for M <= 2: W4A4 on the FP4 matrix core with the
+                                blocks kept apart, W4A16 on the vector ALU (any M) */
 #define NVFP4_PATH_STREAM 2  /* weight-streaming MFMA kernel (any M, sized for M <= 64) */
 #define NVFP4_PATH_TILED 3   /* LDS-tiled MFMA GEMM (any M) */
 

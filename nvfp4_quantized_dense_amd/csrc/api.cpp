@@ -93,7 +93,10 @@ hipError_t run_gemm(int path, int mode, int epi, const nvfp4::GemmArgs& a, hipSt
   const bool fits = fits_buffers(a, mode);
   switch (path) {
     case NVFP4_PATH_GEMV:
-      if (fits) return nvfp4::launch_valu_gemv(mode, epi, a, s);
+      if (fits && mode == NVFP4_MODE_W4A4 && nvfp4::fp4_gemv_supported(a.M, a.K))
+        return nvfp4::launch_fp4_gemv(epi, a, s);
+      if (fits && a.K * 2 <= nvfp4::kValuGemvLdsBytes) return nvfp4::launch_valu_gemv(mode, epi, a, s);
+      if (fits) return nvfp4::launch_stream_gemm(mode, epi, a, s);
       break;
     case NVFP4_PATH_STREAM:
       if (fits) return nvfp4::launch_stream_gemm(mode, epi, a, s);

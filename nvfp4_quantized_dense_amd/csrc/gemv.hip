@@ -1,22 +1,21 @@
-// gemv.hip -- VALU GEMV for the smallest token counts (decode), no MFMA.
+// gemv.hip -- VALU GEMV for W4A16 at the smallest token counts (decode).
 //
-// The decode fast path streams the packed weight with 16-byte loads and
-// does the arithmetic on the vector ALU with packed dot products: codes are
-// widened exactly (E2M1 -> f16/bf16, two per instruction), multiplied
-// against the activation pairs with v_dot2_f32_{f16,bf16}, and each
-// 16-element block sum is scaled once by its E4M3 factor(s). In W4A4 the
-// activation codes enter unscaled as well, and the block sum is scaled by
-// s_w * s_a (a product of two E4M3 values, exact in fp32); the block sum
-// itself, of 16 products of grid values, is exact.
+// The weight streams with 16-byte loads; the arithmetic is on the vector ALU
+// with packed dot products: codes are widened exactly (E2M1 -> bf16, two per
+// instruction), multiplied against the bf16 activation pairs with
+// v_dot2_f32_bf16 (products of a grid value and a bf16 value are exact in
+// fp32), and each 16-element block sum is scaled once by its E4M3 factor.
+// (W4A4 runs on the FP4 matrix core instead, in fp4gemv.hip.)
 //
 // Lane l owns row l % 16 of each row group and columns 32 (l / 16) + [0, 32)
 // of each 128-column half tile (the packed layout's lane order). NW waves
-// divide a row group's K tiles; each wave keeps the next tile's loads in
-// flight while it computes the current one (two register sets, no branch
-// around the prefetch: past the last tile it loads from out of range, which
-// returns zeros without a memory access). Token rows past M are out of range
-// of the activation buffers as well and read as zeros. The four lanes of a
-// row and the NW waves are summed at the end in a fixed order.
+// divide a row group's K tiles; each wave has one tile in flight at a time
+// (past the last tile the load is out of range: zeros without a memory
+// access, and never computed). The workgroup's MT token rows are
+// staged once in LDS (rows past M read as zeros): their reads then wait on
+// the LDS counter, not behind the weight prefetch on the in-order vector
+// memory counter. The four lanes of a row and the NW waves are summed at the
+// end in a fixed order.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -38,29 +37,21 @@ __device__ __forceinline__ float dot2_bf16(bf16x2 w, uint32_t x, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(w, __builtin_bit_cast(bf16x2, x), acc, false);
 }
 
-template <int MODE, int MT>
 struct GemvSrc {
-  Rsrc w, a, s;
-  uint32_t a_row[MT];  // lane offset of each token row in the activation codes (W4A4) or bf16 (W4A16)
-  uint32_t s_row[MT];  // lane offset of each token row in the activation scales (W4A4)
+  Rsrc w, a;
 };
 
-// Loads of one K tile for one wave: NG weight tiles and (W4A4) the NVFP4
-// activation slices of MT tokens.
-template <int MODE, int NG, int MT>
+// Weight loads of one K tile for one wave: NG row groups.
+template <int NG>
 struct GemvTile {
   u32x4 wc[NG][2];
   uint32_t wsd[NG];
-  u32x4 xc[MODE == kW4A4 ? MT : 1][2];
-  uint32_t xsd[MODE == kW4A4 ? MT : 1];
 };
 
-template <int MODE, int NG, int MT>
-__device__ __forceinline__ void gemv_load(GemvTile<MODE, NG, MT>& d, const GemvSrc<MODE, MT>& src,
-                                          int64_t rg0, int64_t T, int64_t t, int lane) {
-  const int q = lane >> 4;
-  const bool in = t < T;
-  const uint32_t tw = in ? (uint32_t)(t * kTileBytes) : kOutOfRange;
+template <int NG>
+__device__ __forceinline__ void gemv_load(GemvTile<NG>& d, const GemvSrc& src, int64_t rg0,
+                                          int T, int t, int lane) {
+  const uint32_t tw = t < T ? (uint32_t)(t * kTileBytes) : kOutOfRange;
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
     const uint32_t gbase = (uint32_t)((rg0 + g) * T * kTileBytes);
@@ -68,116 +59,60 @@ __device__ __forceinline__ void gemv_load(GemvTile<MODE, NG, MT>& d, const GemvS
     d.wc[g][1] = bload16_nt(src.w, tw + 1024 + 16 * lane, gbase);
     d.wsd[g] = bload4_nt(src.w, tw + kTileCodeBytes + 4 * lane, gbase);
   }
-  if constexpr (MODE == kW4A4) {
-    const uint32_t ta = in ? (uint32_t)(t * 128 + q * 16) : kOutOfRange;
-    const uint32_t ts = in ? (uint32_t)(t * 16 + q * 2) : kOutOfRange;
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      d.xc[m][0] = bload16(src.a, src.a_row[m] + ta);
-      d.xc[m][1] = bload16(src.a, src.a_row[m] + ta + 64);
-      d.xsd[m] = bload2(src.s, src.s_row[m] + ts) | (bload2(src.s, src.s_row[m] + ts + 8) << 16);
-    }
-  }
 }
 
-template <int MODE, int NG, int MT>
-__device__ __forceinline__ void gemv_compute(float (&acc)[NG][MT], const GemvTile<MODE, NG, MT>& d,
-                                             const GemvSrc<MODE, MT>& src, int64_t t, int lane) {
+// Tile t (< T) of one wave. xs: the MT staged token rows, K bf16 each.
+template <int NG, int MT>
+__device__ __forceinline__ void gemv_compute(float (&acc)[NG][MT], const GemvTile<NG>& d,
+                                             const uint8_t* xs, int T, int t, int lane) {
+  const int q = lane >> 4;
+  const int tc = t;
   float ws[NG][4];
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
     ws[g][0] = e4m3_to_f32<0>(d.wsd[g]); ws[g][1] = e4m3_to_f32<1>(d.wsd[g]);
     ws[g][2] = e4m3_to_f32<2>(d.wsd[g]); ws[g][3] = e4m3_to_f32<3>(d.wsd[g]);
   }
-  if constexpr (MODE == kW4A4) {
-    float xs[MT][4];
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      xs[m][0] = e4m3_to_f32<0>(d.xsd[m]); xs[m][1] = e4m3_to_f32<1>(d.xsd[m]);
-      xs[m][2] = e4m3_to_f32<2>(d.xsd[m]); xs[m][3] = e4m3_to_f32<3>(d.xsd[m]);
-    }
+  for (int c = 0; c < 2; ++c) {
+    u32x4 xv[MT][4];
+    const int tx = (tc * kTileK + c * 128 + q * 32) * 2;
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        xv[m][u] = *reinterpret_cast<const u32x4*>(xs + (size_t)m * T * kTileK * 2 + tx + 16 * u);
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
-        f16x2 xp[MT][8];  // activation pairs of this block, unscaled
+        float bs[MT];
 #pragma unroll
-        for (int m = 0; m < MT; ++m)
+        for (int m = 0; m < MT; ++m) bs[m] = 0.0f;
 #pragma unroll
-          for (int uu = 0; uu < 2; ++uu) {
-            const uint32_t v = d.xc[m][c][2 * blk + uu];
-            xp[m][4 * uu + 0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 0);
-            xp[m][4 * uu + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 1);
-            xp[m][4 * uu + 2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 2);
-            xp[m][4 * uu + 3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 3);
-          }
-#pragma unroll
-        for (int g = 0; g < NG; ++g) {
-          float bs[MT];
-#pragma unroll
-          for (int m = 0; m < MT; ++m) bs[m] = 0.0f;
-#pragma unroll
-          for (int uu = 0; uu < 2; ++uu) {
-            const uint32_t v = d.wc[g][c][2 * blk + uu];
-            const f16x2 w0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 0);
-            const f16x2 w1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 1);
-            const f16x2 w2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 2);
-            const f16x2 w3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(v, 1.0f, 3);
-#pragma unroll
-            for (int m = 0; m < MT; ++m) {
-              bs[m] = __builtin_amdgcn_fdot2(w0, xp[m][4 * uu + 0], bs[m], false);
-              bs[m] = __builtin_amdgcn_fdot2(w1, xp[m][4 * uu + 1], bs[m], false);
-              bs[m] = __builtin_amdgcn_fdot2(w2, xp[m][4 * uu + 2], bs[m], false);
-              bs[m] = __builtin_amdgcn_fdot2(w3, xp[m][4 * uu + 3], bs[m], false);
-            }
-          }
+        for (int uu = 0; uu < 2; ++uu) {
+          const int u = 2 * blk + uu;
+          const uint32_t v = d.wc[g][c][u];
+          bf16x2 w[4];
+          w[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, 0);
+          w[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, 1);
+          w[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, 2);
+          w[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, 3);
 #pragma unroll
           for (int m = 0; m < MT; ++m)
-            acc[g][m] = __builtin_fmaf(bs[m], ws[g][2 * c + blk] * xs[m][2 * c + blk], acc[g][m]);
+#pragma unroll
+            for (int p = 0; p < 4; ++p) bs[m] = dot2_bf16(w[p], xv[m][u][p], bs[m]);
         }
+#pragma unroll
+        for (int m = 0; m < MT; ++m) acc[g][m] = __builtin_fmaf(bs[m], ws[g][2 * c + blk], acc[g][m]);
       }
-  } else {
-    const int q = lane >> 4;
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      u32x4 xv[MT][4];
-      const uint32_t tx = (uint32_t)((t * kTileK + c * 128 + q * 32) * 2);
-#pragma unroll
-      for (int m = 0; m < MT; ++m)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) xv[m][u] = bload16(src.a, src.a_row[m] + tx + 16 * u);
-#pragma unroll
-      for (int g = 0; g < NG; ++g)
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-          float bs[MT];
-#pragma unroll
-          for (int m = 0; m < MT; ++m) bs[m] = 0.0f;
-#pragma unroll
-          for (int uu = 0; uu < 2; ++uu) {
-            const int u = 2 * blk + uu;
-            const uint32_t v = d.wc[g][c][u];
-            bf16x2 w[4];
-            w[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, 0);
-            w[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, 1);
-            w[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, 2);
-            w[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, 3);
-#pragma unroll
-            for (int m = 0; m < MT; ++m)
-#pragma unroll
-              for (int p = 0; p < 4; ++p) bs[m] = dot2_bf16(w[p], xv[m][u][p], bs[m]);
-          }
-#pragma unroll
-          for (int m = 0; m < MT; ++m) acc[g][m] = __builtin_fmaf(bs[m], ws[g][2 * c + blk], acc[g][m]);
-        }
-    }
   }
 }
 
 }  // namespace
 #endif  // __HIP_DEVICE_COMPILE__
 
-template <int MODE, int EPI, int MT, int NW>
+template <int EPI, int MT, int NW>
 __global__ __launch_bounds__(NW * 64) void k_valu_gemv(GemmArgs args) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int NG = EpiTraits<EPI>::swiglu ? 2 : 1;
@@ -188,21 +123,10 @@ __global__ __launch_bounds__(NW * 64) void k_valu_gemv(GemmArgs args) {
   const int64_t rg0 = (int64_t)blockIdx.x * NG;
   const int64_t tok0 = (int64_t)blockIdx.y * MT;
 
-  GemvSrc<MODE, MT> src;
+  extern __shared__ __attribute__((aligned(16))) uint8_t xs[];  // MT rows of K bf16
+  GemvSrc src;
   src.w = make_rsrc(args.w, (uint32_t)(args.N / kTileRows * T * kTileBytes));
-  if constexpr (MODE == kW4A4) {
-    src.a = make_rsrc(args.a, (uint32_t)(args.M * (K / 2)));
-    src.s = make_rsrc(args.a_scales, (uint32_t)(args.M * (K / 16)));
-  } else {
-    src.a = make_rsrc(args.a, (uint32_t)(args.M * K * 2));
-    src.s = src.a;
-  }
-#pragma unroll
-  for (int m = 0; m < MT; ++m) {
-    // rows past M start past the end of the buffer: they read as zeros
-    src.a_row[m] = (uint32_t)((tok0 + m) * (MODE == kW4A4 ? K / 2 : K * 2));
-    src.s_row[m] = (uint32_t)((tok0 + m) * (K / 16));
-  }
+  src.a = make_rsrc(args.a, (uint32_t)(args.M * K * 2));
 
   float acc[NG][MT];
 #pragma unroll
@@ -210,18 +134,57 @@ __global__ __launch_bounds__(NW * 64) void k_valu_gemv(GemmArgs args) {
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[g][m] = 0.0f;
 
-  // Tiles t = wave, wave + NW, ...; two register sets alternate.
-  int64_t t = wave;
-  GemvTile<MODE, NG, MT> ta, tb;
-  gemv_load<MODE, NG, MT>(ta, src, rg0, T, t, lane);
-  while (t < T) {
-    gemv_load<MODE, NG, MT>(tb, src, rg0, T, t + NW, lane);
-    gemv_compute<MODE, NG, MT>(acc, ta, src, t, lane);
+  // Tiles t = wave, wave + NW, ...: one tile in flight per wave (measured
+  // faster here than two: fewer outstanding requests stream better). The
+  // scheduling barriers keep the arithmetic after the wait for its tile and
+  // the next tile's loads after the arithmetic. A tile past the last one is
+  // never computed.
+  int t = wave;
+  const int nt = (int)T;
+  GemvTile<NG> ta;
+  {
+    // Staging of the token rows in 16-byte chunks (rows past M start past
+    // the end of the buffer and read as zeros). The first four chunks per
+    // thread are requested before the first weight tile, so that writing
+    // them to LDS waits for these loads only (the vector memory counter is
+    // in order), not for the weights.
+    const int row_chunks = (int)(K / 8);
+    const int chunks = MT * row_chunks;
+    constexpr int kStride = NW * 64;
+    u32x4 v[4];
+    auto fetch = [&](int base) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = base + u * kStride;
+        const int m = i / row_chunks;
+        const uint32_t off = i < chunks ? (uint32_t)((tok0 + m) * K * 2 + (int64_t)(i - m * row_chunks) * 16)
+                                        : kOutOfRange;
+        v[u] = bload16(src.a, off);
+      }
+    };
+    auto store = [&](int base) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = base + u * kStride;
+        if (i < chunks) *reinterpret_cast<u32x4*>(xs + (size_t)i * 16) = v[u];
+      }
+    };
+    fetch(threadIdx.x);
+    gemv_load<NG>(ta, src, rg0, nt, t, lane);
+    store(threadIdx.x);
+    for (int base = threadIdx.x + 4 * kStride; base < chunks; base += 4 * kStride) {
+      fetch(base);
+      store(base);
+    }
+  }
+  __syncthreads();
+
+  while (t < nt) {
+    gemv_compute<NG, MT>(acc, ta, xs, nt, t, lane);
+    __builtin_amdgcn_sched_barrier(0);
     t += NW;
-    if (t >= T) break;
-    gemv_load<MODE, NG, MT>(ta, src, rg0, T, t + NW, lane);
-    gemv_compute<MODE, NG, MT>(acc, tb, src, t, lane);
-    t += NW;
+    gemv_load<NG>(ta, src, rg0, nt, t, lane);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // Sum the four lanes of each row (xor 16, then 32), then the waves.
@@ -269,54 +232,43 @@ __global__ __launch_bounds__(NW * 64) void k_valu_gemv(GemmArgs args) {
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-template <int MODE, int EPI, int MT, int NW>
+template <int EPI, int MT, int NW>
 static hipError_t launch_mt_nw(const GemmArgs& a, hipStream_t s) {
   constexpr int NG = EpiTraits<EPI>::swiglu ? 2 : 1;
   dim3 grid((unsigned)(a.N / kTileRows / NG), (unsigned)((a.M + MT - 1) / MT));
-  k_valu_gemv<MODE, EPI, MT, NW><<<grid, NW * 64, 0, s>>>(a);
+  k_valu_gemv<EPI, MT, NW><<<grid, NW * 64, (size_t)MT * a.K * 2, s>>>(a);
   return hipGetLastError();
 }
 
-// Waves per workgroup: enough that the grid keeps about 16 waves per CU
-// streaming (small grids such as down_proj's get 16-wave workgroups).
-// (16-wave workgroups only where the tile fits 128 VGPRs per lane.)
-template <int MODE, int EPI, int MT>
+// Waves per workgroup: 8 (measured best at the decode shapes, 320 to 1088
+// workgroups), 16 for grids too small to spread over the CUs otherwise.
+template <int EPI, int MT>
 static hipError_t launch_mt(const GemmArgs& a, hipStream_t s) {
   constexpr int NG = EpiTraits<EPI>::swiglu ? 2 : 1;
   const int64_t wgs = a.N / kTileRows / NG * ((a.M + MT - 1) / MT);
-  if (wgs >= 1024) return launch_mt_nw<MODE, EPI, MT, 4>(a, s);
-  if constexpr (MT <= 2) {
-    if (wgs < 512) return launch_mt_nw<MODE, EPI, MT, 16>(a, s);
-  }
-  return launch_mt_nw<MODE, EPI, MT, 8>(a, s);
+  if (wgs < 128) return launch_mt_nw<EPI, MT, 16>(a, s);
+  return launch_mt_nw<EPI, MT, 8>(a, s);
 }
 
-template <int MODE, int EPI>
+// Token rows per workgroup: up to 4, as many as fit the LDS budget.
+template <int EPI>
 static hipError_t launch_me(const GemmArgs& a, hipStream_t s) {
-  if (a.M <= 1) return launch_mt<MODE, EPI, 1>(a, s);
-  if (a.M == 2) return launch_mt<MODE, EPI, 2>(a, s);
-  return launch_mt<MODE, EPI, 4>(a, s);
+  if (a.M >= 3 && 4 * a.K * 2 <= kValuGemvLdsBytes) return launch_mt<EPI, 4>(a, s);
+  if (a.M >= 2 && 2 * a.K * 2 <= kValuGemvLdsBytes) return launch_mt<EPI, 2>(a, s);
+  return launch_mt<EPI, 1>(a, s);
 }
 
-// Needs the packed weight and the activations below 2^31 bytes (32-bit
-// buffer offsets); the caller checks.
+// W4A16 only. Needs the packed weight and the activations below 2^31 bytes
+// (32-bit buffer offsets) and one bf16 token row within the LDS budget
+// (K * 2 <= kValuGemvLdsBytes); the caller checks.
 hipError_t launch_valu_gemv(int mode, int epi, const GemmArgs& a, hipStream_t s) {
   if (a.M == 0) return hipSuccess;
-  if (mode == kW4A4) {
-    switch (epi) {
-      case kOutF32: return launch_me<kW4A4, kOutF32>(a, s);
-      case kOutBF16: return launch_me<kW4A4, kOutBF16>(a, s);
-      case kSwigluNvfp4: return launch_me<kW4A4, kSwigluNvfp4>(a, s);
-      case kSwigluBF16: return launch_me<kW4A4, kSwigluBF16>(a, s);
-      case kSwigluF32: return launch_me<kW4A4, kSwigluF32>(a, s);
-    }
-  } else {
-    switch (epi) {
-      case kOutF32: return launch_me<kW4A16, kOutF32>(a, s);
-      case kOutBF16: return launch_me<kW4A16, kOutBF16>(a, s);
-      case kSwigluBF16: return launch_me<kW4A16, kSwigluBF16>(a, s);
-      case kSwigluF32: return launch_me<kW4A16, kSwigluF32>(a, s);
-    }
+  if (mode != kW4A16 || a.K * 2 > kValuGemvLdsBytes) return hipErrorInvalidValue;
+  switch (epi) {
+    case kOutF32: return launch_me<kOutF32>(a, s);
+    case kOutBF16: return launch_me<kOutBF16>(a, s);
+    case kSwigluBF16: return launch_me<kSwigluBF16>(a, s);
+    case kSwigluF32: return launch_me<kSwigluF32>(a, s);
   }
   return hipErrorInvalidValue;
 }

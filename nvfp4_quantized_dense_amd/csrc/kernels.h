@@ -39,7 +39,14 @@ struct GemmArgs {
 
 // epi: Epi enum of device_common.h; mode: Mode enum.
 hipError_t launch_stream_gemm(int mode, int epi, const GemmArgs& a, hipStream_t s);
+// LDS the W4A16 GEMV may stage token rows in (one row of K bf16 at least).
+constexpr int64_t kValuGemvLdsBytes = 65536;
 hipError_t launch_valu_gemv(int mode, int epi, const GemmArgs& a, hipStream_t s);
+// LDS the W4A4 GEMV stages its token rows in: with up to 2 rows per
+// workgroup, the codes, scales and a zero region of K / 2 bytes.
+constexpr int64_t kFp4GemvLdsBytes = 65536;
+bool fp4_gemv_supported(int64_t M, int64_t K);
+hipError_t launch_fp4_gemv(int epi, const GemmArgs& a, hipStream_t s);
 hipError_t launch_tiled_gemm(int mode, int epi, const GemmArgs& a, hipStream_t s);
 // W4A4 only; packed weight, activation codes and scales each < 2^31 bytes.
 hipError_t launch_tiled2_gemm(int epi, const GemmArgs& a, hipStream_t s);
