@@ -246,16 +246,17 @@ def run_one(args, dev, M, H, I, mode, outliers, n_seeds, steps, warmup, copies, 
         else:
             nv.gemm_swiglu(1, xs[i % n_seeds], None, p_gu[r], I, H, a_gu, h=hb, stream=stream)
 
+    # One step: the whole forward in one library call (quantize x, fused
+    # gate_up + SwiGLU + NVFP4 re-quant, down_proj), on the rotating weight
+    # copies and seeds.
     def step(i):
         x = xs[i % n_seeds]
         r = i % copies
         if mode == "w4a4":
-            nv.nvfp4_quantize(x, g1_inv, xq, xsc, stream=stream)
-            fused(i)
-            nv.nvfp4_gemm(0, hq, hsc, p_d[r], H, I, a_d, out=out, stream=stream)
+            nv.mlp_forward(0, x, p_gu[r], a_gu, p_d[r], a_d, I, g1_inv=g1_inv, g2_inv=g2_inv,
+                           ws=ws, out=out, stream=stream)
         else:
-            fused(i)
-            nv.nvfp4_gemm(1, hb, None, p_d[r], H, I, a_d, out=out, stream=stream)
+            nv.mlp_forward(1, x, p_gu[r], a_gu, p_d[r], a_d, I, ws=ws, out=out, stream=stream)
 
     for i in range(warmup):
         step(i)

@@ -3,6 +3,7 @@
 // the choice of kernel class by token count, and the launches.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdarg>
 #include <cstdio>
@@ -71,11 +72,13 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
-// Kernel class for a GEMM of M tokens.
-int choose_path(int64_t M) {
+// Kernel class for a GEMM of M tokens: the decode GEMV up to M = 2 (W4A4,
+// whose FP4 GEMV carries two tokens per workgroup) or M = 1 (W4A16), the
+// weight-streaming MFMA kernel up to M = 64, the LDS-tiled kernel above.
+int choose_path(int mode, int64_t M) {
   int p = g_path.load();
   if (p != NVFP4_PATH_AUTO) return p;
-  if (M <= 1) return NVFP4_PATH_GEMV;
+  if (M <= (mode == NVFP4_MODE_W4A4 ? 2 : 1)) return NVFP4_PATH_GEMV;
   if (M <= 64) return NVFP4_PATH_STREAM;
   return NVFP4_PATH_TILED;
 }
@@ -89,25 +92,73 @@ bool fits_buffers(const nvfp4::GemmArgs& a, int mode) {
   return a.N * a.K / 16 * 9 < lim && (a.M + 256) * row < lim;
 }
 
-hipError_t run_gemm(int path, int mode, int epi, const nvfp4::GemmArgs& a, hipStream_t s) {
-  const bool fits = fits_buffers(a, mode);
-  switch (path) {
-    case NVFP4_PATH_GEMV:
-      if (fits && mode == NVFP4_MODE_W4A4 && nvfp4::fp4_gemv_supported(a.M, a.K))
-        return nvfp4::launch_fp4_gemv(epi, a, s);
-      if (fits && a.K * 2 <= nvfp4::kValuGemvLdsBytes) return nvfp4::launch_valu_gemv(mode, epi, a, s);
-      if (fits) return nvfp4::launch_stream_gemm(mode, epi, a, s);
-      break;
-    case NVFP4_PATH_STREAM:
-      if (fits) return nvfp4::launch_stream_gemm(mode, epi, a, s);
-      break;
-    default:
-      if (mode == NVFP4_MODE_W4A4 && fits) return nvfp4::launch_tiled2_gemm(epi, a, s);
-      break;
+// The kernel a GEMM runs on, from the path and what the operands allow.
+enum Kernel { kFp4Gemv, kValuGemv, kStream, kTiled2, kTiled };
+
+Kernel select_kernel(int path, int mode, const nvfp4::GemmArgs& a) {
+  if (fits_buffers(a, mode)) {
+    if (path == NVFP4_PATH_GEMV) {
+      if (mode == NVFP4_MODE_W4A4 && nvfp4::fp4_gemv_supported(a.M, a.K)) return kFp4Gemv;
+      if (mode == NVFP4_MODE_W4A16 && a.K * 2 + 16 <= nvfp4::kValuGemvLdsBytes) return kValuGemv;
+      return kStream;
+    }
+    if (path == NVFP4_PATH_STREAM) return kStream;
+    if (mode == NVFP4_MODE_W4A4) return kTiled2;
   }
   // Beyond 2^31-byte operands only the 64-bit-addressed tiled kernel runs.
-  return nvfp4::launch_tiled_gemm(mode, epi, a, s);
+  return kTiled;
 }
+
+hipError_t run_gemm(int path, int mode, int epi, const nvfp4::GemmArgs& a, hipStream_t s) {
+  switch (select_kernel(path, mode, a)) {
+    case kFp4Gemv: return nvfp4::launch_fp4_gemv(epi, a, s);
+    case kValuGemv: return nvfp4::launch_valu_gemv(mode, epi, a, s);
+    case kStream: return nvfp4::launch_stream_gemm(mode, epi, a, s);
+    case kTiled2: return nvfp4::launch_tiled2_gemm(epi, a, s);
+    default: return nvfp4::launch_tiled_gemm(mode, epi, a, s);
+  }
+}
+
+// Split-K of a dense GEMM on the weight-streaming kernel: K is split until
+// about kSplitTargetWaves waves run (the down projection has few output
+// tiles, H / 16 per token group), each split keeping at least one tile per
+// wave. (At M = 16 on hidden 5120: W4A4 down 21.2 -> 19-20 us, W4A16 40.8 ->
+// 30.7 us. The decode GEMVs measured no gain from it and do not split.)
+constexpr int64_t kSplitTargetWaves = 8192;
+
+struct SplitPlan {
+  int ways = 1;
+  int64_t units = 0;
+  size_t part_bytes = 0, counter_bytes = 0;
+};
+
+SplitPlan split_plan(Kernel k, int mode, int64_t M, int64_t N, int64_t K) {
+  SplitPlan p;
+  if (M <= 0) return p;
+  if (k != kStream) return p;
+  (void)mode;
+  const nvfp4::TileShape ts = nvfp4::stream_shape(M, N);
+  p.ways = nvfp4::splitk_ways(ts.units, K / 256, kSplitTargetWaves / ts.waves, ts.waves);
+  if (p.ways > 1) {
+    p.units = ts.units;
+    p.part_bytes = align256((size_t)(ts.units * p.ways * ts.tile_floats) * sizeof(float));
+    p.counter_bytes = align256((size_t)ts.units * sizeof(uint32_t));
+  }
+  return p;
+}
+
+// Kernel of an mlp_forward GEMM (the activation buffers do not matter for
+// the choice beyond their size, which depends on M and K only).
+Kernel mlp_kernel(int path, int mode, int64_t M, int64_t N, int64_t K) {
+  nvfp4::GemmArgs a{};
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  return select_kernel(path, mode, a);
+}
+
+// The kernels that clear the split-K counters of the GEMM after them.
+bool clears_counters(Kernel k) { return k == kFp4Gemv || k == kValuGemv || k == kStream; }
 
 // Shared checks of the GEMM entry points. N is the packed row count.
 int check_gemm(int mode, const void* a, const uint8_t* a_scales, const void* w, int64_t M,
@@ -221,7 +272,7 @@ int nvfp4_gemm(int mode, const void* a, const uint8_t* a_scales, const void* w_p
   if (st) return st;
   nvfp4::GemmArgs ga{a, a_scales, static_cast<const uint8_t*>(w_packed), M, N, K, alpha, nullptr, out, nullptr};
   const int epi = out_dtype == NVFP4_DTYPE_F32 ? nvfp4::kOutF32 : nvfp4::kOutBF16;
-  return hip_status(run_gemm(choose_path(M), mode, epi, ga, as_stream(stream)), "gemm launch");
+  return hip_status(run_gemm(choose_path(mode, M), mode, epi, ga, as_stream(stream)), "gemm launch");
 }
 
 int gemm_swiglu_nvfp4_quant(const uint8_t* a_codes, const uint8_t* a_scales, const void* w_gu_packed,
@@ -237,7 +288,7 @@ int gemm_swiglu_nvfp4_quant(const uint8_t* a_codes, const uint8_t* a_scales, con
   if (st) return st;
   nvfp4::GemmArgs ga{a_codes, a_scales, static_cast<const uint8_t*>(w_gu_packed), M, 2 * I, K, alpha, g2_inv,
                      h_codes, h_scales};
-  return hip_status(run_gemm(choose_path(M), NVFP4_MODE_W4A4, nvfp4::kSwigluNvfp4, ga, as_stream(stream)),
+  return hip_status(run_gemm(choose_path(NVFP4_MODE_W4A4, M), NVFP4_MODE_W4A4, nvfp4::kSwigluNvfp4, ga, as_stream(stream)),
                     "gemm_swiglu_nvfp4_quant launch");
 }
 
@@ -254,17 +305,31 @@ int gemm_swiglu(int mode, const void* a, const uint8_t* a_scales, const void* w_
   if (st) return st;
   nvfp4::GemmArgs ga{a, a_scales, static_cast<const uint8_t*>(w_gu_packed), M, 2 * I, K, alpha, nullptr, h, nullptr};
   const int epi = h_dtype == NVFP4_DTYPE_F32 ? nvfp4::kSwigluF32 : nvfp4::kSwigluBF16;
-  return hip_status(run_gemm(choose_path(M), mode, epi, ga, as_stream(stream)), "gemm_swiglu launch");
+  return hip_status(run_gemm(choose_path(mode, M), mode, epi, ga, as_stream(stream)), "gemm_swiglu launch");
+}
+
+// Activation part of the workspace: W4A4 x and h as NVFP4, W4A16 h in bf16.
+static size_t mlp_act_bytes(int mode, size_t m, int64_t H, int64_t I) {
+  if (mode == NVFP4_MODE_W4A4)
+    return align256(m * H / 2) + align256(m * H / 16) + align256(m * I / 2) + align256(m * I / 16);
+  return align256(m * I * 2);
+}
+
+// Split-K part: sized for the largest plan over the decode kernels, so the
+// size does not depend on the process-wide path override.
+static size_t mlp_split_bytes(int mode, int64_t M, int64_t H, int64_t I) {
+  size_t most = 0;
+  for (int path : {NVFP4_PATH_GEMV, NVFP4_PATH_STREAM}) {
+    const SplitPlan p = split_plan(mlp_kernel(path, mode, M, H, I), mode, M, H, I);
+    most = std::max(most, p.part_bytes + p.counter_bytes);
+  }
+  return most;
 }
 
 size_t mlp_workspace_bytes(int mode, int64_t M, int64_t H, int64_t I) {
   if (M < 0 || H <= 0 || I <= 0 || !dim_ok(M) || !dim_ok(H) || !dim_ok(I)) return 0;
-  const size_t m = static_cast<size_t>(M);
-  if (mode == NVFP4_MODE_W4A4) {
-    return align256(m * H / 2) + align256(m * H / 16) + align256(m * I / 2) + align256(m * I / 16);
-  }
-  if (mode == NVFP4_MODE_W4A16) return align256(m * I * 2);
-  return 0;
+  if (mode != NVFP4_MODE_W4A4 && mode != NVFP4_MODE_W4A16) return 0;
+  return mlp_act_bytes(mode, static_cast<size_t>(M), H, I) + mlp_split_bytes(mode, M, H, I);
 }
 
 int mlp_forward(int mode, const uint16_t* x, int64_t M, int64_t H, int64_t I, const void* w_gu_packed,
@@ -293,30 +358,63 @@ int mlp_forward(int mode, const uint16_t* x, int64_t M, int64_t H, int64_t I, co
   int st = check_device();
   if (st) return st;
   hipStream_t s = as_stream(stream);
-  const int path = choose_path(M);
+  const int path = choose_path(mode, M);
   const int epi_out = out_dtype == NVFP4_DTYPE_F32 ? nvfp4::kOutF32 : nvfp4::kOutBF16;
   uint8_t* base = static_cast<uint8_t*>(ws);
   const size_t m = static_cast<size_t>(M);
+
+  // Split-K of the down projection (partials and counters after the
+  // activations); the gate_up kernel clears the counters before it runs.
+  const Kernel k_gu = mlp_kernel(path, mode, M, 2 * I, H);
+  const Kernel k_d = mlp_kernel(path, mode, M, H, I);
+  SplitPlan sp = split_plan(k_d, mode, M, H, I);
+  if (!clears_counters(k_gu)) sp = SplitPlan{};
+  uint8_t* split_base = base + mlp_act_bytes(mode, m, H, I);
+  float* part = reinterpret_cast<float*>(split_base);
+  uint32_t* counters = reinterpret_cast<uint32_t*>(split_base + sp.part_bytes);
+  auto with_split = [&](nvfp4::GemmArgs& gu, nvfp4::GemmArgs& dn) {
+    if (sp.ways <= 1) return;
+    gu.zero_ptr = counters;
+    gu.zero_n = (int)sp.units;
+    dn.part = part;
+    dn.counters = counters;
+    dn.ksplit = sp.ways;
+  };
+
   hipError_t e;
   if (mode == NVFP4_MODE_W4A4) {
     uint8_t* xq = base;
     uint8_t* xs = xq + align256(m * H / 2);
     uint8_t* hq = xs + align256(m * H / 16);
     uint8_t* hs = hq + align256(m * I / 2);
-    e = nvfp4::launch_quantize(x, false, M, H, g1_inv, xq, xs, s);
-    if (e != hipSuccess) return hip_status(e, "mlp_forward quantize");
+    // At M = 1 the decode GEMV quantizes x itself as it stages it (no
+    // separate launch); otherwise x is quantized by launch_quantize (with two
+    // token rows per workgroup the fused variant needs more registers than
+    // keep its grid resident: measured 35.5 against 26.5 + 4.8 us).
+    const bool fused_quant = k_gu == kFp4Gemv && M == 1;
+    if (!fused_quant) {
+      e = nvfp4::launch_quantize(x, false, M, H, g1_inv, xq, xs, s);
+      if (e != hipSuccess) return hip_status(e, "mlp_forward quantize");
+    }
     nvfp4::GemmArgs g1{xq, xs, static_cast<const uint8_t*>(w_gu_packed), M, 2 * I, H, alpha_gu, g2_inv, hq, hs};
+    if (fused_quant) {
+      g1.a = x;
+      g1.a_scales = nullptr;
+      g1.a_g_inv = g1_inv;
+    }
+    nvfp4::GemmArgs g2{hq, hs, static_cast<const uint8_t*>(w_d_packed), M, H, I, alpha_d, nullptr, out, nullptr};
+    with_split(g1, g2);
     e = run_gemm(path, NVFP4_MODE_W4A4, nvfp4::kSwigluNvfp4, g1, s);
     if (e != hipSuccess) return hip_status(e, "mlp_forward gate_up");
-    nvfp4::GemmArgs g2{hq, hs, static_cast<const uint8_t*>(w_d_packed), M, H, I, alpha_d, nullptr, out, nullptr};
     e = run_gemm(path, NVFP4_MODE_W4A4, epi_out, g2, s);
     return hip_status(e, "mlp_forward down");
   }
   uint8_t* hb = base;
   nvfp4::GemmArgs g1{x, nullptr, static_cast<const uint8_t*>(w_gu_packed), M, 2 * I, H, alpha_gu, nullptr, hb, nullptr};
+  nvfp4::GemmArgs g2{hb, nullptr, static_cast<const uint8_t*>(w_d_packed), M, H, I, alpha_d, nullptr, out, nullptr};
+  with_split(g1, g2);
   e = run_gemm(path, NVFP4_MODE_W4A16, nvfp4::kSwigluBF16, g1, s);
   if (e != hipSuccess) return hip_status(e, "mlp_forward gate_up");
-  nvfp4::GemmArgs g2{hb, nullptr, static_cast<const uint8_t*>(w_d_packed), M, H, I, alpha_d, nullptr, out, nullptr};
   e = run_gemm(path, NVFP4_MODE_W4A16, epi_out, g2, s);
   return hip_status(e, "mlp_forward down");
 }

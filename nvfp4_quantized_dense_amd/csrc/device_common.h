@@ -154,6 +154,56 @@ __device__ __forceinline__ uint32_t bload2(Rsrc r, uint32_t voff) {
 #endif
 
 // ---------------------------------------------------------------------------
+// Split-K combine, run by the one wave that holds a workgroup's result tile
+// (NT token groups, one f32x4 per lane each). Everything the workgroups of a
+// tile exchange goes through device-scope (sc1) atomic loads and stores,
+// which are coherent across the XCDs' separate L2 caches without the
+// whole-L2 write-back and invalidate of a device-scope fence (that costs
+// microseconds per workgroup here). The partial is stored, the wave waits
+// until those stores have completed (vmcnt(0)), then counts its arrival;
+// the workgroup that arrives last (of ks) reads the ks partials, adds them
+// in split order (so the result does not depend on which workgroup
+// finished last), resets the count for the next launch and returns true.
+// The others return false and have nothing left to do. Only vector-memory
+// instructions are used.
+// ---------------------------------------------------------------------------
+template <int NT>
+__device__ __forceinline__ bool splitk_last(f32x4 (&res)[NT], float* part, uint32_t* counters, int ks,
+                                            int64_t unit, int s, int lane) {
+  float* mine = part + ((unit * ks + s) * NT) * 256;
+#pragma unroll
+  for (int j = 0; j < NT; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      __hip_atomic_store(mine + (j * 64 + lane) * 4 + r, res[j][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0): the partial has reached device scope
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  uint32_t arrived = 0;
+  if (lane == 0) arrived = __hip_atomic_fetch_add(counters + unit, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  arrived = __shfl(arrived, 0);
+  if (arrived != (uint32_t)(ks - 1)) return false;
+#pragma unroll
+  for (int j = 0; j < NT; ++j) res[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int sp = 0; sp < ks; ++sp) {
+    const float* p = part + ((unit * ks + sp) * NT) * 256;
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        res[j][r] += __hip_atomic_load(p + (j * 64 + lane) * 4 + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (lane == 0) __hip_atomic_store(counters + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return true;
+}
+
+// Workgroup (0, 0, 0) clears n words at p (the next GEMM's split-K counters).
+__device__ __forceinline__ void clear_words(uint32_t* p, int n) {
+  if (p != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0)
+    for (int i = threadIdx.x; i < n; i += blockDim.x) p[i] = 0u;
+}
+
+// ---------------------------------------------------------------------------
 // Epilogues. The MFMA 16x16x32 result tile of a lane holds rows 4(l/16)+r,
 // r = 0..3, of one token column l % 16.
 // ---------------------------------------------------------------------------

@@ -73,12 +73,12 @@ struct F4Tile {
   uint32_t xsd[MT][2];  // activation scales of blocks 2 q + {0, 1} and 8 + 2 q + {0, 1}
 };
 
-// Weight loads of tile t (out of range past the last tile: zeros, no
-// memory access).
+// Weight loads of tile t of row groups of T tiles (out of range from tile
+// t_end on: zeros, no memory access).
 template <int NG, int MT>
 __device__ __forceinline__ void f4_load_w(F4Tile<NG, MT>& d, const F4Src<MT>& src, int64_t rg0, int T,
-                                          int t, int lane) {
-  const uint32_t tw = t < T ? (uint32_t)(t * kTileBytes) : kOutOfRange;
+                                          int t_end, int t, int lane) {
+  const uint32_t tw = t < t_end ? (uint32_t)(t * kTileBytes) : kOutOfRange;
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
     const uint32_t gbase = (uint32_t)((rg0 + g) * T * kTileBytes);
@@ -88,12 +88,12 @@ __device__ __forceinline__ void f4_load_w(F4Tile<NG, MT>& d, const F4Src<MT>& sr
   }
 }
 
-// The activation slots of tile t from LDS (from the last tile when t is
-// past it: valid addresses, values multiplied by zero weights).
+// The activation slots of tile t from LDS (from tile t_end - 1 when t is
+// past the range: valid addresses, values multiplied by zero weights).
 template <int NG, int MT>
 __device__ __forceinline__ void f4_load_x(F4Tile<NG, MT>& d, const F4Src<MT>& src, const uint8_t* xl,
-                                          int T, int t) {
-  const uint32_t tc = (uint32_t)((t < T ? t : T - 1));
+                                          int t_end, int t) {
+  const uint32_t tc = (uint32_t)((t < t_end ? t : t_end - 1));
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
 #pragma unroll
@@ -141,7 +141,7 @@ __device__ __forceinline__ void f4_compute(f32x4 (&acc)[NG][MT], const F4Tile<NG
 }  // namespace
 #endif  // __HIP_DEVICE_COMPILE__
 
-template <int EPI, int MT, int NW>
+template <int EPI, int MT, int NW, bool QX>
 __global__ __launch_bounds__(NW * 64) void k_fp4_gemv(GemmArgs args) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int NG = EpiTraits<EPI>::swiglu ? 2 : 1;
@@ -180,70 +180,144 @@ __global__ __launch_bounds__(NW * 64) void k_fp4_gemv(GemmArgs args) {
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[g][m] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  int t = wave;
+  clear_words(args.zero_ptr, args.zero_n);
+
+  // K tiles [t0, t1): all of them (the staging and loop are written for a
+  // tile range).
   const int nt = (int)T;
+  const int t0 = 0, t1 = nt, tlast = nt;
+  int t = t0 + wave;
   F4Tile<NG, MT> ta, tb;
   {
-    // Staging of the MT token rows of codes and scales in 16-byte chunks
-    // (rows past M are past the end of the buffers and read as zeros). The
-    // first four chunks per thread are requested before the first two
-    // weight tiles, so that writing them to LDS waits for these loads only
-    // (the vector memory counter is in order), not for the weights.
+    // Staging of tiles [t0, t1) of the MT token rows, codes and scales, in
+    // 16-byte chunks (rows past M are past the end of the buffers and read
+    // as zeros). The first four chunks per thread are requested before the
+    // first two weight tiles, so that writing them to LDS waits for these
+    // loads only (the vector memory counter is in order), not for the
+    // weights.
     const Rsrc ra = make_rsrc(args.a, (uint32_t)(args.M * (K / 2)));
     const Rsrc rs = make_rsrc(args.a_scales, (uint32_t)(args.M * (K / 16)));
-    const int code_chunks = MT * Ki / 32, chunks = code_chunks + MT * Ki / 256;
-    const uint32_t code0 = (uint32_t)(tok0 * (K / 2)), scale0 = (uint32_t)(tok0 * (K / 16));
+    const int nts = t1 > t0 ? t1 - t0 : 0;
+    const int code_row = nts * 8, code_chunks = MT * code_row, chunks = code_chunks + MT * nts;
     constexpr int kStride = NW * 64;
     u32x4 v[4];
+    // Byte offsets in the buffers (code or scale) and in LDS of chunk i.
+    auto offsets = [&](int i, uint32_t& g, uint32_t& l) {
+      if (i < code_chunks) {
+        const int m = i / code_row, j = i - m * code_row;
+        g = (uint32_t)((tok0 + m) * (K / 2)) + (uint32_t)(t0 * 128 + 16 * j);
+        l = (uint32_t)(m * Ki / 2 + t0 * 128 + 16 * j);
+      } else {
+        const int i2 = i - code_chunks, m = i2 / (nts > 0 ? nts : 1), j = i2 - m * nts;
+        g = (uint32_t)((tok0 + m) * (K / 16)) + (uint32_t)((t0 + j) * 16);
+        l = (uint32_t)(lds_scale_off(MT, Ki) + m * Ki / 16 + (t0 + j) * 16);
+      }
+    };
     auto fetch = [&](int base) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int i = base + u * kStride;
-        if (i < code_chunks) v[u] = bload16(ra, code0 + 16 * i);
-        else v[u] = bload16(rs, i < chunks ? scale0 + 16 * (i - code_chunks) : kOutOfRange);
+        uint32_t g = kOutOfRange, l = 0;
+        if (i < chunks) offsets(i, g, l);
+        v[u] = bload16(i < code_chunks ? ra : rs, g);
       }
     };
+    // Every fetched value is written (a chunk past the end loaded zeros and
+    // goes to the zero region), so no load is left pending with its
+    // register free for reuse: reusing one would wait for all later loads.
     auto store = [&](int base) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int i = base + u * kStride;
-        if (i < code_chunks) *reinterpret_cast<u32x4*>(xl + 16 * i) = v[u];
-        else if (i < chunks) *reinterpret_cast<u32x4*>(xl + lds_scale_off(MT, Ki) + 16 * (i - code_chunks)) = v[u];
+        uint32_t g, l = (uint32_t)(lds_zero_off(MT, Ki) + t0 * 128);
+        if (i < chunks) offsets(i, g, l);
+        *reinterpret_cast<u32x4*>(xl + l) = v[u];
       }
     };
-    fetch(threadIdx.x);
-    f4_load_w<NG, MT>(ta, src, rg0, nt, t, lane);
-    f4_load_w<NG, MT>(tb, src, rg0, nt, t + NW, lane);
-    store(threadIdx.x);
-    for (int base = threadIdx.x + 4 * kStride; base < chunks; base += 4 * kStride) {
-      fetch(base);
-      store(base);
+    if constexpr (QX) {
+      // bf16 token rows quantized on the way in: chunk i holds 8 elements,
+      // chunks 2b and 2b + 1 of a row (neighbouring lanes) form block b and
+      // exchange their amax, exactly as in the standalone quantizer.
+      const Rsrc rx = make_rsrc(args.a, (uint32_t)(args.M * K * 2));
+      const float gi = *args.a_g_inv;
+      const int row8 = nts * 32, xchunks = MT * row8;
+      auto xfetch = [&](int base) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = base + u * kStride;
+          const int m = i / row8, j = i - m * row8;
+          v[u] = bload16(rx, i < xchunks ? (uint32_t)((tok0 + m) * K * 2) + (uint32_t)(t0 * 512 + 16 * j)
+                                         : kOutOfRange);
+        }
+      };
+      auto xstore = [&](int base) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = base + u * kStride;
+          float e[8];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            e[2 * k] = __uint_as_float(v[u][k] << 16);
+            e[2 * k + 1] = __uint_as_float(v[u][k] & 0xFFFF0000u);
+          }
+          uint32_t mx = 0;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) mx = max(mx, __float_as_uint(e[k]) & 0x7FFFFFFFu);
+          mx = max(mx, (uint32_t)__shfl_xor((int)mx, 1));
+          const BlockScale bs = block_scale(__uint_as_float(mx), gi);
+          uint32_t packed = 0;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) packed |= e2m1_from_f32(e[k] * bs.r) << (4 * k);
+          if (i < xchunks) {
+            const int m = i / row8, j = i - m * row8;
+            *reinterpret_cast<uint32_t*>(xl + m * Ki / 2 + t0 * 128 + 4 * j) = packed;
+            if ((j & 1) == 0) xl[lds_scale_off(MT, Ki) + m * Ki / 16 + t0 * 16 + j / 2] = (uint8_t)bs.byte;
+          }
+        }
+      };
+      xfetch(threadIdx.x);
+      f4_load_w<NG, MT>(ta, src, rg0, nt, t1, t, lane);
+      f4_load_w<NG, MT>(tb, src, rg0, nt, t1, t + NW, lane);
+      xstore(threadIdx.x);
+      for (int base = threadIdx.x + 4 * kStride; base < xchunks; base += 4 * kStride) {
+        xfetch(base);
+        xstore(base);
+      }
+    } else {
+      fetch(threadIdx.x);
+      f4_load_w<NG, MT>(ta, src, rg0, nt, t1, t, lane);
+      f4_load_w<NG, MT>(tb, src, rg0, nt, t1, t + NW, lane);
+      store(threadIdx.x);
+      for (int base = threadIdx.x + 4 * kStride; base < chunks; base += 4 * kStride) {
+        fetch(base);
+        store(base);
+      }
     }
     const u32x4 z = {0u, 0u, 0u, 0u};
-    for (int i = threadIdx.x; i < Ki / 32; i += kStride)
-      *reinterpret_cast<u32x4*>(xl + lds_zero_off(MT, Ki) + 16 * i) = z;
+    for (int i = threadIdx.x; i < nts * 8; i += kStride)
+      *reinterpret_cast<u32x4*>(xl + lds_zero_off(MT, Ki) + t0 * 128 + 16 * i) = z;
   }
   __syncthreads();
-  f4_load_x<NG, MT>(ta, src, xl, nt, t);
-  f4_load_x<NG, MT>(tb, src, xl, nt, t + NW);
+  f4_load_x<NG, MT>(ta, src, xl, tlast, t);
+  f4_load_x<NG, MT>(tb, src, xl, tlast, t + NW);
 
   // Two register sets, two tiles per trip and no exit between them: a tile
-  // past the last one has all-zero weight codes and scales (out-of-range
+  // past the range has all-zero weight codes and scales (out-of-range
   // loads), so its products add +0. (An exit between the halves lets the
   // compiler sink the second half's prefetch into it.) The scheduling
   // barriers keep each prefetch clear of the arithmetic before it: an
   // instruction on prefetched data pulled forward would wait for every
   // load in flight.
-  while (t < nt) {
+  while (t < t1) {
     f4_compute<NG, MT>(acc, ta);
     __builtin_amdgcn_sched_barrier(0);
-    f4_load_w<NG, MT>(ta, src, rg0, nt, t + 2 * NW, lane);
-    f4_load_x<NG, MT>(ta, src, xl, nt, t + 2 * NW);
+    f4_load_w<NG, MT>(ta, src, rg0, nt, t1, t + 2 * NW, lane);
+    f4_load_x<NG, MT>(ta, src, xl, tlast, t + 2 * NW);
     __builtin_amdgcn_sched_barrier(0);
     f4_compute<NG, MT>(acc, tb);
     __builtin_amdgcn_sched_barrier(0);
-    f4_load_w<NG, MT>(tb, src, rg0, nt, t + 3 * NW, lane);
-    f4_load_x<NG, MT>(tb, src, xl, nt, t + 3 * NW);
+    f4_load_w<NG, MT>(tb, src, rg0, nt, t1, t + 3 * NW, lane);
+    f4_load_x<NG, MT>(tb, src, xl, tlast, t + 3 * NW);
     __builtin_amdgcn_sched_barrier(0);
     t += 2 * NW;
   }
@@ -305,17 +379,26 @@ template <int EPI, int MT, int NW>
 static hipError_t fp4_launch_nw(const GemmArgs& a, hipStream_t s) {
   constexpr int NG = EpiTraits<EPI>::swiglu ? 2 : 1;
   dim3 grid((unsigned)(a.N / kTileRows / NG), (unsigned)((a.M + MT - 1) / MT));
-  k_fp4_gemv<EPI, MT, NW><<<grid, NW * 64, (size_t)fp4_lds_bytes(MT, a.K), s>>>(a);
+  const size_t lds = (size_t)fp4_lds_bytes(MT, a.K);
+  if constexpr (EPI == kSwigluNvfp4 && MT == 1) {
+    if (a.a_g_inv) {
+      k_fp4_gemv<EPI, MT, NW, true><<<grid, NW * 64, lds, s>>>(a);
+      return hipGetLastError();
+    }
+  }
+  k_fp4_gemv<EPI, MT, NW, false><<<grid, NW * 64, lds, s>>>(a);
   return hipGetLastError();
 }
 
 // Waves per workgroup: 4 (measured best from 320 to 1152 workgroups, the
 // decode shapes), 16 for grids too small to spread over the CUs otherwise.
+static int fp4_waves(int64_t wgs) { return wgs < 128 ? 16 : 4; }
+
 template <int EPI, int MT>
 static hipError_t fp4_launch_mt(const GemmArgs& a, hipStream_t s) {
   constexpr int NG = EpiTraits<EPI>::swiglu ? 2 : 1;
   const int64_t wgs = a.N / kTileRows / NG * ((a.M + MT - 1) / MT);
-  if (wgs < 128) return fp4_launch_nw<EPI, MT, 16>(a, s);
+  if (fp4_waves(wgs) == 16) return fp4_launch_nw<EPI, MT, 16>(a, s);
   return fp4_launch_nw<EPI, MT, 4>(a, s);
 }
 
@@ -329,7 +412,8 @@ static hipError_t fp4_launch_e(const GemmArgs& a, hipStream_t s) {
 // (32-bit buffer offsets) and fp4_gemv_supported(M, K); the caller checks.
 hipError_t launch_fp4_gemv(int epi, const GemmArgs& a, hipStream_t s) {
   if (a.M == 0) return hipSuccess;
-  if (!fp4_gemv_supported(a.M, a.K)) return hipErrorInvalidValue;
+  if (!fp4_gemv_supported(a.M, a.K) || a.ksplit != 1 || (a.a_g_inv && (epi != kSwigluNvfp4 || a.M > 1)))
+    return hipErrorInvalidValue;
   switch (epi) {
     case kOutF32: return fp4_launch_e<kOutF32>(a, s);
     case kOutBF16: return fp4_launch_e<kOutBF16>(a, s);

@@ -48,10 +48,12 @@ struct GemvTile {
   uint32_t wsd[NG];
 };
 
+// Tile t of row groups of T tiles (out of range from tile t_end on: zeros,
+// no memory access).
 template <int NG>
 __device__ __forceinline__ void gemv_load(GemvTile<NG>& d, const GemvSrc& src, int64_t rg0,
-                                          int T, int t, int lane) {
-  const uint32_t tw = t < T ? (uint32_t)(t * kTileBytes) : kOutOfRange;
+                                          int T, int t_end, int t, int lane) {
+  const uint32_t tw = t < t_end ? (uint32_t)(t * kTileBytes) : kOutOfRange;
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
     const uint32_t gbase = (uint32_t)((rg0 + g) * T * kTileBytes);
@@ -123,7 +125,7 @@ __global__ __launch_bounds__(NW * 64) void k_valu_gemv(GemmArgs args) {
   const int64_t rg0 = (int64_t)blockIdx.x * NG;
   const int64_t tok0 = (int64_t)blockIdx.y * MT;
 
-  extern __shared__ __attribute__((aligned(16))) uint8_t xs[];  // MT rows of K bf16
+  extern __shared__ __attribute__((aligned(16))) uint8_t xs[];  // MT rows of K bf16, 16 spare bytes
   GemvSrc src;
   src.w = make_rsrc(args.w, (uint32_t)(args.N / kTileRows * T * kTileBytes));
   src.a = make_rsrc(args.a, (uint32_t)(args.M * K * 2));
@@ -134,43 +136,54 @@ __global__ __launch_bounds__(NW * 64) void k_valu_gemv(GemmArgs args) {
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[g][m] = 0.0f;
 
-  // Tiles t = wave, wave + NW, ...: one tile in flight per wave (measured
-  // faster here than two: fewer outstanding requests stream better). The
-  // scheduling barriers keep the arithmetic after the wait for its tile and
-  // the next tile's loads after the arithmetic. A tile past the last one is
-  // never computed.
-  int t = wave;
+  clear_words(args.zero_ptr, args.zero_n);
+  // K tiles [t0, t1): all of them (the staging and loop are written for a
+  // tile range).
   const int nt = (int)T;
+  const int t0 = 0, t1 = nt;
+  int t = t0 + wave;
   GemvTile<NG> ta;
   {
-    // Staging of the token rows in 16-byte chunks (rows past M start past
-    // the end of the buffer and read as zeros). The first four chunks per
-    // thread are requested before the first weight tile, so that writing
-    // them to LDS waits for these loads only (the vector memory counter is
-    // in order), not for the weights.
-    const int row_chunks = (int)(K / 8);
+    // Staging of tiles [t0, t1) of the token rows in 16-byte chunks (rows
+    // past M start past the end of the buffer and read as zeros), at their
+    // place in full rows of K bf16. The first four chunks per thread are
+    // requested before the first weight tile, so that writing them to LDS
+    // waits for these loads only (the vector memory counter is in order),
+    // not for the weights.
+    const int row_chunks = (t1 - t0) * 32;
     const int chunks = MT * row_chunks;
+    const uint32_t sink = (uint32_t)(MT * K * 2);
     constexpr int kStride = NW * 64;
     u32x4 v[4];
+    auto offsets = [&](int i, uint32_t& g, uint32_t& l) {
+      const int m = i / row_chunks, j = i - m * row_chunks;
+      g = (uint32_t)((tok0 + m) * K * 2) + (uint32_t)(t0 * 512 + 16 * j);
+      l = (uint32_t)(m * K * 2) + (uint32_t)(t0 * 512 + 16 * j);
+    };
     auto fetch = [&](int base) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int i = base + u * kStride;
-        const int m = i / row_chunks;
-        const uint32_t off = i < chunks ? (uint32_t)((tok0 + m) * K * 2 + (int64_t)(i - m * row_chunks) * 16)
-                                        : kOutOfRange;
-        v[u] = bload16(src.a, off);
+        uint32_t g = kOutOfRange, l;
+        if (i < chunks) offsets(i, g, l);
+        v[u] = bload16(src.a, g);
       }
     };
+    // Every fetched value is written (a chunk past the end loaded zeros and
+    // goes to the 16 spare bytes after the rows), so no load is left pending
+    // with its register free for reuse: reusing one would wait for all
+    // later loads.
     auto store = [&](int base) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int i = base + u * kStride;
-        if (i < chunks) *reinterpret_cast<u32x4*>(xs + (size_t)i * 16) = v[u];
+        uint32_t g, l = sink;
+        if (i < chunks) offsets(i, g, l);
+        *reinterpret_cast<u32x4*>(xs + l) = v[u];
       }
     };
     fetch(threadIdx.x);
-    gemv_load<NG>(ta, src, rg0, nt, t, lane);
+    gemv_load<NG>(ta, src, rg0, nt, t1, t, lane);
     store(threadIdx.x);
     for (int base = threadIdx.x + 4 * kStride; base < chunks; base += 4 * kStride) {
       fetch(base);
@@ -179,11 +192,15 @@ __global__ __launch_bounds__(NW * 64) void k_valu_gemv(GemmArgs args) {
   }
   __syncthreads();
 
-  while (t < nt) {
+  // One tile in flight per wave (measured faster here than two: fewer
+  // outstanding requests stream better). The scheduling barriers keep the
+  // arithmetic after the wait for its tile and the next tile's loads after
+  // the arithmetic. A tile past the range is never computed.
+  while (t < t1) {
     gemv_compute<NG, MT>(acc, ta, xs, nt, t, lane);
     __builtin_amdgcn_sched_barrier(0);
     t += NW;
-    gemv_load<NG>(ta, src, rg0, nt, t, lane);
+    gemv_load<NG>(ta, src, rg0, nt, t1, t, lane);
     __builtin_amdgcn_sched_barrier(0);
   }
 
@@ -236,34 +253,43 @@ template <int EPI, int MT, int NW>
 static hipError_t launch_mt_nw(const GemmArgs& a, hipStream_t s) {
   constexpr int NG = EpiTraits<EPI>::swiglu ? 2 : 1;
   dim3 grid((unsigned)(a.N / kTileRows / NG), (unsigned)((a.M + MT - 1) / MT));
-  k_valu_gemv<EPI, MT, NW><<<grid, NW * 64, (size_t)MT * a.K * 2, s>>>(a);
+  k_valu_gemv<EPI, MT, NW><<<grid, NW * 64, (size_t)MT * a.K * 2 + 16, s>>>(a);
   return hipGetLastError();
 }
 
 // Waves per workgroup: 8 (measured best at the decode shapes, 320 to 1088
 // workgroups), 16 for grids too small to spread over the CUs otherwise.
+static int valu_waves(int64_t wgs) { return wgs < 128 ? 16 : 8; }
+
 template <int EPI, int MT>
 static hipError_t launch_mt(const GemmArgs& a, hipStream_t s) {
   constexpr int NG = EpiTraits<EPI>::swiglu ? 2 : 1;
   const int64_t wgs = a.N / kTileRows / NG * ((a.M + MT - 1) / MT);
-  if (wgs < 128) return launch_mt_nw<EPI, MT, 16>(a, s);
+  if (valu_waves(wgs) == 16) return launch_mt_nw<EPI, MT, 16>(a, s);
   return launch_mt_nw<EPI, MT, 8>(a, s);
 }
 
 // Token rows per workgroup: up to 4, as many as fit the LDS budget.
+static int valu_rows(int64_t M, int64_t K) {
+  if (M >= 3 && 4 * K * 2 + 16 <= kValuGemvLdsBytes) return 4;
+  if (M >= 2 && 2 * K * 2 + 16 <= kValuGemvLdsBytes) return 2;
+  return 1;
+}
+
 template <int EPI>
 static hipError_t launch_me(const GemmArgs& a, hipStream_t s) {
-  if (a.M >= 3 && 4 * a.K * 2 <= kValuGemvLdsBytes) return launch_mt<EPI, 4>(a, s);
-  if (a.M >= 2 && 2 * a.K * 2 <= kValuGemvLdsBytes) return launch_mt<EPI, 2>(a, s);
+  const int mt = valu_rows(a.M, a.K);
+  if (mt == 4) return launch_mt<EPI, 4>(a, s);
+  if (mt == 2) return launch_mt<EPI, 2>(a, s);
   return launch_mt<EPI, 1>(a, s);
 }
 
 // W4A16 only. Needs the packed weight and the activations below 2^31 bytes
 // (32-bit buffer offsets) and one bf16 token row within the LDS budget
-// (K * 2 <= kValuGemvLdsBytes); the caller checks.
+// (K * 2 + 16 <= kValuGemvLdsBytes); the caller checks.
 hipError_t launch_valu_gemv(int mode, int epi, const GemmArgs& a, hipStream_t s) {
   if (a.M == 0) return hipSuccess;
-  if (mode != kW4A16 || a.K * 2 > kValuGemvLdsBytes) return hipErrorInvalidValue;
+  if (mode != kW4A16 || a.K * 2 + 16 > kValuGemvLdsBytes || a.ksplit != 1) return hipErrorInvalidValue;
   switch (epi) {
     case kOutF32: return launch_me<kOutF32>(a, s);
     case kOutBF16: return launch_me<kOutBF16>(a, s);

@@ -35,7 +35,51 @@ struct GemmArgs {
   const float* g2_inv;       // SwiGLU + NVFP4 output only
   void* out;                 // [M, N] dense, or h [M, I] (dense or codes)
   uint8_t* out_scales;       // h scales [M, I/16]
+  // Split-K (weight-streaming kernel, dense epilogues): ksplit > 1 divides the K
+  // tiles over gridDim.z. Each workgroup stores its partial result tile to
+  // part (tile u, split s at ((u * ksplit + s) * tile_floats)); the last of
+  // the ksplit workgroups of a tile to finish (counted in counters[u], which
+  // must be zero at launch and are left zero) adds the partials in split
+  // order and runs the epilogue.
+  float* part = nullptr;
+  uint32_t* counters = nullptr;
+  int ksplit = 1;
+  // Words that workgroup (0, 0, 0) clears before its own work (the split-K
+  // counters of the GEMM launched next on the same stream).
+  uint32_t* zero_ptr = nullptr;
+  int zero_n = 0;
+  // W4A4 decode GEMV with the SwiGLU-NVFP4 epilogue at M = 1 only: when
+  // set, `a` is bf16 [M, K] and each workgroup quantizes it to NVFP4 with
+  // this global scale inverse as it stages it (the same arithmetic as
+  // launch_quantize); a_scales is unused.
+  const float* a_g_inv = nullptr;
 };
+
+// Split-K is valid for the dense epilogues, with the buffers given and every
+// split non-empty: tiles per split ceil(T / ksplit), (ksplit - 1) of them
+// fewer than T.
+inline bool splitk_valid(const GemmArgs& a, int epi) {
+  if (a.ksplit == 1) return true;
+  const int64_t T = a.K / 256, per = (T + a.ksplit - 1) / a.ksplit;
+  return a.ksplit > 1 && (epi == kOutF32 || epi == kOutBF16) && a.part && a.counters &&
+         (a.ksplit - 1) * per < T;
+}
+// Launch shape of the weight-streaming kernel's dense GEMM: output tiles
+// (workgroups before any K split), floats of one partial result tile, waves
+// per workgroup.
+struct TileShape {
+  int64_t units, tile_floats, waves;
+};
+TileShape stream_shape(int64_t M, int64_t N);
+
+// The number of K splits that brings a dense GEMM of `units` output tiles to
+// about `target` workgroups, each split keeping at least `min_tiles` tiles.
+inline int splitk_ways(int64_t units, int64_t T, int64_t target, int64_t min_tiles) {
+  int64_t ks = units >= target ? 1 : (target + units - 1) / units;
+  if (ks > 8) ks = 8;
+  while (ks > 1 && ((ks - 1) * ((T + ks - 1) / ks) >= T || (T + ks - 1) / ks < min_tiles)) --ks;
+  return (int)ks;
+}
 
 // epi: Epi enum of device_common.h; mode: Mode enum.
 hipError_t launch_stream_gemm(int mode, int epi, const GemmArgs& a, hipStream_t s);

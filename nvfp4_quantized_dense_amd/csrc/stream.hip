@@ -10,10 +10,10 @@
 // their NVFP4 or bf16 form and dequantized in registers like the weights.
 //
 // Work split: a workgroup owns NG packed row groups (2 for the SwiGLU pair
-// gate/up) and NW waves divide the K tiles between them; each wave keeps the
-// next tile's loads in flight while it multiplies the current one (two
-// register sets, branch-free prefetch). Partial sums are combined through LDS
-// in a fixed order (deterministic).
+// gate/up) and NW waves divide the K tiles between them; each wave loads a
+// tile (weights and activations together, branch-free: past the last tile
+// the loads are out of range) and multiplies it. Partial sums are combined
+// through LDS in a fixed order (deterministic).
 #include "device_common.h"
 #include "kernels.h"
 
@@ -29,19 +29,24 @@ struct StreamSrc {
   uint32_t s_row[NT];
 };
 
+// One K tile for one wave: NG weight tiles and the activation slices of
+// NT token groups (W4A4: codes and scales; W4A16: bf16, 64 bytes per lane
+// and half tile).
 template <int MODE, int NG, int NT>
 struct StreamTile {
   u32x4 wc[NG][2];
   uint32_t wsd[NG];
-  u32x4 xc[MODE == kW4A4 ? NT : 1][2];
-  uint32_t xsd[MODE == kW4A4 ? NT : 1];
+  u32x4 xc[NT][MODE == kW4A4 ? 2 : 8];
+  uint32_t xsd[MODE == kW4A4 ? NT : 1][2];
 };
 
+// Tile t of row groups of T tiles. From tile t_end on every load is out of
+// range: zeros, no memory access, and the tile adds +0.
 template <int MODE, int NG, int NT>
 __device__ __forceinline__ void stream_load(StreamTile<MODE, NG, NT>& d, const StreamSrc<MODE, NT>& src,
-                                            int64_t rg0, int64_t T, int64_t t, int lane) {
+                                            int64_t rg0, int T, int t_end, int t, int lane) {
   const int q = lane >> 4;
-  const bool in = t < T;
+  const bool in = t < t_end;
   const uint32_t tw = in ? (uint32_t)(t * kTileBytes) : kOutOfRange;
 #pragma unroll
   for (int g = 0; g < NG; ++g) {
@@ -57,14 +62,23 @@ __device__ __forceinline__ void stream_load(StreamTile<MODE, NG, NT>& d, const S
     for (int j = 0; j < NT; ++j) {
       d.xc[j][0] = bload16(src.a, src.a_row[j] + ta);
       d.xc[j][1] = bload16(src.a, src.a_row[j] + ta + 64);
-      d.xsd[j] = bload2(src.s, src.s_row[j] + ts) | (bload2(src.s, src.s_row[j] + ts + 8) << 16);
+      d.xsd[j][0] = bload2(src.s, src.s_row[j] + ts);
+      d.xsd[j][1] = bload2(src.s, src.s_row[j] + ts + 8);
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const uint32_t tx = in ? (uint32_t)((t * kTileK + c * 128 + q * 32) * 2) : kOutOfRange;
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) d.xc[j][4 * c + u] = bload16(src.a, src.a_row[j] + tx + 16 * u);
     }
   }
 }
 
 template <int MODE, int NG, int NT>
-__device__ __forceinline__ void stream_compute(f32x4 (&acc)[NG][NT], const StreamTile<MODE, NG, NT>& d,
-                                               const StreamSrc<MODE, NT>& src, int64_t t, int lane) {
+__device__ __forceinline__ void stream_compute(f32x4 (&acc)[NG][NT], const StreamTile<MODE, NG, NT>& d) {
   if constexpr (MODE == kW4A4) {
     _Float16 ws[NG][4], xs[NT][4];
 #pragma unroll
@@ -74,8 +88,8 @@ __device__ __forceinline__ void stream_compute(f32x4 (&acc)[NG][NT], const Strea
     }
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-      xs[j][0] = scale_f16<0>(d.xsd[j]); xs[j][1] = scale_f16<1>(d.xsd[j]);
-      xs[j][2] = scale_f16<2>(d.xsd[j]); xs[j][3] = scale_f16<3>(d.xsd[j]);
+      xs[j][0] = scale_f16<0>(d.xsd[j][0]); xs[j][1] = scale_f16<1>(d.xsd[j][0]);
+      xs[j][2] = scale_f16<0>(d.xsd[j][1]); xs[j][3] = scale_f16<1>(d.xsd[j][1]);
     }
 #pragma unroll
     for (int c = 0; c < 2; ++c)
@@ -93,7 +107,6 @@ __device__ __forceinline__ void stream_compute(f32x4 (&acc)[NG][NT], const Strea
           for (int j = 0; j < NT; ++j) acc[g][j] = mfma16x16x32(A[g], B[j], acc[g][j]);
       }
   } else {
-    const int q = lane >> 4;
     float ws[NG][4];
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
@@ -102,12 +115,6 @@ __device__ __forceinline__ void stream_compute(f32x4 (&acc)[NG][NT], const Strea
     }
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      u32x4 xv[NT][4];
-      const uint32_t tx = (uint32_t)((t * kTileK + c * 128 + q * 32) * 2);
-#pragma unroll
-      for (int j = 0; j < NT; ++j)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) xv[j][u] = bload16(src.a, src.a_row[j] + tx + 16 * u);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int sb = 2 * c + (u >> 1);
@@ -117,7 +124,7 @@ __device__ __forceinline__ void stream_compute(f32x4 (&acc)[NG][NT], const Strea
 #pragma unroll
         for (int g = 0; g < NG; ++g)
 #pragma unroll
-          for (int j = 0; j < NT; ++j) acc[g][j] = mfma16x16x32(A[g], as_bf16x8(xv[j][u]), acc[g][j]);
+          for (int j = 0; j < NT; ++j) acc[g][j] = mfma16x16x32(A[g], as_bf16x8(d.xc[j][4 * c + u]), acc[g][j]);
       }
     }
   }
@@ -163,17 +170,27 @@ __global__ __launch_bounds__(NW * 64) void k_stream(GemmArgs args) {
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[g][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  int64_t t = wave;
-  StreamTile<MODE, NG, NT> ta, tb;
-  stream_load<MODE, NG, NT>(ta, src, rg0, T, t, lane);
-  while (t < T) {
-    stream_load<MODE, NG, NT>(tb, src, rg0, T, t + NW, lane);
-    stream_compute<MODE, NG, NT>(acc, ta, src, t, lane);
+  // Tiles t = wave, wave + NW, ...: one tile in flight per wave (measured
+  // faster than two at M = 2..16: fewer outstanding requests stream better,
+  // and one register set leaves room for more waves). The scheduling
+  // barriers keep the arithmetic after the wait for its tile and the next
+  // tile's loads after the arithmetic.
+  clear_words(args.zero_ptr, args.zero_n);
+  // K tiles [t0, t1) of this workgroup's split (all of them without split-K).
+  const int nt = (int)T;
+  const int ks = args.ksplit;
+  const int tper = (nt + ks - 1) / ks;
+  const int t0 = (int)blockIdx.z * tper;
+  const int t1 = t0 + tper < nt ? t0 + tper : nt;
+  int t = t0 + wave;
+  StreamTile<MODE, NG, NT> ta;
+  stream_load<MODE, NG, NT>(ta, src, rg0, nt, t1, t, lane);
+  while (t < t1) {
+    stream_compute<MODE, NG, NT>(acc, ta);
+    __builtin_amdgcn_sched_barrier(0);
     t += NW;
-    if (t >= T) break;
-    stream_load<MODE, NG, NT>(ta, src, rg0, T, t + NW, lane);
-    stream_compute<MODE, NG, NT>(acc, tb, src, t, lane);
-    t += NW;
+    stream_load<MODE, NG, NT>(ta, src, rg0, nt, t1, t, lane);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // Combine the waves' partial sums in wave order.
@@ -199,6 +216,12 @@ __global__ __launch_bounds__(NW * 64) void k_stream(GemmArgs args) {
         }
   }
 
+  if constexpr (!EpiTraits<EPI>::swiglu) {
+    if (ks > 1) {
+      const int64_t unit = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+      if (!splitk_last<NT>(acc[0], args.part, args.counters, ks, unit, (int)blockIdx.z, lane)) return;
+    }
+  }
   const float alpha = *args.alpha;
   if constexpr (EpiTraits<EPI>::swiglu) {
     const float g2i = (EPI == kSwigluNvfp4) ? *args.g2_inv : 0.0f;
@@ -222,28 +245,24 @@ __global__ __launch_bounds__(NW * 64) void k_stream(GemmArgs args) {
 template <int MODE, int EPI, int NT, int NW>
 static hipError_t launch_nt_nw(const GemmArgs& a, hipStream_t s) {
   constexpr int NG = EpiTraits<EPI>::swiglu ? 2 : 1;
-  dim3 grid((unsigned)(a.N / kTileRows / NG), (unsigned)((a.M + 16 * NT - 1) / (16 * NT)));
+  dim3 grid((unsigned)(a.N / kTileRows / NG), (unsigned)((a.M + 16 * NT - 1) / (16 * NT)), (unsigned)a.ksplit);
   k_stream<MODE, EPI, NT, NW><<<grid, NW * 64, 0, s>>>(a);
   return hipGetLastError();
 }
 
-// Waves per workgroup: enough that the grid keeps about 16 waves per CU,
-// capped where two register sets of NT token groups would not fit the
-// per-lane register budget of larger workgroups (16 waves: 128 VGPRs).
+// Waves per workgroup: 8 for one token group (measured best at M = 2..16
+// on the decode shapes), 4 for more token groups (their register sets leave
+// room for fewer waves per SIMD).
 template <int MODE, int EPI, int NT>
 static hipError_t launch_nt(const GemmArgs& a, hipStream_t s) {
-  constexpr int NG = EpiTraits<EPI>::swiglu ? 2 : 1;
-  const int64_t wgs = a.N / kTileRows / NG * ((a.M + 16 * NT - 1) / (16 * NT));
-  if constexpr (NT >= 3) {
-    return launch_nt_nw<MODE, EPI, NT, 4>(a, s);
-  } else if constexpr (NT == 2) {
-    if (wgs >= 1024) return launch_nt_nw<MODE, EPI, NT, 4>(a, s);
-    return launch_nt_nw<MODE, EPI, NT, 8>(a, s);
-  } else {
-    if (wgs >= 1024) return launch_nt_nw<MODE, EPI, NT, 4>(a, s);
-    if (wgs >= 512) return launch_nt_nw<MODE, EPI, NT, 8>(a, s);
-    return launch_nt_nw<MODE, EPI, NT, 16>(a, s);
-  }
+  if constexpr (NT == 1) return launch_nt_nw<MODE, EPI, NT, 8>(a, s);
+  return launch_nt_nw<MODE, EPI, NT, 4>(a, s);
+}
+
+TileShape stream_shape(int64_t M, int64_t N) {
+  int64_t groups = (M + 15) / 16;
+  const int64_t nt = groups < 4 ? groups : 4;
+  return TileShape{N / kTileRows * ((M + 16 * nt - 1) / (16 * nt)), 256 * nt, nt == 1 ? 8 : 4};
 }
 
 template <int MODE, int EPI>
@@ -259,6 +278,7 @@ static hipError_t launch_mode_epi(const GemmArgs& a, hipStream_t s) {
 // buffer offsets); the caller checks.
 hipError_t launch_stream_gemm(int mode, int epi, const GemmArgs& a, hipStream_t s) {
   if (a.M == 0) return hipSuccess;
+  if (!splitk_valid(a, epi)) return hipErrorInvalidValue;
   if (mode == kW4A4) {
     switch (epi) {
       case kOutF32: return launch_mode_epi<kW4A4, kOutF32>(a, s);

@@ -254,6 +254,54 @@ def test_mlp_small_batch_full_size(M):
     _check_mlp("w4a4", M, 7168, 18432, rows=np.arange(min(M, 16)))
 
 
+# -- mlp_forward workspace use: split-K of the down projection (weight-
+# streaming kernel) and the decode GEMV's in-kernel activation quantization
+#
+# Hidden 512 leaves 32 output row groups, so the streaming kernel splits
+# the down projection's K (intermediate) over several workgroups: 27 tiles
+# (6912) split unevenly, 32 tiles (8192) evenly. The workspace starts as
+# 0xFF bytes (the counters must be cleared by the gate_up launch) and is
+# reused by a call on another input and then on the first input again,
+# which must give bit-identical output (counts reset, no stale partials).
+# The GEMV cases run the W4A4 gate_up with the quantization of x fused.
+
+@pytest.mark.parametrize("I", [6912, 8192])
+@pytest.mark.parametrize("kpath,M", [("gemv", 1), ("gemv", 2), ("stream", 3), ("stream", 16),
+                                     ("stream", 40)])
+@pytest.mark.parametrize("mode", ["w4a4", "w4a16"])
+def test_mlp_split_k(mode, kpath, M, I):
+    H = 512
+    prev = nv.set_path(PATHS[kpath])
+    try:
+        w = mlp_weights(H, I, 0)
+        p_gu, p_d = packed_weights(H, I, 0)
+        x = synth.activations(M + I, M, H)
+        xd = to_dev(x)
+        nws = nv.mlp_workspace_bytes(0 if mode == "w4a4" else 1, M, H, I)
+        ws = torch.full((nws,), 0xFF, dtype=torch.uint8, device=dev())
+        if mode == "w4a4":
+            sc = calibrate_activation_scales(x, w)
+            args = (0, xd, p_gu, scalar(sc["a_gu"]), p_d, scalar(sc["a_d"]), I)
+            kw = dict(g1_inv=scalar(sc["g1_inv"]), g2_inv=scalar(sc["g2_inv"]), ws=ws)
+            r = oracle.mlp_w4a4(x, w["c_gu"], w["s_gu"], sc["a_gu"], w["c_d"], w["s_d"], sc["a_d"],
+                                sc["g1_inv"], sc["g2_inv"])
+        else:
+            args = (1, xd, p_gu, scalar(w["g_gu"]), p_d, scalar(w["g_d"]), I)
+            kw = dict(ws=ws)
+            r = oracle.mlp_w4a16(x, w["c_gu"], w["s_gu"], w["g_gu"], w["c_d"], w["s_d"], w["g_d"])
+        y1 = to_host(nv.mlp_forward(*args, **kw))
+        # another input through the same workspace, then the first again:
+        # partials or counts left from one call must not leak into the next
+        xb = to_dev(synth.activations(M + I + 1, M, H))
+        nv.mlp_forward(args[0], xb, *args[2:], **kw)
+        y2 = to_host(nv.mlp_forward(*args, **kw))
+        torch.cuda.synchronize()
+        gemm_close(y1, r["out"], f"split-K mlp {mode} {kpath} M={M} I={I}")
+        assert np.array_equal(y1, y2), "the same input through a reused workspace differs"
+    finally:
+        nv.set_path(prev)
+
+
 def test_mlp_prefill_full_size_sampled_rows():
     """Prefill W4A4: M=8192 on the GPU, 64 seeded rows checked by the oracle."""
     nv.set_path(nv.PATH_AUTO)
