@@ -206,8 +206,13 @@ __global__ __launch_bounds__(NWR * NWT * 64, 1) void k_tiled2(GemmArgs args, int
       xsd[j] = (uint32_t)*reinterpret_cast<const uint16_t*>(srow + 2 * q) |
                ((uint32_t)*reinterpret_cast<const uint16_t*>(srow + 8 + 2 * q) << 16);
     }
+    // Raised wave priority over the dequant + MFMA section (measured +1%:
+    // a wave that has its stage's operands keeps the matrix core fed ahead
+    // of waves still issuing their copies).
+    __builtin_amdgcn_s_setprio(1);
     compute_chunk<0, GR, TG>(acc, buf, GR * wr, TG * wt, lane, wsd, xsd);
     compute_chunk<1, GR, TG>(acc, buf, GR * wr, TG * wt, lane, wsd, xsd);
+    __builtin_amdgcn_s_setprio(0);
   }
 
   const float alpha = *args.alpha;
