@@ -179,7 +179,8 @@ int gemm_swiglu(int mode, const void* a, const uint8_t* a_scales, const void* w_
                 void* stream);
 
 /* Workspace bytes mlp_forward needs: W4A4 holds x and h in NVFP4; W4A16
- * holds h in bf16. Each region starts 256-byte aligned. */
+ * holds h in bf16. Each region starts 256-byte aligned. At W4A4 M = 1 it
+ * also holds the single-launch decode kernel's records (see mlp_forward). */
 size_t mlp_workspace_bytes(int mode, int64_t M, int64_t H, int64_t I);
 
 /*
@@ -190,6 +191,13 @@ size_t mlp_workspace_bytes(int mode, int64_t M, int64_t H, int64_t I);
  *          alpha_d = g_wd) -> out; g1_inv and g2_inv must be NULL.
  * x bf16 [M, H]; w_gu_packed: SWIGLU packed [2I, H]; w_d_packed: PLAIN packed
  * [H, I]; H % 256 == 0, I % 256 == 0. out [M, H] of out_dtype.
+ * W4A4 at M = 1 under NVFP4_PATH_AUTO (and outside stream capture) runs as
+ * one launch: its workgroups pass h and the down projection's partial sums
+ * to each other through 64-bit records in the workspace, each tagged with a
+ * 32-bit number new to the call. The workspace must therefore hold zeros the
+ * first time it is used this way (every call leaves it ready for the next;
+ * memory with other contents could hold a current tag by chance). Calls that
+ * share a workspace must not overlap (the same holds on every path).
  */
 int mlp_forward(int mode, const uint16_t* x, int64_t M, int64_t H, int64_t I,
                 const void* w_gu_packed, const float* alpha_gu, const void* w_d_packed,

@@ -210,7 +210,7 @@ def mlp_forward(mode, x, w_gu_packed, alpha_gu, w_d_packed, alpha_d, I, g1_inv=N
     M, H = x.shape
     nws = mlp_workspace_bytes(mode, M, H, I)
     if ws is None:
-        ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=x.device)
+        ws = torch.zeros(max(nws, 1), dtype=torch.uint8, device=x.device)
     if out is None:
         out = torch.empty((M, H), dtype=out_dtype, device=x.device)
     _check("mlp_forward", lib().mlp_forward(int(mode), _ptr(x), M, H, I, _ptr(w_gu_packed), _ptr(alpha_gu),

@@ -5,10 +5,12 @@
 
 #include <algorithm>
 #include <atomic>
+#include <chrono>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
 #include <mutex>
+#include <random>
 
 #include "../../include/nvfp4.h"
 #include "kernels.h"
@@ -69,6 +71,31 @@ int hip_status(hipError_t e, const char* what) {
 }
 
 hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// Epochs of the single-launch decode kernel's records: a new value for every
+// launch, counting up from a random start drawn once per process (records
+// are tagged with the low 32 bits, which are never 0, the tag of no record).
+uint64_t next_epoch() {
+  static std::atomic<uint64_t> epoch{0};
+  static std::once_flag once;
+  std::call_once(once, [] {
+    std::random_device rd;
+    const uint64_t t = (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count();
+    epoch.store((((uint64_t)rd() << 32) | rd()) ^ (t * 0x9E3779B97F4A7C15ull));
+  });
+  for (;;) {
+    const uint64_t e = epoch.fetch_add(1) + 1;
+    if ((uint32_t)e != 0u) return e;
+  }
+}
+
+// The decode kernel needs a fresh epoch per launch, which a replayed graph
+// would not give: under stream capture the two-kernel path runs.
+bool stream_capturing(hipStream_t s) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess) return true;
+  return cs != hipStreamCaptureStatusNone;
+}
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
@@ -315,14 +342,21 @@ static size_t mlp_act_bytes(int mode, size_t m, int64_t H, int64_t I) {
   return align256(m * I * 2);
 }
 
-// Split-K part: sized for the largest plan over the decode kernels, so the
-// size does not depend on the process-wide path override.
+// Records of the single-launch W4A4 decode kernel.
+static size_t decode_bytes(int64_t H, int64_t I) {
+  return align256((size_t)nvfp4::decode_record_words(H, I) * sizeof(uint64_t));
+}
+
+// Split-K part: sized for the largest plan over the decode kernels (and, at
+// W4A4 M = 1, for the single-launch decode kernel's records), so the size
+// does not depend on the process-wide path override.
 static size_t mlp_split_bytes(int mode, int64_t M, int64_t H, int64_t I) {
   size_t most = 0;
   for (int path : {NVFP4_PATH_GEMV, NVFP4_PATH_STREAM}) {
     const SplitPlan p = split_plan(mlp_kernel(path, mode, M, H, I), mode, M, H, I);
     most = std::max(most, p.part_bytes + p.counter_bytes);
   }
+  if (mode == NVFP4_MODE_W4A4 && M == 1 && nvfp4::decode_supported(H, I)) most = std::max(most, decode_bytes(H, I));
   return most;
 }
 
@@ -387,6 +421,15 @@ int mlp_forward(int mode, const uint16_t* x, int64_t M, int64_t H, int64_t I, co
     uint8_t* xs = xq + align256(m * H / 2);
     uint8_t* hq = xs + align256(m * H / 16);
     uint8_t* hs = hq + align256(m * I / 2);
+    // One token under the automatic path: the whole forward in one launch
+    // (x quantized as it is staged, h handed from the gate_up workgroups to
+    // the down workgroups as epoch-tagged records in the workspace).
+    if (M == 1 && g_path.load() == NVFP4_PATH_AUTO && nvfp4::decode_supported(H, I) && !stream_capturing(s)) {
+      nvfp4::DecodeArgs d{x, g1_inv, static_cast<const uint8_t*>(w_gu_packed), static_cast<const uint8_t*>(w_d_packed),
+                          alpha_gu, alpha_d, g2_inv, hq, hs, out, reinterpret_cast<uint64_t*>(split_base),
+                          H, I, nvfp4::decode_splits(H, I), next_epoch()};
+      return hip_status(nvfp4::launch_decode_mlp(epi_out, d, s), "mlp_forward decode");
+    }
     // At M = 1 the decode GEMV quantizes x itself as it stages it (no
     // separate launch); otherwise x is quantized by launch_quantize (with two
     // token rows per workgroup the fused variant needs more registers than

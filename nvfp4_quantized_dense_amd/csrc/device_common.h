@@ -148,6 +148,11 @@ __device__ __forceinline__ uint32_t bload4_nt(Rsrc r, uint32_t voff, uint32_t so
 __device__ __forceinline__ u32x4 bload16(Rsrc r, uint32_t voff) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0);
 }
+// Device-scope (sc1) load: sees stores of other workgroups made with
+// device-scope stores, whichever XCD they ran on.
+__device__ __forceinline__ u32x4 bload16_dev(Rsrc r, uint32_t voff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 16);
+}
 __device__ __forceinline__ uint32_t bload2(Rsrc r, uint32_t voff) {
   return __builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, 0, 0);
 }
@@ -197,6 +202,15 @@ __device__ __forceinline__ bool splitk_last(f32x4 (&res)[NT], float* part, uint3
   return true;
 }
 
+// A kernel-uniform scalar read at this point of the program: the scalar load
+// is issued here and kept in a register, not sunk to its use (an epilogue
+// reading it after the main loop would wait there for a memory round trip).
+__device__ __forceinline__ float uniform_now(const float* p) {
+  int v = __builtin_amdgcn_readfirstlane(__float_as_int(*p));
+  asm volatile("" : "+s"(v));
+  return __int_as_float(v);
+}
+
 // Workgroup (0, 0, 0) clears n words at p (the next GEMM's split-K counters).
 __device__ __forceinline__ void clear_words(uint32_t* p, int n) {
   if (p != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0)
@@ -228,42 +242,61 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
   return s * u;
 }
 
-// SwiGLU of matching gate/up tiles. Lane l holds outputs j = j0 + 4(l/16) + r
-// of token l % 16; j0 is a multiple of 16, so the 64 lanes of the wave hold
-// whole 16-element NVFP4 blocks of h (one per token column). All lanes of the
-// wave must call this (the block amax is a cross-lane reduction).
+// SwiGLU of matching gate/up tiles re-quantized to NVFP4. Lane l holds
+// outputs j0 + 4(l/16) + r of token l % 16 (j0 a multiple of 16), so the 64
+// lanes of the wave hold whole 16-element blocks of h, one per token column.
+// Returns the lane's 4 codes (16 bits, element 4(l/16) + r in bits 4r..) and
+// the block's scale byte. All lanes of the wave must call this (the block
+// amax is a cross-lane reduction).
+struct SwigluBlock {
+  uint32_t codes;  // 16 bits
+  uint32_t scale;  // E4M3 byte
+};
+__device__ __forceinline__ SwigluBlock swiglu_nvfp4(const f32x4& gate, const f32x4& up, float alpha,
+                                                    float g2_inv) {
+  float h[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) h[r] = silu_mul(alpha * gate[r], alpha * up[r]);
+  float amax = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(h[0]), __builtin_fabsf(h[1])),
+                               __builtin_fmaxf(__builtin_fabsf(h[2]), __builtin_fabsf(h[3])));
+  amax = __builtin_fmaxf(amax, __shfl_xor(amax, 16));
+  amax = __builtin_fmaxf(amax, __shfl_xor(amax, 32));
+  BlockScale bs = block_scale(amax, g2_inv);
+  SwigluBlock b;
+  b.codes = e2m1_from_f32(h[0] * bs.r) | (e2m1_from_f32(h[1] * bs.r) << 4) |
+            (e2m1_from_f32(h[2] * bs.r) << 8) | (e2m1_from_f32(h[3] * bs.r) << 12);
+  b.scale = bs.byte;
+  return b;
+}
+
+// SwiGLU of matching gate/up tiles, stored. Lane layout as swiglu_nvfp4; all
+// lanes of the wave must call this for the NVFP4 output.
 template <int E>
 __device__ __forceinline__ void store_swiglu(const f32x4& gate, const f32x4& up, float alpha,
                                              float g2_inv, bool valid, int64_t token, int64_t j0,
                                              int lane, int64_t I, void* out, uint8_t* out_scales) {
   const int q = lane >> 4;
-  float h[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) h[r] = silu_mul(alpha * gate[r], alpha * up[r]);
   const int64_t j = j0 + 4 * q;
-  if constexpr (E == kSwigluF32) {
+  if constexpr (E == kSwigluF32 || E == kSwigluBF16) {
+    float h[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) h[r] = silu_mul(alpha * gate[r], alpha * up[r]);
     if (valid) {
-      f32x4 v = {h[0], h[1], h[2], h[3]};
-      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + token * I + j) = v;
-    }
-  } else if constexpr (E == kSwigluBF16) {
-    if (valid) {
-      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-      bf16x4 b = {(__bf16)h[0], (__bf16)h[1], (__bf16)h[2], (__bf16)h[3]};
-      *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(out) + token * I + j) = b;
+      if constexpr (E == kSwigluF32) {
+        f32x4 v = {h[0], h[1], h[2], h[3]};
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + token * I + j) = v;
+      } else {
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        bf16x4 b = {(__bf16)h[0], (__bf16)h[1], (__bf16)h[2], (__bf16)h[3]};
+        *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(out) + token * I + j) = b;
+      }
     }
   } else {
-    float amax = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(h[0]), __builtin_fabsf(h[1])),
-                                 __builtin_fmaxf(__builtin_fabsf(h[2]), __builtin_fabsf(h[3])));
-    amax = __builtin_fmaxf(amax, __shfl_xor(amax, 16));
-    amax = __builtin_fmaxf(amax, __shfl_xor(amax, 32));
-    BlockScale bs = block_scale(amax, g2_inv);
-    uint32_t packed = e2m1_from_f32(h[0] * bs.r) | (e2m1_from_f32(h[1] * bs.r) << 4) |
-                      (e2m1_from_f32(h[2] * bs.r) << 8) | (e2m1_from_f32(h[3] * bs.r) << 12);
+    const SwigluBlock b = swiglu_nvfp4(gate, up, alpha, g2_inv);
     if (valid) {
       uint8_t* codes = reinterpret_cast<uint8_t*>(out);
-      *reinterpret_cast<uint16_t*>(codes + token * (I / 2) + j / 2) = (uint16_t)packed;
-      if (q == 0) out_scales[token * (I / 16) + j0 / 16] = (uint8_t)bs.byte;
+      *reinterpret_cast<uint16_t*>(codes + token * (I / 2) + j / 2) = (uint16_t)b.codes;
+      if (q == 0) out_scales[token * (I / 16) + j0 / 16] = (uint8_t)b.scale;
     }
   }
 }

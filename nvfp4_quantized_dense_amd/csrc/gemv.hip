@@ -137,6 +137,8 @@ __global__ __launch_bounds__(NW * 64) void k_valu_gemv(GemmArgs args) {
     for (int m = 0; m < MT; ++m) acc[g][m] = 0.0f;
 
   clear_words(args.zero_ptr, args.zero_n);
+  const float alpha = uniform_now(args.alpha);
+  const float g2i = EPI == kSwigluNvfp4 ? uniform_now(args.g2_inv) : 0.0f;
   // K tiles [t0, t1): all of them (the staging and loop are written for a
   // tile range).
   const int nt = (int)T;
@@ -237,10 +239,8 @@ __global__ __launch_bounds__(NW * 64) void k_valu_gemv(GemmArgs args) {
       for (int w = 0; w < NW; ++w) s += red[w][g][tm][4 * q + r];
       res[g][r] = lvalid ? s : 0.0f;
     }
-  const float alpha = *args.alpha;
   const int64_t token = tok0 + tl;
   if constexpr (EpiTraits<EPI>::swiglu) {
-    const float g2i = (EPI == kSwigluNvfp4) ? *args.g2_inv : 0.0f;
     store_swiglu<EPI>(res[0], res[1], alpha, g2i, lvalid, token, (int64_t)blockIdx.x * kTileRows,
                       lane, args.N / 2, args.out, args.out_scales);
   } else {

@@ -92,7 +92,33 @@ constexpr int64_t kFp4GemvLdsBytes = 65536;
 bool fp4_gemv_supported(int64_t M, int64_t K);
 hipError_t launch_fp4_gemv(int epi, const GemmArgs& a, hipStream_t s);
 hipError_t launch_tiled_gemm(int mode, int epi, const GemmArgs& a, hipStream_t s);
+
 // W4A4 only; packed weight, activation codes and scales each < 2^31 bytes.
 hipError_t launch_tiled2_gemm(int epi, const GemmArgs& a, hipStream_t s);
+
+// decode.hip: the W4A4 MLP forward of one token in one launch (gate_up
+// units hand h to the down units, and those their partial sums to the last
+// K split, as 64-bit records tagged with the launch's epoch).
+constexpr int kDecodeMaxSplits = 8;
+struct DecodeArgs {
+  const void* x;          // bf16 [1, H]
+  const float* g1_inv;    // global scale inverse of x
+  const uint8_t* w_gu;    // SWIGLU packed [2I, H]
+  const uint8_t* w_d;     // PLAIN packed [H, I]
+  const float* alpha_gu;
+  const float* alpha_d;
+  const float* g2_inv;    // global scale inverse of h
+  uint8_t* h_codes;       // [I / 2], written (as by the two-launch path)
+  uint8_t* h_scales;      // [I / 16], written
+  void* out;              // [1, H], f32 or bf16
+  uint64_t* records;      // decode_record_words(H, I) words: zeros or left by earlier launches
+  int64_t H, I;
+  int ksplit;             // decode_splits(H, I), or another count the launcher accepts
+  uint64_t epoch;         // low 32 bits nonzero, differing from the last 2^32 - 1 launches' on records
+};
+bool decode_supported(int64_t H, int64_t I);
+int decode_splits(int64_t H, int64_t I);
+int64_t decode_record_words(int64_t H, int64_t I);
+hipError_t launch_decode_mlp(int epi, const DecodeArgs& d, hipStream_t s);
 
 }  // namespace nvfp4

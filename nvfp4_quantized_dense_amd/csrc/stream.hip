@@ -144,6 +144,8 @@ __global__ __launch_bounds__(NW * 64) void k_stream(GemmArgs args) {
   const int64_t K = args.K, T = K / kTileK;
   const int64_t rg0 = (int64_t)blockIdx.x * NG;
   const int64_t tok0 = (int64_t)blockIdx.y * 16 * NT;
+  const float alpha = uniform_now(args.alpha);
+  const float g2i = EPI == kSwigluNvfp4 ? uniform_now(args.g2_inv) : 0.0f;
 
   StreamSrc<MODE, NT> src;
   src.w = make_rsrc(args.w, (uint32_t)(args.N / kTileRows * T * kTileBytes));
@@ -222,9 +224,7 @@ __global__ __launch_bounds__(NW * 64) void k_stream(GemmArgs args) {
       if (!splitk_last<NT>(acc[0], args.part, args.counters, ks, unit, (int)blockIdx.z, lane)) return;
     }
   }
-  const float alpha = *args.alpha;
   if constexpr (EpiTraits<EPI>::swiglu) {
-    const float g2i = (EPI == kSwigluNvfp4) ? *args.g2_inv : 0.0f;
     const int64_t I = args.N / 2;
     const int64_t j0 = (int64_t)blockIdx.x * kTileRows;
 #pragma unroll

@@ -302,6 +302,98 @@ def test_mlp_split_k(mode, kpath, M, I):
         nv.set_path(prev)
 
 
+# -- single-launch W4A4 decode (M = 1 under the automatic path) ----------------
+#
+# The gate_up workgroups hand h to the down workgroups, and those their
+# partial sums to the last K split, as records tagged with a per-launch
+# epoch; the down projection's K is split over 1 to 5 workgroups per row
+# group over these shapes (ragged where the tiles do not divide). The
+# workspace starts zero-filled and is reused by a launch on another input,
+# so records left by an earlier launch would show. h (NVFP4, in the
+# workspace) must equal the two-launch GEMV path's byte for byte: the same
+# arithmetic produces it.
+
+def _ws_h(ws, H, I):
+    """h codes and scale bytes inside an M = 1 W4A4 mlp_forward workspace."""
+    a256 = lambda v: (v + 255) // 256 * 256
+    o = a256(H // 2) + a256(H // 16)
+    b = to_host(ws)
+    return b[o:o + I // 2].copy(), b[o + a256(I // 2):o + a256(I // 2) + I // 16].copy()
+
+
+@pytest.mark.parametrize("H,I", [(256, 256), (256, 4096), (512, 4352), (1024, 2304), (2048, 6912),
+                                 (256, 18432)])
+def test_mlp_decode_single_launch(H, I):
+    nv.set_path(nv.PATH_AUTO)
+    w = mlp_weights(H, I, 0)
+    p_gu, p_d = packed_weights(H, I, 0)
+    x = synth.activations(H + I, 1, H)
+    sc = calibrate_activation_scales(x, w)
+    args = (0, to_dev(x), p_gu, scalar(sc["a_gu"]), p_d, scalar(sc["a_d"]), I)
+    gkw = dict(g1_inv=scalar(sc["g1_inv"]), g2_inv=scalar(sc["g2_inv"]))
+    nws = nv.mlp_workspace_bytes(0, 1, H, I)
+    ws = torch.zeros((nws,), dtype=torch.uint8, device=dev())
+    y1 = to_host(nv.mlp_forward(*args, ws=ws, **gkw))
+    h1 = _ws_h(ws, H, I)
+    nv.mlp_forward(0, to_dev(synth.activations(H + I + 1, 1, H)), *args[2:], ws=ws, **gkw)
+    y2 = to_host(nv.mlp_forward(*args, ws=ws, **gkw))
+    yb = to_host(nv.mlp_forward(*args, ws=ws, out_dtype=torch.bfloat16, **gkw))
+    prev = nv.set_path(PATHS["gemv"])
+    try:
+        ws2 = torch.full((nws,), 0xFF, dtype=torch.uint8, device=dev())
+        y3 = to_host(nv.mlp_forward(*args, ws=ws2, **gkw))
+        h3 = _ws_h(ws2, H, I)
+    finally:
+        nv.set_path(prev)
+    torch.cuda.synchronize()
+    r = oracle.mlp_w4a4(x, w["c_gu"], w["s_gu"], sc["a_gu"], w["c_d"], w["s_d"], sc["a_d"],
+                        sc["g1_inv"], sc["g2_inv"])
+    gemm_close(y1, r["out"], f"decode H={H} I={I}")
+    gemm_close(y3, r["out"], f"two-launch decode H={H} I={I}")
+    assert np.array_equal(y1, y2), "the same input through a reused workspace differs"
+    assert np.array_equal(yb, synth.f32_to_bf16_bits(y1)), "bf16 output is not the f32 output rounded"
+    assert np.array_equal(h1[0], h3[0]) and np.array_equal(h1[1], h3[1]), "h differs from the two-launch path"
+
+
+def test_mlp_decode_graph_capture():
+    """Under stream capture mlp_forward records the two-launch path (the
+    single launch needs a new epoch per run); replays match eager results."""
+    nv.set_path(nv.PATH_AUTO)
+    H, I = 512, 4352
+    w = mlp_weights(H, I, 0)
+    p_gu, p_d = packed_weights(H, I, 0)
+    xs = [synth.activations(7 + k, 1, H) for k in range(3)]
+    sc = calibrate_activation_scales(xs[0], w)
+    xd = to_dev(xs[0])
+    nws = nv.mlp_workspace_bytes(0, 1, H, I)
+    ws = torch.zeros((nws,), dtype=torch.uint8, device=dev())
+    out = torch.empty((1, H), dtype=torch.float32, device=dev())
+    a_gu, a_d = scalar(sc["a_gu"]), scalar(sc["a_d"])
+    g1i, g2i = scalar(sc["g1_inv"]), scalar(sc["g2_inv"])
+    call = lambda: nv.mlp_forward(0, xd, p_gu, a_gu, p_d, a_d, I, g1_inv=g1i, g2_inv=g2i, ws=ws, out=out)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()  # warm-up outside the graph
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for x in xs + xs[:1]:
+        xd.copy_(to_dev(x))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        y_graph = to_host(out)
+        eager = to_host(nv.mlp_forward(0, xd, p_gu, a_gu, p_d, a_d, I, g1_inv=g1i, g2_inv=g2i,
+                                       ws=torch.zeros_like(ws)))
+        torch.cuda.synchronize()
+        r = oracle.mlp_w4a4(x, w["c_gu"], w["s_gu"], sc["a_gu"], w["c_d"], w["s_d"], sc["a_d"],
+                            sc["g1_inv"], sc["g2_inv"])
+        gemm_close(y_graph, r["out"], "graph replay")
+        gemm_close(eager, r["out"], "eager")
+
+
 def test_mlp_prefill_full_size_sampled_rows():
     """Prefill W4A4: M=8192 on the GPU, 64 seeded rows checked by the oracle."""
     nv.set_path(nv.PATH_AUTO)
