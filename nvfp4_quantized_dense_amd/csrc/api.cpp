@@ -120,7 +120,7 @@ bool fits_buffers(const nvfp4::GemmArgs& a, int mode) {
 }
 
 // The kernel a GEMM runs on, from the path and what the operands allow.
-enum Kernel { kFp4Gemv, kValuGemv, kStream, kTiled2, kTiled };
+enum Kernel { kFp4Gemv, kValuGemv, kStream, kTiled2, kTiled16, kTiled };
 
 Kernel select_kernel(int path, int mode, const nvfp4::GemmArgs& a) {
   if (fits_buffers(a, mode)) {
@@ -130,7 +130,7 @@ Kernel select_kernel(int path, int mode, const nvfp4::GemmArgs& a) {
       return kStream;
     }
     if (path == NVFP4_PATH_STREAM) return kStream;
-    if (mode == NVFP4_MODE_W4A4) return kTiled2;
+    return mode == NVFP4_MODE_W4A4 ? kTiled2 : kTiled16;
   }
   // Beyond 2^31-byte operands only the 64-bit-addressed tiled kernel runs.
   return kTiled;
@@ -142,6 +142,7 @@ hipError_t run_gemm(int path, int mode, int epi, const nvfp4::GemmArgs& a, hipSt
     case kValuGemv: return nvfp4::launch_valu_gemv(mode, epi, a, s);
     case kStream: return nvfp4::launch_stream_gemm(mode, epi, a, s);
     case kTiled2: return nvfp4::launch_tiled2_gemm(epi, a, s);
+    case kTiled16: return nvfp4::launch_tiled16_gemm(epi, a, s);
     default: return nvfp4::launch_tiled_gemm(mode, epi, a, s);
   }
 }

@@ -95,6 +95,9 @@ hipError_t launch_tiled_gemm(int mode, int epi, const GemmArgs& a, hipStream_t s
 
 // W4A4 only; packed weight, activation codes and scales each < 2^31 bytes.
 hipError_t launch_tiled2_gemm(int epi, const GemmArgs& a, hipStream_t s);
+// W4A16 only; packed weight and the activation rows (+256 of padding) each
+// < 2^31 bytes.
+hipError_t launch_tiled16_gemm(int epi, const GemmArgs& a, hipStream_t s);
 
 // decode.hip: the W4A4 MLP forward of one token in one launch (gate_up
 // units hand h to the down units, and those their partial sums to the last

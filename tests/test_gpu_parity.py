@@ -173,6 +173,40 @@ def test_gemm_deterministic_and_guarded(path):
     assert np.all(g[:16] == 12345.0) and np.all(g[16 + M * N:] == 12345.0)
 
 
+# -- W4A16 prefill kernel: 128-row x 256-token workgroup tiles ------------------
+#
+# Several token tiles (ragged past 256 and 512), a last row tile that is
+# partly past N (21 row groups = 2 full tiles of 8 and one of 5; for SwiGLU
+# 42 groups = 5 full tiles and one of 2), 5 K tiles (10 staged halves).
+
+@pytest.mark.parametrize("M", [256, 257, 600])
+def test_w4a16_prefill_tiles(M):
+    prev = nv.set_path(PATHS["tiled"])
+    try:
+        rng = np.random.default_rng(700 + M)
+        N, K = 16 * 21, 1280
+        wc, ws = rand_nvfp4(rng, N, K)
+        p = nv.nvfp4_repack_weight(0, to_dev(wc), to_dev(ws))
+        x = synth.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+        alpha = np.float32(0.031)
+        y = nv.nvfp4_gemm(1, to_dev(x), None, p, N, K, scalar(alpha))
+        gemm_close(to_host(y), oracle.gemm_w4a16(x, wc, ws, alpha), f"w4a16 prefill gemm M={M}")
+        yb = nv.nvfp4_gemm(1, to_dev(x), None, p, N, K, scalar(alpha), out_dtype=torch.bfloat16)
+        assert np.array_equal(to_host(yb), synth.f32_to_bf16_bits(to_host(y)))
+        H, I = 768, 336
+        w = mlp_weights(H, I, 2)
+        p_gu = nv.nvfp4_repack_weight(nv.REPACK_SWIGLU, to_dev(w["c_gu"]), to_dev(w["s_gu"]))
+        xh = synth.activations(M, M, H)
+        a_gu = np.float32(w["g_gu"])
+        h32 = nv.gemm_swiglu(1, to_dev(xh), None, p_gu, I, H, scalar(a_gu), h_dtype=torch.float32)
+        h_ref = oracle.swiglu(oracle.gemm_w4a16(xh, w["c_gu"], w["s_gu"], a_gu))
+        gemm_close(to_host(h32), h_ref, f"w4a16 prefill swiglu M={M}")
+        hb = nv.gemm_swiglu(1, to_dev(xh), None, p_gu, I, H, scalar(a_gu), h_dtype=torch.bfloat16)
+        assert np.array_equal(to_host(hb), synth.f32_to_bf16_bits(to_host(h32)))
+    finally:
+        nv.set_path(prev)
+
+
 # -- fused gate_up + SwiGLU (+ NVFP4) ------------------------------------------
 
 @pytest.mark.parametrize("M", [1, 3, 16, 40, 129])
