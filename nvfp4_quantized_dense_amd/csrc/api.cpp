@@ -153,6 +153,8 @@ hipError_t run_gemm(int path, int mode, int epi, const nvfp4::GemmArgs& a, hipSt
 // wave. (At M = 16 on hidden 5120: W4A4 down 21.2 -> 19-20 us, W4A16 40.8 ->
 // 30.7 us. The decode GEMVs measured no gain from it and do not split.)
 constexpr int64_t kSplitTargetWaves = 8192;
+// The W4A16 tiled kernel splits K below this many output tiles (the CU count).
+constexpr int64_t kTiledSplitBelow = 256;
 
 struct SplitPlan {
   int ways = 1;
@@ -163,10 +165,19 @@ struct SplitPlan {
 SplitPlan split_plan(Kernel k, int mode, int64_t M, int64_t N, int64_t K) {
   SplitPlan p;
   if (M <= 0) return p;
-  if (k != kStream) return p;
+  if (k != kStream && k != kTiled16) return p;
   (void)mode;
-  const nvfp4::TileShape ts = nvfp4::stream_shape(M, N);
-  p.ways = nvfp4::splitk_ways(ts.units, K / 256, kSplitTargetWaves / ts.waves, ts.waves);
+  nvfp4::TileShape ts;
+  if (k == kStream) {
+    ts = nvfp4::stream_shape(M, N);
+    p.ways = nvfp4::splitk_ways(ts.units, K / 256, kSplitTargetWaves / ts.waves, ts.waves);
+  } else {
+    // The W4A16 tiled kernel (one 8-wave workgroup per CU) splits only
+    // grids of less than one workgroup per CU: to about 2 per CU, at least
+    // 4 K tiles per split (the down projection at a few hundred tokens).
+    ts = nvfp4::tiled16_shape(M, N);
+    p.ways = ts.units < kTiledSplitBelow ? nvfp4::splitk_ways(ts.units, K / 256, 2 * kTiledSplitBelow, 4) : 1;
+  }
   if (p.ways > 1) {
     p.units = ts.units;
     p.part_bytes = align256((size_t)(ts.units * p.ways * ts.tile_floats) * sizeof(float));
@@ -186,7 +197,7 @@ Kernel mlp_kernel(int path, int mode, int64_t M, int64_t N, int64_t K) {
 }
 
 // The kernels that clear the split-K counters of the GEMM after them.
-bool clears_counters(Kernel k) { return k == kFp4Gemv || k == kValuGemv || k == kStream; }
+bool clears_counters(Kernel k) { return k == kFp4Gemv || k == kValuGemv || k == kStream || k == kTiled16; }
 
 // Shared checks of the GEMM entry points. N is the packed row count.
 int check_gemm(int mode, const void* a, const uint8_t* a_scales, const void* w, int64_t M,
@@ -348,12 +359,12 @@ static size_t decode_bytes(int64_t H, int64_t I) {
   return align256((size_t)nvfp4::decode_record_words(H, I) * sizeof(uint64_t));
 }
 
-// Split-K part: sized for the largest plan over the decode kernels (and, at
-// W4A4 M = 1, for the single-launch decode kernel's records), so the size
-// does not depend on the process-wide path override.
+// Split-K part: sized for the largest plan over the kernels of every path
+// (and, at W4A4 M = 1, for the single-launch decode kernel's records), so
+// the size does not depend on the process-wide path override.
 static size_t mlp_split_bytes(int mode, int64_t M, int64_t H, int64_t I) {
   size_t most = 0;
-  for (int path : {NVFP4_PATH_GEMV, NVFP4_PATH_STREAM}) {
+  for (int path : {NVFP4_PATH_GEMV, NVFP4_PATH_STREAM, NVFP4_PATH_TILED}) {
     const SplitPlan p = split_plan(mlp_kernel(path, mode, M, H, I), mode, M, H, I);
     most = std::max(most, p.part_bytes + p.counter_bytes);
   }

@@ -153,6 +153,11 @@ __device__ __forceinline__ u32x4 bload16(Rsrc r, uint32_t voff) {
 __device__ __forceinline__ u32x4 bload16_dev(Rsrc r, uint32_t voff) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 16);
 }
+// Device-scope (sc1) 16-byte store: completed (vmcnt), visible to
+// device-scope loads of other workgroups on any XCD.
+__device__ __forceinline__ void bstore16_dev(Rsrc r, uint32_t voff, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)voff, 0, 16);
+}
 __device__ __forceinline__ uint32_t bload2(Rsrc r, uint32_t voff) {
   return __builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, 0, 0);
 }

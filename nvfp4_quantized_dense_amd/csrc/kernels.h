@@ -35,12 +35,13 @@ struct GemmArgs {
   const float* g2_inv;       // SwiGLU + NVFP4 output only
   void* out;                 // [M, N] dense, or h [M, I] (dense or codes)
   uint8_t* out_scales;       // h scales [M, I/16]
-  // Split-K (weight-streaming kernel, dense epilogues): ksplit > 1 divides the K
-  // tiles over gridDim.z. Each workgroup stores its partial result tile to
-  // part (tile u, split s at ((u * ksplit + s) * tile_floats)); the last of
-  // the ksplit workgroups of a tile to finish (counted in counters[u], which
-  // must be zero at launch and are left zero) adds the partials in split
-  // order and runs the epilogue.
+  // Split-K (weight-streaming and W4A16 tiled kernels, dense epilogues):
+  // ksplit > 1 divides the K tiles over that many workgroups per output
+  // tile. Each workgroup stores its partial result tile to part (tile u,
+  // split s at ((u * ksplit + s) * tile_floats)); the last of the ksplit
+  // workgroups of a tile to finish (counted in counters[u], which must be
+  // zero at launch and are left zero) adds the partials in split order and
+  // runs the epilogue.
   float* part = nullptr;
   uint32_t* counters = nullptr;
   int ksplit = 1;
@@ -71,6 +72,7 @@ struct TileShape {
   int64_t units, tile_floats, waves;
 };
 TileShape stream_shape(int64_t M, int64_t N);
+TileShape tiled16_shape(int64_t M, int64_t N);
 
 // The number of K splits that brings a dense GEMM of `units` output tiles to
 // about `target` workgroups, each split keeping at least `min_tiles` tiles.

@@ -130,6 +130,46 @@ __device__ __forceinline__ void compute_stage16(f32x4 (&acc)[2][8], const uint8_
   }
 }
 
+// Split-K combine of a workgroup tile (every thread holds 16 f32x4 of it):
+// the partial is stored with device-scope stores in thread-major order,
+// every wave waits for its stores to complete, then one thread counts the
+// workgroup's arrival. The workgroup that arrives last (of ks) adds the ks
+// partials in split order (the result does not depend on arrival order),
+// resets the count and returns true; the others return false.
+__device__ __forceinline__ bool tile_splitk_last(f32x4 (&acc)[2][8], float* part, uint32_t* counters, int ks,
+                                                 int64_t unit, int split, int tid, uint32_t* arrived_lds) {
+  constexpr int kTileFloats = kG16 * 16 * kTG16 * 16;
+  const Rsrc rp = make_rsrc(part + unit * ks * kTileFloats, (uint32_t)(ks * kTileFloats * 4));
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      bstore16_dev(rp, (uint32_t)(((split * 16 + 8 * g + j) * (kNW16 * 64) + tid) * 16),
+                   __builtin_bit_cast(u32x4, acc[g][j]));
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0): this wave's partial is at device scope
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __syncthreads();
+  if (tid == 0)
+    *arrived_lds = __hip_atomic_fetch_add(counters + unit, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (*arrived_lds != (uint32_t)(ks - 1)) return false;
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[g][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int sp = 0; sp < ks; ++sp) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        acc[g][j] += __builtin_bit_cast(
+            f32x4, bload16_dev(rp, (uint32_t)(((sp * 16 + 8 * g + j) * (kNW16 * 64) + tid) * 16)));
+  }
+  if (tid == 0) __hip_atomic_store(counters + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return true;
+}
+
 }  // namespace
 #endif  // __HIP_DEVICE_COMPILE__
 
@@ -138,13 +178,19 @@ __global__ __launch_bounds__(kNW16 * 64, 1) void k_tiled16(GemmArgs args, int64_
                                                            int64_t per_xcd) {
 #if defined(__HIP_DEVICE_COMPILE__)
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage16];
+  __shared__ uint32_t arrived;
+  clear_words(args.zero_ptr, args.zero_n);
   // XCD-aware order: workgroup ids are dealt round-robin to the 8 XCDs, so
   // XCD x takes a contiguous run of output tiles, token-tile-major; its
   // resident workgroups share an activation tile in its L2 while sweeping
-  // weight tiles.
+  // weight tiles. With a K split (dense epilogues), the ks splits of an
+  // output tile are consecutive.
+  const int ks = args.ksplit;
   const int64_t id = blockIdx.x;
-  const int64_t tile = (id & 7) * per_xcd + (id >> 3);
-  if (tile >= n_tiles * m_tiles) return;
+  const int64_t f = (id & 7) * per_xcd + (id >> 3);
+  if (f >= n_tiles * m_tiles * ks) return;
+  const int64_t tile = f / ks;
+  const int split = (int)(f - tile * ks);
   const int64_t m_tile = tile / n_tiles, n_tile = tile % n_tiles;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -162,9 +208,11 @@ __global__ __launch_bounds__(kNW16 * 64, 1) void k_tiled16(GemmArgs args, int64_
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[g][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // K tiles [t0, t1) of this split (all of them without a split).
+  const int64_t per = (T + ks - 1) / ks, t0 = split * per, t1 = min(T, t0 + per);
   const Stage16Src src = stage16_src(args, lane);
-  issue_stage16(src, smem, 0, T, K, rg0, ngroups, tok0, wave, lane);
-  for (int64_t s = 0; s < 2 * T; s += 2) {
+  issue_stage16(src, smem, 2 * t0, T, K, rg0, ngroups, tok0, wave, lane);
+  for (int64_t s = 2 * t0; s < 2 * t1; s += 2) {
     // Two halves per trip (C = 0 in stage buffer 0, C = 1 in buffer 1).
     __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0): this wave's copies of stage s
     __builtin_amdgcn_s_barrier();
@@ -174,10 +222,14 @@ __global__ __launch_bounds__(kNW16 * 64, 1) void k_tiled16(GemmArgs args, int64_
     __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_s_waitcnt(0x3F70);
     __builtin_amdgcn_s_barrier();
-    if (s + 2 < 2 * T) issue_stage16(src, smem, s + 2, T, K, rg0, ngroups, tok0, wave, lane);
+    if (s + 2 < 2 * t1) issue_stage16(src, smem, s + 2, T, K, rg0, ngroups, tok0, wave, lane);
     __builtin_amdgcn_s_setprio(1);
     compute_stage16<1>(acc, smem + kStage16, wave, lane);
     __builtin_amdgcn_s_setprio(0);
+  }
+  if constexpr (!EpiTraits<EPI>::swiglu) {
+    if (ks > 1 && !tile_splitk_last(acc, args.part, args.counters, ks, tile, split, (int)threadIdx.x, &arrived))
+      return;
   }
 
 #pragma unroll
@@ -199,12 +251,18 @@ __global__ __launch_bounds__(kNW16 * 64, 1) void k_tiled16(GemmArgs args, int64_
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
+TileShape tiled16_shape(int64_t M, int64_t N) {
+  const int64_t n_tiles = (N / kTileRows + kG16 - 1) / kG16;
+  const int64_t m_tiles = (M + kTG16 * 16 - 1) / (kTG16 * 16);
+  return TileShape{n_tiles * m_tiles, kG16 * 16 * kTG16 * 16, kNW16};
+}
+
 template <int EPI>
 static hipError_t launch16_e(const GemmArgs& a, hipStream_t s) {
   const int64_t ngroups = a.N / kTileRows;
   const int64_t n_tiles = (ngroups + kG16 - 1) / kG16;
   const int64_t m_tiles = (a.M + kTG16 * 16 - 1) / (kTG16 * 16);
-  const int64_t per_xcd = (n_tiles * m_tiles + 7) / 8;
+  const int64_t per_xcd = (n_tiles * m_tiles * a.ksplit + 7) / 8;
   k_tiled16<EPI><<<(unsigned)(8 * per_xcd), kNW16 * 64, 0, s>>>(a, n_tiles, m_tiles, per_xcd);
   return hipGetLastError();
 }
@@ -214,6 +272,7 @@ static hipError_t launch16_e(const GemmArgs& a, hipStream_t s) {
 // offsets); the caller checks.
 hipError_t launch_tiled16_gemm(int epi, const GemmArgs& a, hipStream_t s) {
   if (a.M == 0) return hipSuccess;
+  if (!splitk_valid(a, epi)) return hipErrorInvalidValue;
   switch (epi) {
     case kOutF32: return launch16_e<kOutF32>(a, s);
     case kOutBF16: return launch16_e<kOutBF16>(a, s);

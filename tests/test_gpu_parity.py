@@ -289,11 +289,13 @@ def test_mlp_small_batch_full_size(M):
 
 
 # -- mlp_forward workspace use: split-K of the down projection (weight-
-# streaming kernel) and the decode GEMV's in-kernel activation quantization
+# streaming kernel; W4A16 tiled kernel) and the decode GEMV's in-kernel
+# activation quantization
 #
 # Hidden 512 leaves 32 output row groups, so the streaming kernel splits
 # the down projection's K (intermediate) over several workgroups: 27 tiles
-# (6912) split unevenly, 32 tiles (8192) evenly. The workspace starts as
+# (6912) split unevenly, 32 tiles (8192) evenly. At 200 tokens the W4A16
+# tiled kernel has 4 output tiles and splits K 7 ways (6912) or 8 (8192). The workspace starts as
 # 0xFF bytes (the counters must be cleared by the gate_up launch) and is
 # reused by a call on another input and then on the first input again,
 # which must give bit-identical output (counts reset, no stale partials).
@@ -301,7 +303,7 @@ def test_mlp_small_batch_full_size(M):
 
 @pytest.mark.parametrize("I", [6912, 8192])
 @pytest.mark.parametrize("kpath,M", [("gemv", 1), ("gemv", 2), ("stream", 3), ("stream", 16),
-                                     ("stream", 40)])
+                                     ("stream", 40), ("tiled", 200)])
 @pytest.mark.parametrize("mode", ["w4a4", "w4a16"])
 def test_mlp_split_k(mode, kpath, M, I):
     H = 512
