@@ -52,6 +52,11 @@ def _lib():
                                     _f32, _f32, _f32p, _u8p, _u8p, _f32p, _f32p, _u8p, _u8p]),
             "orc_mlp_w4a16": (None, [_u16p, _i64, _i64, _i64, _u8p, _u8p, _f32, _u8p, _u8p, _f32,
                                      _f32p, _f32p, _u16p]),
+            "orc_quantize_per_token": (None, [_f32p, _i64, _i64, _u8p, _u8p, _f32p]),
+            "orc_gemm_w4a4_rows": (None, [_u8p, _u8p, _u8p, _u8p, _i64, _i64, _i64, _f32p, _f32p]),
+            "orc_mlp_w4a4_per_token": (None, [_u16p, _i64, _i64, _i64, _u8p, _u8p, _f32, _u8p, _u8p,
+                                              _f32, _f32, _f32p, _u8p, _u8p, _f32p, _f32p, _f32p,
+                                              _u8p, _u8p]),
             "orc_num_threads": (ctypes.c_int, []),
         }
         for name, (res, args) in sig.items():
@@ -134,6 +139,21 @@ def quantize(x: np.ndarray, g_inv):
     return codes, scales
 
 
+def quantize_per_token(x: np.ndarray):
+    """Per-token dynamic quantization of x [M, K] (fp32, or bf16 bits as
+    uint16): returns (codes, scales, g) with g [M] fp32, each row's own
+    global scale."""
+    x = bf16_to_f32(x) if x.dtype == np.uint16 else _c(x, np.float32)
+    x = np.ascontiguousarray(x)
+    M, K = x.shape
+    assert K % 16 == 0
+    codes = np.empty((M, K // 2), np.uint8)
+    scales = np.empty((M, K // 16), np.uint8)
+    g = np.empty(M, np.float32)
+    _lib().orc_quantize_per_token(_p(x, _f32p), M, K, _p(codes, _u8p), _p(scales, _u8p), _p(g, _f32p))
+    return codes, scales, g
+
+
 def dequantize(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     codes = _c(codes, np.uint8)
     scales = _c(scales, np.uint8)
@@ -181,6 +201,44 @@ def swiglu(gu: np.ndarray) -> np.ndarray:
 
 
 # -- MLP -------------------------------------------------------------------
+
+def gemm_w4a4_rows(a_codes, a_scales, w_codes, w_scales, alpha_rows) -> np.ndarray:
+    """W4A4 GEMM whose output row i is scaled by alpha_rows[i]."""
+    a_codes, a_scales = _c(a_codes, np.uint8), _c(a_scales, np.uint8)
+    w_codes, w_scales = _c(w_codes, np.uint8), _c(w_scales, np.uint8)
+    alpha_rows = _c(alpha_rows, np.float32)
+    M, K = a_codes.shape[0], a_codes.shape[1] * 2
+    N = w_codes.shape[0]
+    out = np.empty((M, N), np.float32)
+    _lib().orc_gemm_w4a4_rows(_p(a_codes, _u8p), _p(a_scales, _u8p), _p(w_codes, _u8p),
+                              _p(w_scales, _u8p), M, N, K, _p(alpha_rows, _f32p), _p(out, _f32p))
+    return out
+
+
+def mlp_w4a4_per_token(x_bf16, wgu_codes, wgu_scales, g_wgu, wd_codes, wd_scales, alpha_d,
+                       g2_inv) -> dict:
+    """W4A4 forward with per-token dynamic scales for x; every stage."""
+    x = _c(x_bf16, np.uint16)
+    M, H = x.shape
+    I = wd_codes.shape[1] * 2
+    assert wgu_codes.shape == (2 * I, H // 2) and wd_codes.shape == (H, I // 2)
+    wgu_codes, wgu_scales = _c(wgu_codes, np.uint8), _c(wgu_scales, np.uint8)
+    wd_codes, wd_scales = _c(wd_codes, np.uint8), _c(wd_scales, np.uint8)
+    r = {
+        "out": np.empty((M, H), np.float32),
+        "xq": np.empty((M, H // 2), np.uint8), "xs": np.empty((M, H // 16), np.uint8),
+        "g": np.empty(M, np.float32),
+        "gu": np.empty((M, 2 * I), np.float32), "h": np.empty((M, I), np.float32),
+        "hq": np.empty((M, I // 2), np.uint8), "hs": np.empty((M, I // 16), np.uint8),
+    }
+    _lib().orc_mlp_w4a4_per_token(_p(x, _u16p), M, H, I, _p(wgu_codes, _u8p), _p(wgu_scales, _u8p),
+                                  float(g_wgu), _p(wd_codes, _u8p), _p(wd_scales, _u8p),
+                                  float(alpha_d), float(g2_inv), _p(r["out"], _f32p),
+                                  _p(r["xq"], _u8p), _p(r["xs"], _u8p), _p(r["g"], _f32p),
+                                  _p(r["gu"], _f32p), _p(r["h"], _f32p), _p(r["hq"], _u8p),
+                                  _p(r["hs"], _u8p))
+    return r
+
 
 def mlp_w4a4(x_bf16, wgu_codes, wgu_scales, alpha_gu, wd_codes, wd_scales, alpha_d,
              g1_inv, g2_inv) -> dict:

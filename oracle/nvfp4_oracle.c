@@ -37,6 +37,16 @@
  *    PR #34859 digest, qwen2_moe.py forward), then re-quantization with
  *    `down_proj.input_scale_inv` and the down_proj GEMM on the pre-quantized
  *    (codes, scales) pair (PR #26626 digest, DeepseekV2MLP.forward).
+ *  - Per-token dynamic activation scales (`nvfp4_quantize(hidden_states,
+ *    a1_scale, per_token_activation=True)` returning a per-token scale that
+ *    the GEMM takes as `per_token_scale`, while the second GEMM's input keeps
+ *    its static `a2_scale`: PR #35120 report, key source snippets,
+ *    flashinfer_cutedsl.py activation-quant branch). The pages print only the
+ *    call; the reading used here is the per-tensor calibration applied to
+ *    each token row: g_t = fl(amax_t / 2688), g_inv_t = fl(1 / g_t), the row
+ *    quantized with g_inv_t, and the GEMM output of token t scaled by
+ *    fl(g_t * g_w). A row of zeros has g_t = 0 and quantizes with g_inv = 0
+ *    to zero codes and scales (the pages do not say; this keeps it finite).
  *
  * Arithmetic conventions:
  *  - Encoding steps are binary32 operations with round-to-nearest-even,
@@ -203,6 +213,25 @@ ORC_API void orc_quantize(const float* x, int64_t M, int64_t K, float g_inv,
   }
 }
 
+/* Per-token dynamic quantization of x [M, K]: each row calibrated on its own
+ * amax like orc_global_scale, then quantized like orc_quantize with its own
+ * g_inv; g_rows[i] receives the row's g. */
+ORC_API void orc_quantize_per_token(const float* x, int64_t M, int64_t K, uint8_t* codes,
+                                    uint8_t* scales, float* g_rows) {
+  for (int64_t i = 0; i < M; ++i) {
+    const float* row = x + i * K;
+    float amax = 0.0f;
+    for (int64_t k = 0; k < K; ++k) {
+      float a = fabsf(row[k]);
+      if (a > amax) amax = a;
+    }
+    float g = amax / 2688.0f;
+    float g_inv = (g != 0.0f) ? 1.0f / g : 0.0f;
+    g_rows[i] = g;
+    orc_quantize(row, 1, K, g_inv, codes + i * (K / 2), scales + i * (K / 16));
+  }
+}
+
 /* Element (row, k) of an NVFP4 matrix without its global scale: q * s. */
 static double nvfp4_elem(const uint8_t* codes, const uint8_t* scales, int64_t K,
                          int64_t row, int64_t k) {
@@ -320,6 +349,54 @@ ORC_API void orc_swiglu(const float* gu, int64_t M, int64_t I, float* h) {
       double silu = g / (1.0 + exp(-g));
       h[i * I + j] = (float)(silu * u);
     }
+}
+
+/* W4A4 GEMM with a per-row output scale: row i of the output is the W4A4
+ * GEMM of row i of A with alpha_rows[i] (block-factored as orc_gemm_w4a4). */
+ORC_API void orc_gemm_w4a4_rows(const uint8_t* a_codes, const uint8_t* a_scales,
+                                const uint8_t* w_codes, const uint8_t* w_scales, int64_t M,
+                                int64_t N, int64_t K, const float* alpha_rows, float* out) {
+  for (int64_t i = 0; i < M; ++i)
+    orc_gemm_w4a4(a_codes + i * (K / 2), a_scales + i * (K / 16), w_codes, w_scales, 1, N, K,
+                  alpha_rows[i], out + i * N);
+}
+
+/* W4A4 MLP forward with per-token dynamic scales for x (h keeps its static
+ * g2_inv):
+ *   x  -> NVFP4 per token, g_t                     (orc_quantize_per_token)
+ *   gu = fl32(fl(g_t * g_wgu) * x_t @ Wgu^T)       per token row t
+ *   h  = SwiGLU(gu); hq = NVFP4(h) with g2_inv; out = fl32(alpha_d * hq @ Wd^T)
+ * Optional stage outputs (NULL to skip): xq/xs, g_rows, gu, h, hq/hs. */
+ORC_API void orc_mlp_w4a4_per_token(const uint16_t* x, int64_t M, int64_t H, int64_t I,
+                                    const uint8_t* wgu_codes, const uint8_t* wgu_scales, float g_wgu,
+                                    const uint8_t* wd_codes, const uint8_t* wd_scales, float alpha_d,
+                                    float g2_inv, float* out, uint8_t* xq_out, uint8_t* xs_out,
+                                    float* g_out, float* gu_out, float* h_out, uint8_t* hq_out,
+                                    uint8_t* hs_out) {
+  float* xf = (float*)malloc(sizeof(float) * (size_t)(M * H));
+  uint8_t* xq = (uint8_t*)malloc((size_t)(M * H / 2));
+  uint8_t* xs = (uint8_t*)malloc((size_t)(M * H / 16));
+  float* g = (float*)malloc(sizeof(float) * (size_t)M);
+  float* a_rows = (float*)malloc(sizeof(float) * (size_t)M);
+  float* gu = (float*)malloc(sizeof(float) * (size_t)(M * 2 * I));
+  float* h = (float*)malloc(sizeof(float) * (size_t)(M * I));
+  uint8_t* hq = (uint8_t*)malloc((size_t)(M * I / 2));
+  uint8_t* hs = (uint8_t*)malloc((size_t)(M * I / 16));
+  for (int64_t t = 0; t < M * H; ++t) xf[t] = orc_bf16_to_f32(x[t]);
+  orc_quantize_per_token(xf, M, H, xq, xs, g);
+  for (int64_t i = 0; i < M; ++i) a_rows[i] = orc_alpha(g[i], g_wgu);
+  orc_gemm_w4a4_rows(xq, xs, wgu_codes, wgu_scales, M, 2 * I, H, a_rows, gu);
+  orc_swiglu(gu, M, I, h);
+  orc_quantize(h, M, I, g2_inv, hq, hs);
+  orc_gemm_w4a4(hq, hs, wd_codes, wd_scales, M, H, I, alpha_d, out);
+  if (xq_out) memcpy(xq_out, xq, (size_t)(M * H / 2));
+  if (xs_out) memcpy(xs_out, xs, (size_t)(M * H / 16));
+  if (g_out) memcpy(g_out, g, sizeof(float) * (size_t)M);
+  if (gu_out) memcpy(gu_out, gu, sizeof(float) * (size_t)(M * 2 * I));
+  if (h_out) memcpy(h_out, h, sizeof(float) * (size_t)(M * I));
+  if (hq_out) memcpy(hq_out, hq, (size_t)(M * I / 2));
+  if (hs_out) memcpy(hs_out, hs, (size_t)(M * I / 16));
+  free(xf); free(xq); free(xs); free(g); free(a_rows); free(gu); free(h); free(hq); free(hs);
 }
 
 /* W4A4 MLP forward, x bf16 [M, H]:

@@ -377,3 +377,85 @@ def test_mlp_uses_gate_as_first_half(orc):
     g, u = gu[:, :512].astype(np.float64), gu[:, 512:].astype(np.float64)
     assert np.allclose(h, g / (1 + np.exp(-g)) * u, rtol=1e-6, atol=1e-30)
     assert not np.allclose(h, u / (1 + np.exp(-u)) * g, rtol=1e-3)
+
+
+# -- per-token dynamic activation scales ------------------------------------
+
+@pytest.mark.parametrize("v", [3.0, -0.015625, 1.0e-3, -1234.5, 2688.0])
+def test_per_token_single_element_row(orc, v):
+    """A row whose only nonzero is v: g = fl(|v| / 2688); v's block takes the
+    largest scale (E4M3 448 = 0x7E) and v the largest code (6, signed);
+    every other block is zero."""
+    K = 64
+    x = np.zeros((1, K), np.float32)
+    x[0, 21] = v
+    c, s, g = orc.quantize_per_token(x)
+    assert g[0] == np.float32(np.float32(abs(v)) / np.float32(2688.0))
+    assert s[0, 1] == 0x7E and ref_e4m3(s[0, 1]) == 448.0
+    n = nibbles(c)[0]
+    assert n[21] == (0xF if v < 0 else 0x7)
+    assert np.all(np.delete(n, 21) & 7 == 0) and np.all(np.delete(s[0], 1) == 0)
+    # dequantized back: q * s * g reproduces v to the E2M1/E4M3 rounding
+    assert abs(6 * 448 * float(g[0]) - abs(v)) <= 1e-6 * abs(v)
+
+
+def test_per_token_power_of_two_rows(orc):
+    """Rows that are one row times powers of two quantize to the same codes
+    and scales, with g scaled by exactly that power (amax, the division by
+    2688 and g_inv all scale exactly)."""
+    base = np.random.default_rng(11).standard_normal(256).astype(np.float32)
+    ks = [-3, -1, 0, 2, 5]
+    x = np.stack([base * np.float32(2.0 ** k) for k in ks])
+    c, s, g = orc.quantize_per_token(x)
+    for i in range(1, len(ks)):
+        assert np.array_equal(c[i], c[0]) and np.array_equal(s[i], s[0])
+        assert g[i] == np.float32(g[0] * np.float32(2.0 ** (ks[i] - ks[0])))
+
+
+def test_per_token_zero_row_and_mixed_magnitudes(orc):
+    """A zero row gets g = 0, zero codes and scales; the other rows are
+    quantized as each alone with the per-tensor calibration (rows of very
+    different magnitude share nothing)."""
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((4, 128)).astype(np.float32)
+    x[1] = 0.0
+    x[2] *= np.float32(1e-4)
+    x[3] *= np.float32(300.0)
+    c, s, g = orc.quantize_per_token(x)
+    assert g[1] == 0 and not c[1].any() and not s[1].any()
+    for i in (0, 2, 3):
+        gi, gi_inv = orc.global_scale(x[i:i + 1])
+        assert g[i] == gi
+        ci, si = orc.quantize(x[i:i + 1], gi_inv)
+        assert np.array_equal(c[i:i + 1], ci) and np.array_equal(s[i:i + 1], si)
+
+
+def test_gemm_rows_scale_each_row(orc):
+    """Per-row alphas scale output rows exactly where they differ by powers of
+    two, and each row equals numpy's float64 matmul of the decoded operands
+    times its own alpha."""
+    rng = np.random.default_rng(13)
+    M, N, K = 3, 20, 256
+    wc, ws = rand_nvfp4(rng, N, K)
+    ac1, as1 = rand_nvfp4(rng, 1, K)
+    ac, as_ = np.repeat(ac1, M, axis=0), np.repeat(as1, M, axis=0)
+    a = np.array([0.0625, 0.125, 0.5], np.float32)
+    y = orc.gemm_w4a4_rows(ac, as_, wc, ws, a)
+    assert np.array_equal(y[1], 2 * y[0]) and np.array_equal(y[2], 8 * y[0])
+    ref = ref_dequant(ac, as_) @ ref_dequant(wc, ws).T
+    assert np.allclose(y, (ref * a[:, None].astype(np.float64)).astype(np.float32), rtol=1e-6, atol=0)
+
+
+def test_mlp_per_token_single_row_equals_static(orc):
+    """On one token the per-token forward is the static one with that token's
+    own calibration (g1 = its g, alpha_gu = fl(g1 * g_wgu)); on several tokens
+    each row equals its own single-token forward."""
+    x, wgu, wd, (ggu, wguc, wgus), (gd, wdc, wds), _ = _tiny_mlp_inputs(orc, M=3)
+    a_d, g2_inv = np.float32(0.002), np.float32(50.0)
+    r = orc.mlp_w4a4_per_token(x, wguc, wgus, ggu, wdc, wds, a_d, g2_inv)
+    for t in range(3):
+        g1, g1_inv = orc.global_scale(x[t:t + 1])
+        assert r["g"][t] == g1
+        s = orc.mlp_w4a4(x[t:t + 1], wguc, wgus, orc.alpha(g1, ggu), wdc, wds, a_d, g1_inv, g2_inv)
+        assert np.array_equal(r["out"][t:t + 1], s["out"])
+        assert np.array_equal(r["xq"][t:t + 1], s["xq"]) and np.array_equal(r["hq"][t:t + 1], s["hq"])
