@@ -115,7 +115,7 @@ def prepare_weights(H, I, dev, copies):
     return out[0], out[1], gs[0], gs[1]
 
 
-def cpu_baseline(M, H, I, mode, outliers, per_step_bytes, per_step_flops, budget_s, use_flops):
+def cpu_baseline(M, H, I, mode, outliers, per_step_bytes, per_step_flops, budget_s, use_flops, dyn=False):
     """The CPU oracle on a bounded sample of the workload's steps."""
     import oracle
     wgu = synth.weights(0, 2 * I, H, synth.TENSOR_W_GATE_UP)
@@ -138,7 +138,9 @@ def cpu_baseline(M, H, I, mode, outliers, per_step_bytes, per_step_flops, budget
     t0 = time.perf_counter()
     while True:
         x = synth.activations(n, M, H, outliers=outliers)[:rows]
-        if mode == "w4a4":
+        if dyn:
+            oracle.mlp_w4a4_per_token(x, c_gu, s_gu, g_gu, c_d, s_d, a_d, g2_inv)
+        elif mode == "w4a4":
             oracle.mlp_w4a4(x, c_gu, s_gu, a_gu, c_d, s_d, a_d, g1_inv, g2_inv)
         else:
             oracle.mlp_w4a16(x, c_gu, s_gu, g_gu, c_d, s_d, g_d)
@@ -168,6 +170,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--path", type=int, default=0, help="kernel class override (0 = auto)")
+    ap.add_argument("--per-token", action="store_true",
+                    help="W4A4 with per-token dynamic activation scales for x")
     ap.add_argument("--sweep", default=None,
                     help="comma-separated token counts: one JSON line per M on the same weights")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -217,8 +221,9 @@ def run_one(args, dev, M, H, I, mode, outliers, n_seeds, steps, warmup, copies, 
 
     # Static activation scales, calibrated on the seed-0 input: g1 from x,
     # g2 from the fused kernel's own fp32 h for that x.
-    ws = torch.zeros(max(1, nv.mlp_workspace_bytes(0 if mode == "w4a4" else 1, M, H, I)),
-                     dtype=torch.uint8, device=dev)
+    dyn = mode == "w4a4" and args.per_token
+    qmode = nv.MODE_W4A4_DYN if dyn else (nv.MODE_W4A4 if mode == "w4a4" else nv.MODE_W4A16)
+    ws = torch.zeros(max(1, nv.mlp_workspace_bytes(qmode, M, H, I)), dtype=torch.uint8, device=dev)
     out = torch.empty((M, H), dtype=out_dtype, device=dev)
     if mode == "w4a4":
         g1, g1_inv = nv.nvfp4_calibrate(xs[0])
@@ -232,6 +237,10 @@ def run_one(args, dev, M, H, I, mode, outliers, n_seeds, steps, warmup, copies, 
         xsc = torch.empty((M, H // 16), dtype=torch.uint8, device=dev)
         hq = torch.empty((M, I // 2), dtype=torch.uint8, device=dev)
         hsc = torch.empty((M, I // 16), dtype=torch.uint8, device=dev)
+        if dyn:
+            # x scaled per token: gate_up takes the weight's g alone (h keeps
+            # the static g2 calibrated above) and the fused leg the token g's
+            xq, xsc, row_g = nv.nvfp4_quantize_per_token(xs[0])
     else:
         a_gu, a_d = g_gu, g_d
         hb = torch.empty((M, I), dtype=torch.bfloat16, device=dev)
@@ -241,7 +250,10 @@ def run_one(args, dev, M, H, I, mode, outliers, n_seeds, steps, warmup, copies, 
 
     def fused(i):
         r = i % copies
-        if mode == "w4a4":
+        if dyn:
+            nv.gemm_swiglu_nvfp4_quant_rowscale(xq, xsc, row_g, p_gu[r], I, H, g_gu, g2_inv, hq, hsc,
+                                                stream=stream)
+        elif mode == "w4a4":
             nv.gemm_swiglu_nvfp4_quant(xq, xsc, p_gu[r], I, H, a_gu, g2_inv, hq, hsc, stream=stream)
         else:
             nv.gemm_swiglu(1, xs[i % n_seeds], None, p_gu[r], I, H, a_gu, h=hb, stream=stream)
@@ -252,7 +264,10 @@ def run_one(args, dev, M, H, I, mode, outliers, n_seeds, steps, warmup, copies, 
     def step(i):
         x = xs[i % n_seeds]
         r = i % copies
-        if mode == "w4a4":
+        if dyn:
+            nv.mlp_forward(nv.MODE_W4A4_DYN, x, p_gu[r], g_gu, p_d[r], a_d, I, g2_inv=g2_inv,
+                           ws=ws, out=out, stream=stream)
+        elif mode == "w4a4":
             nv.mlp_forward(0, x, p_gu[r], a_gu, p_d[r], a_d, I, g1_inv=g1_inv, g2_inv=g2_inv,
                            ws=ws, out=out, stream=stream)
         else:
@@ -274,7 +289,7 @@ def run_one(args, dev, M, H, I, mode, outliers, n_seeds, steps, warmup, copies, 
     # automatic path the whole forward is one launch (the single-launch
     # decode kernel), so that launch, with the whole forward's bytes;
     # otherwise the fused gate_up launch alone.
-    single = mode == "w4a4" and M == 1 and args.path == 0
+    single = mode == "w4a4" and not dyn and M == 1 and args.path == 0
     leg = step if single else fused
     leg_bytes = alg["total"] if single else alg["fused"]
     leg_flops = alg["flops"] if single else alg["flops_fused"]
@@ -300,11 +315,12 @@ def run_one(args, dev, M, H, I, mode, outliers, n_seeds, steps, warmup, copies, 
         achieved = leg_bytes / (fused_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "traffic": None}
-    roof["traffic"] = recorded_traffic(args.workload, M)
+    roof["traffic"] = None if dyn else recorded_traffic(args.workload, M)
     if single:
         roof["kernel"] = "mlp_forward single-launch decode (k_decode_mlp)"
     else:
-        roof["kernel"] = "gemm_swiglu_nvfp4_quant" if mode == "w4a4" else "gemm_swiglu(w4a16, bf16 h)"
+        roof["kernel"] = ("gemm_swiglu_nvfp4_quant_rowscale" if dyn else
+                          "gemm_swiglu_nvfp4_quant" if mode == "w4a4" else "gemm_swiglu(w4a16, bf16 h)")
     roof["kernel_us"] = fused_ms * 1e3
     roof["launches_timed"] = n_k
     roof["algorithmic_bytes"] = leg_bytes
@@ -313,7 +329,8 @@ def run_one(args, dev, M, H, I, mode, outliers, n_seeds, steps, warmup, copies, 
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
-        cpu = cpu_baseline(M, H, I, mode, outliers, alg["total"], alg["flops"], args.cpu_budget, prefill)
+        cpu = cpu_baseline(M, H, I, mode, outliers, alg["total"], alg["flops"], args.cpu_budget, prefill,
+                           dyn)
 
     res = {
         "metric": "NVFP4 MLP TFLOPS + GB/s (% roofline), decode M=1..16 and prefill M=8192",
@@ -328,8 +345,8 @@ def run_one(args, dev, M, H, I, mode, outliers, n_seeds, steps, warmup, copies, 
         "vs_baseline": None,
         "dtype": "f16" if mode == "w4a4" else "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{args.workload} M={M} H={H} I={I}", "M": M, "hidden": H,
-                   "intermediate": I, "mode": mode, "seeds": n_seeds, "weight_copies": copies,
+        "config": {"workload": f"{args.workload}{' per-token' if dyn else ''} M={M} H={H} I={I}", "M": M,
+                   "hidden": H, "intermediate": I, "mode": "w4a4_per_token" if dyn else mode, "seeds": n_seeds, "weight_copies": copies,
                    "out_dtype": "bf16", "tflops": alg["flops"] / (ms_per_step * 1e-3) / 1e12,
                    "gbs": alg["total"] / (ms_per_step * 1e-3) / 1e9},
         "roofline": roof,

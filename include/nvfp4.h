@@ -65,6 +65,7 @@ extern "C" {
  * PR #35120 report, implementation breakdown item 1). */
 #define NVFP4_MODE_W4A4 0  /* NVFP4 activations x NVFP4 weights */
 #define NVFP4_MODE_W4A16 1 /* bf16 activations x NVFP4 weights */
+#define NVFP4_MODE_W4A4_DYN 2 /* W4A4 with per-token dynamic scales for x (mlp_forward only) */
 
 /* Repack kinds. */
 #define NVFP4_REPACK_PLAIN 0  /* any [R, C] weight, e.g. down_proj */
@@ -104,6 +105,19 @@ int nvfp4_calibrate(const void* x, int x_dtype, int64_t n, float* g, float* g_in
  */
 int nvfp4_quantize(const void* x, int x_dtype, int64_t M, int64_t K, const float* g_inv,
                    uint8_t* codes, uint8_t* scales, void* stream);
+
+/*
+ * Per-token dynamic quantization (the pages' `nvfp4_quantize(hidden_states,
+ * a1_scale, per_token_activation=True)`, PR #35120 report, key source
+ * snippets, flashinfer_cutedsl.py; the pages print only the call): every row
+ * t of x is calibrated on its own amax, g_t = fl(amax_t / 2688),
+ * g_inv_t = fl(1 / g_t) (0 for an all-zero row, which quantizes to zeros),
+ * and quantized with g_inv_t exactly as nvfp4_quantize does.
+ * x [M, K] of x_dtype (finite), K % 16 == 0; codes [M, K/2], scales
+ * [M, K/16] and row_g [M] (fp32 g_t, the GEMM's per-token factor) out.
+ */
+int nvfp4_quantize_per_token(const void* x, int x_dtype, int64_t M, int64_t K, uint8_t* codes,
+                             uint8_t* scales, float* row_g, void* stream);
 
 /*
  * Bytes of the packed weight for an [R, C] NVFP4 matrix: R * C * 9 / 16
@@ -169,6 +183,22 @@ int gemm_swiglu_nvfp4_quant(const uint8_t* a_codes, const uint8_t* a_scales,
                             uint8_t* h_scales, void* stream);
 
 /*
+ * W4A4 GEMM and fused gate_up + SwiGLU + NVFP4 re-quantization on
+ * activations with per-token dynamic scales (row_g from
+ * nvfp4_quantize_per_token, the pages' `per_token_scale` argument of the
+ * GEMM): token t's output scale is fl(g_w * row_g[t]), g_w (device fp32) the
+ * weight's global scale; otherwise as nvfp4_gemm (mode W4A4) and
+ * gemm_swiglu_nvfp4_quant.
+ */
+int nvfp4_gemm_rowscale(const uint8_t* a_codes, const uint8_t* a_scales, const float* row_g,
+                        const void* w_packed, int64_t M, int64_t N, int64_t K, const float* g_w,
+                        void* out, int out_dtype, void* stream);
+int gemm_swiglu_nvfp4_quant_rowscale(const uint8_t* a_codes, const uint8_t* a_scales,
+                                     const float* row_g, const void* w_gu_packed, int64_t M,
+                                     int64_t I, int64_t K, const float* g_w, const float* g2_inv,
+                                     uint8_t* h_codes, uint8_t* h_scales, void* stream);
+
+/*
  * gate_up GEMM + SiLU(gate) * up to a dense h [M, I] of h_dtype (bf16: the
  * W4A16 chain's activation; f32: calibration of g2 and checks of the
  * re-quantization). mode and a/a_scales as in nvfp4_gemm. Uses the same
@@ -178,9 +208,10 @@ int gemm_swiglu(int mode, const void* a, const uint8_t* a_scales, const void* w_
                 int64_t M, int64_t I, int64_t K, const float* alpha, void* h, int h_dtype,
                 void* stream);
 
-/* Workspace bytes mlp_forward needs: W4A4 holds x and h in NVFP4; W4A16
- * holds h in bf16. Each region starts 256-byte aligned. At W4A4 M = 1 it
- * also holds the single-launch decode kernel's records (see mlp_forward). */
+/* Workspace bytes mlp_forward needs: W4A4 holds x and h in NVFP4 (W4A4_DYN
+ * also x's per-token scales); W4A16 holds h in bf16. Each region starts
+ * 256-byte aligned. At W4A4 M = 1 it also holds the single-launch decode
+ * kernel's records (see mlp_forward). */
 size_t mlp_workspace_bytes(int mode, int64_t M, int64_t H, int64_t I);
 
 /*
@@ -189,6 +220,9 @@ size_t mlp_workspace_bytes(int mode, int64_t M, int64_t H, int64_t I);
  *          g2_inv) -> nvfp4_gemm(alpha_d) -> out
  *   W4A16: x -> gemm_swiglu(bf16 h, alpha_gu = g_wgu) -> nvfp4_gemm(W4A16,
  *          alpha_d = g_wd) -> out; g1_inv and g2_inv must be NULL.
+ *   W4A4_DYN: x -> nvfp4_quantize_per_token -> gemm_swiglu_nvfp4_quant_rowscale(
+ *          g_w = alpha_gu = g_wgu, g2_inv) -> nvfp4_gemm(alpha_d) -> out;
+ *          g1_inv must be NULL (h keeps its static g2_inv, as on the pages).
  * x bf16 [M, H]; w_gu_packed: SWIGLU packed [2I, H]; w_d_packed: PLAIN packed
  * [H, I]; H % 256 == 0, I % 256 == 0. out [M, H] of out_dtype.
  * W4A4 at M = 1 under NVFP4_PATH_AUTO (and outside stream capture) runs as

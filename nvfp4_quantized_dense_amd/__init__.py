@@ -19,7 +19,7 @@ NVFP4_ERR_INVALID_ARG = -1
 NVFP4_ERR_UNSUPPORTED = -2
 NVFP4_ERR_HIP = -3
 DTYPE_BF16, DTYPE_F32 = 0, 1
-MODE_W4A4, MODE_W4A16 = 0, 1
+MODE_W4A4, MODE_W4A16, MODE_W4A4_DYN = 0, 1, 2
 REPACK_PLAIN, REPACK_SWIGLU = 0, 1
 PATH_AUTO, PATH_GEMV, PATH_STREAM, PATH_TILED = 0, 1, 2, 3
 
@@ -34,11 +34,15 @@ SIGNATURES = {
     "nvfp4_set_path": (_int, [_int]),
     "nvfp4_calibrate": (_int, [_vp, _int, _i64, _vp, _vp, _vp]),
     "nvfp4_quantize": (_int, [_vp, _int, _i64, _i64, _vp, _vp, _vp, _vp]),
+    "nvfp4_quantize_per_token": (_int, [_vp, _int, _i64, _i64, _vp, _vp, _vp, _vp]),
     "nvfp4_packed_bytes": (_sz, [_int, _i64, _i64]),
     "nvfp4_repack_weight": (_int, [_int, _vp, _vp, _i64, _i64, _vp, _vp]),
     "nvfp4_unpack_weight": (_int, [_int, _vp, _i64, _i64, _vp, _vp, _vp]),
     "nvfp4_gemm": (_int, [_int, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _int, _vp]),
     "gemm_swiglu_nvfp4_quant": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp]),
+    "nvfp4_gemm_rowscale": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _int, _vp]),
+    "gemm_swiglu_nvfp4_quant_rowscale": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp,
+                                                _vp, _vp]),
     "gemm_swiglu": (_int, [_int, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _int, _vp]),
     "mlp_workspace_bytes": (_sz, [_int, _i64, _i64, _i64]),
     "mlp_forward": (_int, [_int, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
@@ -134,6 +138,23 @@ def nvfp4_quantize(x, g_inv, codes=None, scales=None, stream=None):
     return codes, scales
 
 
+def nvfp4_quantize_per_token(x, codes=None, scales=None, row_g=None, stream=None):
+    """x [M, K] bf16/f32 -> (codes [M, K/2], scales [M, K/16], row_g fp32 [M]), each row
+    quantized with its own global scale row_g[t] = amax(|x[t]|)/2688."""
+    _dense(x, "x")
+    M, K = x.shape
+    if codes is None:
+        codes = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((M, K // 16), dtype=torch.uint8, device=x.device)
+    if row_g is None:
+        row_g = torch.empty(M, dtype=torch.float32, device=x.device)
+    _check("nvfp4_quantize_per_token",
+           lib().nvfp4_quantize_per_token(_ptr(x), _dtype_code(x.dtype), M, K, _ptr(codes), _ptr(scales),
+                                          _ptr(row_g), _stream(stream)))
+    return codes, scales, row_g
+
+
 def nvfp4_packed_bytes(kind, R, C) -> int:
     return int(lib().nvfp4_packed_bytes(int(kind), int(R), int(C)))
 
@@ -184,6 +205,35 @@ def gemm_swiglu_nvfp4_quant(a_codes, a_scales, w_gu_packed, I, K, alpha, g2_inv,
            lib().gemm_swiglu_nvfp4_quant(_ptr(a_codes), _ptr(a_scales), _ptr(w_gu_packed), M, I, K,
                                          _ptr(alpha), _ptr(g2_inv), _ptr(h_codes), _ptr(h_scales),
                                          _stream(stream)))
+    return h_codes, h_scales
+
+
+def nvfp4_gemm_rowscale(a_codes, a_scales, row_g, w_packed, N, K, g_w, out=None,
+                        out_dtype=torch.float32, stream=None):
+    """W4A4 out [M, N] = g_w * row_g[t] * (A @ W^T) with per-token activation scales."""
+    _dense(a_codes, "a_codes")
+    M = a_codes.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a_codes.device)
+    _check("nvfp4_gemm_rowscale",
+           lib().nvfp4_gemm_rowscale(_ptr(a_codes), _ptr(a_scales), _ptr(row_g), _ptr(w_packed), M, N, K,
+                                     _ptr(g_w), _ptr(out), _dtype_code(out.dtype), _stream(stream)))
+    return out
+
+
+def gemm_swiglu_nvfp4_quant_rowscale(a_codes, a_scales, row_g, w_gu_packed, I, K, g_w, g2_inv,
+                                     h_codes=None, h_scales=None, stream=None):
+    """gemm_swiglu_nvfp4_quant with per-token activation scales row_g."""
+    _dense(a_codes, "a_codes")
+    M = a_codes.shape[0]
+    if h_codes is None:
+        h_codes = torch.empty((M, I // 2), dtype=torch.uint8, device=a_codes.device)
+    if h_scales is None:
+        h_scales = torch.empty((M, I // 16), dtype=torch.uint8, device=a_codes.device)
+    _check("gemm_swiglu_nvfp4_quant_rowscale",
+           lib().gemm_swiglu_nvfp4_quant_rowscale(_ptr(a_codes), _ptr(a_scales), _ptr(row_g), _ptr(w_gu_packed),
+                                                  M, I, K, _ptr(g_w), _ptr(g2_inv), _ptr(h_codes),
+                                                  _ptr(h_scales), _stream(stream)))
     return h_codes, h_scales
 
 

@@ -265,6 +265,24 @@ int nvfp4_quantize(const void* x, int x_dtype, int64_t M, int64_t K, const float
                     "quantize launch");
 }
 
+int nvfp4_quantize_per_token(const void* x, int x_dtype, int64_t M, int64_t K, uint8_t* codes,
+                             uint8_t* scales, float* row_g, void* stream) {
+  if (x_dtype != NVFP4_DTYPE_BF16 && x_dtype != NVFP4_DTYPE_F32)
+    return fail(NVFP4_ERR_INVALID_ARG, "x_dtype must be BF16 or F32");
+  if (!dim_ok(M) || K < 0 || K > (int64_t(1) << 30) || K % 16 != 0)
+    return fail(NVFP4_ERR_INVALID_ARG, "need 0 <= M and K a multiple of 16 (M=%lld K=%lld)",
+                (long long)M, (long long)K);
+  if (M * K == 0) { g_err[0] = '\0'; return NVFP4_OK; }
+  if (!x || !codes || !scales || !row_g) return fail(NVFP4_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(x) || !aligned16(codes) || reinterpret_cast<uintptr_t>(row_g) % 4)
+    return fail(NVFP4_ERR_INVALID_ARG, "x and codes must be 16-byte aligned, row_g 4-byte aligned");
+  int st = check_device();
+  if (st) return st;
+  return hip_status(nvfp4::launch_quantize_per_token(x, x_dtype == NVFP4_DTYPE_F32, M, K, codes, scales, row_g,
+                                                     as_stream(stream)),
+                    "quantize_per_token launch");
+}
+
 size_t nvfp4_packed_bytes(int kind, int64_t R, int64_t C) {
   if (kind != NVFP4_REPACK_PLAIN && kind != NVFP4_REPACK_SWIGLU) return 0;
   if (R <= 0 || C <= 0 || R % 16 != 0 || C % 256 != 0 || R > kMaxDim || C > kMaxDim) return 0;
@@ -331,6 +349,44 @@ int gemm_swiglu_nvfp4_quant(const uint8_t* a_codes, const uint8_t* a_scales, con
                     "gemm_swiglu_nvfp4_quant launch");
 }
 
+int nvfp4_gemm_rowscale(const uint8_t* a_codes, const uint8_t* a_scales, const float* row_g,
+                        const void* w_packed, int64_t M, int64_t N, int64_t K, const float* g_w,
+                        void* out, int out_dtype, void* stream) {
+  int st = check_gemm(NVFP4_MODE_W4A4, a_codes, a_scales, w_packed, M, N, K, g_w, out);
+  if (st) return st;
+  if (out_dtype != NVFP4_DTYPE_F32 && out_dtype != NVFP4_DTYPE_BF16)
+    return fail(NVFP4_ERR_INVALID_ARG, "out_dtype must be F32 or BF16");
+  if (M > 0 && !row_g) return fail(NVFP4_ERR_INVALID_ARG, "null pointer argument");
+  if (M == 0) { g_err[0] = '\0'; return NVFP4_OK; }
+  st = check_device();
+  if (st) return st;
+  nvfp4::GemmArgs ga{a_codes, a_scales, static_cast<const uint8_t*>(w_packed), M, N, K, g_w, nullptr, out, nullptr};
+  ga.row_scale = row_g;
+  const int epi = out_dtype == NVFP4_DTYPE_F32 ? nvfp4::kOutF32 : nvfp4::kOutBF16;
+  return hip_status(run_gemm(choose_path(NVFP4_MODE_W4A4, M), NVFP4_MODE_W4A4, epi, ga, as_stream(stream)),
+                    "gemm_rowscale launch");
+}
+
+int gemm_swiglu_nvfp4_quant_rowscale(const uint8_t* a_codes, const uint8_t* a_scales, const float* row_g,
+                                     const void* w_gu_packed, int64_t M, int64_t I, int64_t K,
+                                     const float* g_w, const float* g2_inv, uint8_t* h_codes,
+                                     uint8_t* h_scales, void* stream) {
+  if (!dim_ok(I) || I <= 0 || I % 16 != 0)
+    return fail(NVFP4_ERR_INVALID_ARG, "I=%lld must be a positive multiple of 16", (long long)I);
+  int st = check_gemm(NVFP4_MODE_W4A4, a_codes, a_scales, w_gu_packed, M, 2 * I, K, g_w, h_codes);
+  if (st) return st;
+  if (M > 0 && (!g2_inv || !h_scales || !row_g)) return fail(NVFP4_ERR_INVALID_ARG, "null pointer argument");
+  if (M == 0) { g_err[0] = '\0'; return NVFP4_OK; }
+  st = check_device();
+  if (st) return st;
+  nvfp4::GemmArgs ga{a_codes, a_scales, static_cast<const uint8_t*>(w_gu_packed), M, 2 * I, K, g_w, g2_inv,
+                     h_codes, h_scales};
+  ga.row_scale = row_g;
+  return hip_status(run_gemm(choose_path(NVFP4_MODE_W4A4, M), NVFP4_MODE_W4A4, nvfp4::kSwigluNvfp4, ga,
+                             as_stream(stream)),
+                    "gemm_swiglu_nvfp4_quant_rowscale launch");
+}
+
 int gemm_swiglu(int mode, const void* a, const uint8_t* a_scales, const void* w_gu_packed, int64_t M,
                 int64_t I, int64_t K, const float* alpha, void* h, int h_dtype, void* stream) {
   if (!dim_ok(I) || I <= 0 || I % 16 != 0)
@@ -347,10 +403,12 @@ int gemm_swiglu(int mode, const void* a, const uint8_t* a_scales, const void* w_
   return hip_status(run_gemm(choose_path(mode, M), mode, epi, ga, as_stream(stream)), "gemm_swiglu launch");
 }
 
-// Activation part of the workspace: W4A4 x and h as NVFP4, W4A16 h in bf16.
+// Activation part of the workspace: W4A4 x and h as NVFP4 (W4A4_DYN then
+// x's per-token g), W4A16 h in bf16.
 static size_t mlp_act_bytes(int mode, size_t m, int64_t H, int64_t I) {
-  if (mode == NVFP4_MODE_W4A4)
-    return align256(m * H / 2) + align256(m * H / 16) + align256(m * I / 2) + align256(m * I / 16);
+  const size_t nvfp4 = align256(m * H / 2) + align256(m * H / 16) + align256(m * I / 2) + align256(m * I / 16);
+  if (mode == NVFP4_MODE_W4A4) return nvfp4;
+  if (mode == NVFP4_MODE_W4A4_DYN) return nvfp4 + align256(m * sizeof(float));
   return align256(m * I * 2);
 }
 
@@ -362,26 +420,31 @@ static size_t decode_bytes(int64_t H, int64_t I) {
 // Split-K part: sized for the largest plan over the kernels of every path
 // (and, at W4A4 M = 1, for the single-launch decode kernel's records), so
 // the size does not depend on the process-wide path override.
-static size_t mlp_split_bytes(int mode, int64_t M, int64_t H, int64_t I) {
+// Split-K partials and counters of the largest plan over the paths, or the
+// single-launch decode records where that kernel may run.
+static size_t mlp_split_bytes(int mode, int64_t M, int64_t H, int64_t I, bool decode) {
   size_t most = 0;
   for (int path : {NVFP4_PATH_GEMV, NVFP4_PATH_STREAM, NVFP4_PATH_TILED}) {
     const SplitPlan p = split_plan(mlp_kernel(path, mode, M, H, I), mode, M, H, I);
     most = std::max(most, p.part_bytes + p.counter_bytes);
   }
-  if (mode == NVFP4_MODE_W4A4 && M == 1 && nvfp4::decode_supported(H, I)) most = std::max(most, decode_bytes(H, I));
+  if (decode && M == 1 && nvfp4::decode_supported(H, I)) most = std::max(most, decode_bytes(H, I));
   return most;
 }
 
 size_t mlp_workspace_bytes(int mode, int64_t M, int64_t H, int64_t I) {
   if (M < 0 || H <= 0 || I <= 0 || !dim_ok(M) || !dim_ok(H) || !dim_ok(I)) return 0;
-  if (mode != NVFP4_MODE_W4A4 && mode != NVFP4_MODE_W4A16) return 0;
-  return mlp_act_bytes(mode, static_cast<size_t>(M), H, I) + mlp_split_bytes(mode, M, H, I);
+  if (mode != NVFP4_MODE_W4A4 && mode != NVFP4_MODE_W4A16 && mode != NVFP4_MODE_W4A4_DYN) return 0;
+  // W4A4_DYN runs the W4A4 GEMM kernels, never the single-launch decode one.
+  const int kmode = mode == NVFP4_MODE_W4A16 ? NVFP4_MODE_W4A16 : NVFP4_MODE_W4A4;
+  return mlp_act_bytes(mode, static_cast<size_t>(M), H, I) +
+         mlp_split_bytes(kmode, M, H, I, mode == NVFP4_MODE_W4A4);
 }
 
 int mlp_forward(int mode, const uint16_t* x, int64_t M, int64_t H, int64_t I, const void* w_gu_packed,
                 const float* alpha_gu, const void* w_d_packed, const float* alpha_d, const float* g1_inv,
                 const float* g2_inv, void* ws, size_t ws_bytes, void* out, int out_dtype, void* stream) {
-  if (mode != NVFP4_MODE_W4A4 && mode != NVFP4_MODE_W4A16)
+  if (mode != NVFP4_MODE_W4A4 && mode != NVFP4_MODE_W4A16 && mode != NVFP4_MODE_W4A4_DYN)
     return fail(NVFP4_ERR_INVALID_ARG, "unsupported quant mode %d", mode);
   if (!dim_ok(M) || !dim_ok(H) || !dim_ok(I)) return fail(NVFP4_ERR_INVALID_ARG, "dimension out of range");
   if (H <= 0 || H % 256 != 0 || I <= 0 || I % 256 != 0)
@@ -396,6 +459,8 @@ int mlp_forward(int mode, const uint16_t* x, int64_t M, int64_t H, int64_t I, co
     return fail(NVFP4_ERR_INVALID_ARG, "null pointer argument");
   if (mode == NVFP4_MODE_W4A4 && (!g1_inv || !g2_inv))
     return fail(NVFP4_ERR_INVALID_ARG, "W4A4 needs g1_inv and g2_inv");
+  if (mode == NVFP4_MODE_W4A4_DYN && (g1_inv || !g2_inv))
+    return fail(NVFP4_ERR_INVALID_ARG, "W4A4_DYN computes x's scales per token: g1_inv must be NULL, g2_inv set");
   if (!aligned16(x) || !aligned16(w_gu_packed) || !aligned16(w_d_packed) || !aligned16(out) || !aligned16(ws))
     return fail(NVFP4_ERR_INVALID_ARG, "buffers must be 16-byte aligned");
   const size_t need = mlp_workspace_bytes(mode, M, H, I);
@@ -404,6 +469,8 @@ int mlp_forward(int mode, const uint16_t* x, int64_t M, int64_t H, int64_t I, co
   int st = check_device();
   if (st) return st;
   hipStream_t s = as_stream(stream);
+  const bool dyn = mode == NVFP4_MODE_W4A4_DYN;
+  if (dyn) mode = NVFP4_MODE_W4A4;  // the W4A4 kernels, x quantized per token
   const int path = choose_path(mode, M);
   const int epi_out = out_dtype == NVFP4_DTYPE_F32 ? nvfp4::kOutF32 : nvfp4::kOutBF16;
   uint8_t* base = static_cast<uint8_t*>(ws);
@@ -415,7 +482,7 @@ int mlp_forward(int mode, const uint16_t* x, int64_t M, int64_t H, int64_t I, co
   const Kernel k_d = mlp_kernel(path, mode, M, H, I);
   SplitPlan sp = split_plan(k_d, mode, M, H, I);
   if (!clears_counters(k_gu)) sp = SplitPlan{};
-  uint8_t* split_base = base + mlp_act_bytes(mode, m, H, I);
+  uint8_t* split_base = base + mlp_act_bytes(dyn ? NVFP4_MODE_W4A4_DYN : mode, m, H, I);
   float* part = reinterpret_cast<float*>(split_base);
   uint32_t* counters = reinterpret_cast<uint32_t*>(split_base + sp.part_bytes);
   auto with_split = [&](nvfp4::GemmArgs& gu, nvfp4::GemmArgs& dn) {
@@ -433,6 +500,18 @@ int mlp_forward(int mode, const uint16_t* x, int64_t M, int64_t H, int64_t I, co
     uint8_t* xs = xq + align256(m * H / 2);
     uint8_t* hq = xs + align256(m * H / 16);
     uint8_t* hs = hq + align256(m * I / 2);
+    if (dyn) {
+      float* row_g = reinterpret_cast<float*>(hs + align256(m * I / 16));
+      e = nvfp4::launch_quantize_per_token(x, false, M, H, xq, xs, row_g, s);
+      if (e != hipSuccess) return hip_status(e, "mlp_forward quantize_per_token");
+      nvfp4::GemmArgs g1{xq, xs, static_cast<const uint8_t*>(w_gu_packed), M, 2 * I, H, alpha_gu, g2_inv, hq, hs};
+      g1.row_scale = row_g;
+      nvfp4::GemmArgs g2{hq, hs, static_cast<const uint8_t*>(w_d_packed), M, H, I, alpha_d, nullptr, out, nullptr};
+      with_split(g1, g2);
+      e = run_gemm(path, NVFP4_MODE_W4A4, nvfp4::kSwigluNvfp4, g1, s);
+      if (e != hipSuccess) return hip_status(e, "mlp_forward gate_up");
+      return hip_status(run_gemm(path, NVFP4_MODE_W4A4, epi_out, g2, s), "mlp_forward down");
+    }
     // One token under the automatic path: the whole forward in one launch
     // (x quantized as it is staged, h handed from the gate_up workgroups to
     // the down workgroups as epoch-tagged records in the workspace).

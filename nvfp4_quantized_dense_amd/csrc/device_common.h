@@ -227,6 +227,13 @@ __device__ __forceinline__ void clear_words(uint32_t* p, int n) {
 // r = 0..3, of one token column l % 16.
 // ---------------------------------------------------------------------------
 
+// Output scale of a token: alpha, times the token's own factor when the
+// activation has per-token dynamic scales (row_scale[token] = the token's
+// global scale; the product is one fp32 multiply, as alpha itself is).
+__device__ __forceinline__ float row_alpha(float alpha, const float* row_scale, bool valid, int64_t token) {
+  return (row_scale != nullptr && valid) ? alpha * row_scale[token] : alpha;
+}
+
 // Dense output: out[token, row0 + r] = alpha * acc[r].
 template <int E>
 __device__ __forceinline__ void store_dense(const f32x4& acc, float alpha, bool valid,

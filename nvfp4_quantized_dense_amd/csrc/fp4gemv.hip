@@ -34,10 +34,12 @@ __global__ __launch_bounds__(NW * 64) void k_fp4_gemv(GemmArgs args) {
   if (!f4_reduce<NG, MT, NW>(acc, red, wave, lane, lvalid, res)) return;
   const int64_t token = tok0 + tl;
   if constexpr (EpiTraits<EPI>::swiglu) {
-    store_swiglu<EPI>(res[0], res[1], alpha, g2i, lvalid, token, (int64_t)blockIdx.x * kTileRows,
+    store_swiglu<EPI>(res[0], res[1], row_alpha(alpha, args.row_scale, lvalid, token), g2i, lvalid, token,
+                      (int64_t)blockIdx.x * kTileRows,
                       lane, args.N / 2, args.out, args.out_scales);
   } else {
-    store_dense<EPI>(res[0], alpha, lvalid, token, rg0 * kTileRows + 4 * q, args.N, args.out);
+    store_dense<EPI>(res[0], row_alpha(alpha, args.row_scale, lvalid, token), lvalid, token, rg0 * kTileRows + 4 * q,
+                     args.N, args.out);
   }
 #endif  // __HIP_DEVICE_COMPILE__
 }

@@ -17,6 +17,11 @@ hipError_t launch_calibrate(const void* x, bool f32_in, int64_t n, float* g, flo
                             hipStream_t s);
 hipError_t launch_quantize(const void* x, bool f32_in, int64_t M, int64_t K, const float* g_inv,
                            uint8_t* codes, uint8_t* scales, hipStream_t s);
+// Per-token dynamic quantization: each row calibrated on its own amax
+// (g_t = amax_t / 2688, g_inv_t = 1 / g_t, 0 for a zero row) and quantized
+// with g_inv_t; row_g[t] = g_t.
+hipError_t launch_quantize_per_token(const void* x, bool f32_in, int64_t M, int64_t K, uint8_t* codes,
+                                     uint8_t* scales, float* row_g, hipStream_t s);
 
 // repack.hip
 hipError_t launch_repack(int kind, const uint8_t* codes, const uint8_t* scales, int64_t R,
@@ -49,6 +54,10 @@ struct GemmArgs {
   // counters of the GEMM launched next on the same stream).
   uint32_t* zero_ptr = nullptr;
   int zero_n = 0;
+  // Per-token dynamic activation scales (W4A4): when set, token t's output
+  // is scaled by alpha * row_scale[t] (row_scale[t] = the token's global
+  // scale, alpha = the weight's).
+  const float* row_scale = nullptr;
   // W4A4 decode GEMV with the SwiGLU-NVFP4 epilogue at M = 1 only: when
   // set, `a` is bf16 [M, K] and each workgroup quantizes it to NVFP4 with
   // this global scale inverse as it stages it (the same arithmetic as

@@ -229,15 +229,15 @@ __global__ __launch_bounds__(NW * 64) void k_stream(GemmArgs args) {
     const int64_t j0 = (int64_t)blockIdx.x * kTileRows;
 #pragma unroll
     for (int j = 0; j < NT; ++j)
-      store_swiglu<EPI>(acc[0][j], acc[1][j], alpha, g2i, tvalid[j], tok[j], j0, lane, I, args.out,
-                        args.out_scales);
+      store_swiglu<EPI>(acc[0][j], acc[1][j], row_alpha(alpha, args.row_scale, tvalid[j], tok[j]), g2i,
+                        tvalid[j], tok[j], j0, lane, I, args.out, args.out_scales);
   } else {
 #pragma unroll
     for (int g = 0; g < NG; ++g)
 #pragma unroll
       for (int j = 0; j < NT; ++j)
-        store_dense<EPI>(acc[g][j], alpha, tvalid[j], tok[j], (rg0 + g) * kTileRows + 4 * q, args.N,
-                         args.out);
+        store_dense<EPI>(acc[g][j], row_alpha(alpha, args.row_scale, tvalid[j], tok[j]), tvalid[j], tok[j],
+                         (rg0 + g) * kTileRows + 4 * q, args.N, args.out);
   }
 #endif  // __HIP_DEVICE_COMPILE__
 }

@@ -220,19 +220,20 @@ __global__ __launch_bounds__(NWR * NWT * 64, 1) void k_tiled2(GemmArgs args, int
   for (int j = 0; j < TG; ++j) {
     const int64_t token = tok0 + 16 * (TG * wt + j) + tl;
     const bool tv = token < M;
+    const float at = row_alpha(alpha, args.row_scale, tv, token);  // per-token factor, if any
     if constexpr (EpiTraits<EPI>::swiglu) {
       const float g2i = (EPI == kSwigluNvfp4) ? *args.g2_inv : 0.0f;
 #pragma unroll
       for (int g = 0; g < GR; g += 2) {
         const int64_t grp = rg0 + GR * wr + g;  // gate group (even), up group grp + 1
-        store_swiglu<EPI>(acc[g][j], acc[g + 1][j], alpha, g2i, tv && grp < ngroups, token,
+        store_swiglu<EPI>(acc[g][j], acc[g + 1][j], at, g2i, tv && grp < ngroups, token,
                           (grp >> 1) * kTileRows, lane, N / 2, args.out, args.out_scales);
       }
     } else {
 #pragma unroll
       for (int g = 0; g < GR; ++g) {
         const int64_t grp = rg0 + GR * wr + g;
-        store_dense<EPI>(acc[g][j], alpha, tv && grp < ngroups, token, grp * kTileRows + 4 * q, N,
+        store_dense<EPI>(acc[g][j], at, tv && grp < ngroups, token, grp * kTileRows + 4 * q, N,
                          args.out);
       }
     }

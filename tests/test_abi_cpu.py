@@ -44,6 +44,11 @@ def test_packed_and_workspace_sizes():
     assert w >= 2560 + 320 + 8704 + 1088 and w % 256 == 0
     assert nv.mlp_workspace_bytes(nv.MODE_W4A16, 4, 256, 512) == 4 * 512 * 2
     assert nv.mlp_workspace_bytes(9, 1, 256, 512) == 0
+    # W4A4_DYN: the W4A4 activations, then one fp32 g per token
+    # x codes 512, x scales 64 -> 256, h codes 1024, h scales 128 -> 256, g 16 -> 256
+    assert nv.mlp_workspace_bytes(nv.MODE_W4A4_DYN, 4, 256, 512) == 512 + 256 + 1024 + 256 + 256
+    assert nv.mlp_workspace_bytes(nv.MODE_W4A4_DYN, 1000, 256, 512) >= \
+        nv.mlp_workspace_bytes(nv.MODE_W4A4, 1000, 256, 512) + 4000
 
 
 def _code(fn, *args):
@@ -84,6 +89,19 @@ def test_invalid_arguments_are_rejected_on_the_host():
     assert lib.mlp_forward(0, P, 4, 256, 512, P, P, P, P, N, P, P, ws, P, 1, N) == INV  # W4A4 no g1
     assert lib.mlp_forward(0, P, 4, 256, 512, P, P, P, P, P, P, P, ctypes.c_size_t(16), P, 1, N) == INV
     assert b"workspace" in lib.nvfp4_last_error()
+    # per-token dynamic scales
+    assert lib.nvfp4_quantize_per_token(P, 0, 4, 250, P, P, P, N) == INV       # K % 16
+    assert lib.nvfp4_quantize_per_token(P, 0, 4, 256, P, P, N, N) == INV       # null row_g
+    assert lib.nvfp4_quantize_per_token(P, 0, 4, 256, P, P, ctypes.c_void_p(0x100002), N) == INV
+    assert lib.nvfp4_quantize_per_token(N, 0, 0, 256, N, N, N, N) == nv.NVFP4_OK  # empty
+    assert lib.nvfp4_gemm_rowscale(P, P, N, P, 4, 16, 256, P, P, 1, N) == INV   # null row_g
+    assert lib.nvfp4_gemm_rowscale(P, P, P, P, 4, 16, 200, P, P, 1, N) == INV   # K % 256
+    assert lib.nvfp4_gemm_rowscale(N, N, N, P, 0, 16, 256, P, P, 1, N) == nv.NVFP4_OK
+    assert lib.gemm_swiglu_nvfp4_quant_rowscale(P, P, N, P, 4, 32, 256, P, P, P, P, N) == INV
+    assert lib.gemm_swiglu_nvfp4_quant_rowscale(P, P, P, P, 4, 24, 256, P, P, P, P, N) == INV
+    assert lib.mlp_forward(2, P, 4, 256, 512, P, P, P, P, P, P, P, ws, P, 1, N) == INV  # DYN + g1
+    assert b"per token" in lib.nvfp4_last_error()
+    assert lib.mlp_forward(2, P, 4, 256, 512, P, P, P, P, N, N, P, ws, P, 1, N) == INV  # DYN no g2
     assert lib.nvfp4_set_path(9) == INV
 
 
