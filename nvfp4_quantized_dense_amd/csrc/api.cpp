@@ -165,8 +165,24 @@ struct SplitPlan {
 SplitPlan split_plan(Kernel k, int mode, int64_t M, int64_t N, int64_t K) {
   SplitPlan p;
   if (M <= 0) return p;
-  if (k != kStream && k != kTiled16) return p;
   (void)mode;
+  if (k == kTiled2) {
+    // The W4A4 tiled kernel splits only the tiles of a last round that is
+    // at most half full (one workgroup per CU): into as many K splits as
+    // fill that round, at least 8 K tiles each.
+    const nvfp4::TileShape ts = nvfp4::tiled2_shape(M, N);
+    const int64_t tail = nvfp4::tiled2_tail(ts.units), T = K / 256;
+    if (tail == 0 || 2 * tail > nvfp4::kTiled2Slots) return p;
+    int64_t ks = std::min<int64_t>(nvfp4::kTiled2Slots / tail, 8);
+    while (ks > 1 && ((ks - 1) * ((T + ks - 1) / ks) >= T || (T + ks - 1) / ks < 8)) --ks;
+    if (ks <= 1) return p;
+    p.ways = (int)ks;
+    p.units = tail;
+    p.part_bytes = align256((size_t)(tail * ks * ts.tile_floats) * sizeof(float));
+    p.counter_bytes = align256((size_t)tail * sizeof(uint32_t));
+    return p;
+  }
+  if (k != kStream && k != kTiled16) return p;
   nvfp4::TileShape ts;
   if (k == kStream) {
     ts = nvfp4::stream_shape(M, N);
@@ -197,7 +213,9 @@ Kernel mlp_kernel(int path, int mode, int64_t M, int64_t N, int64_t K) {
 }
 
 // The kernels that clear the split-K counters of the GEMM after them.
-bool clears_counters(Kernel k) { return k == kFp4Gemv || k == kValuGemv || k == kStream || k == kTiled16; }
+bool clears_counters(Kernel k) {
+  return k == kFp4Gemv || k == kValuGemv || k == kStream || k == kTiled2 || k == kTiled16;
+}
 
 // Shared checks of the GEMM entry points. N is the packed row count.
 int check_gemm(int mode, const void* a, const uint8_t* a_scales, const void* w, int64_t M,

@@ -207,6 +207,48 @@ __device__ __forceinline__ bool splitk_last(f32x4 (&res)[NT], float* part, uint3
   return true;
 }
 
+// K-split combine of a workgroup's output tile (NT threads, acc[A][B] per
+// thread). Each thread stores its partial of split `split` of tile `unit`
+// (device scope), every wave waits for its stores to complete, then one
+// thread counts the workgroup's arrival. The workgroup that arrives last (of
+// ks) adds the ks partials in split order (the result does not depend on
+// arrival order), resets the count and returns true; the others return
+// false. part holds ks * A * B * 4 * NT floats per tile.
+#if defined(__HIP_DEVICE_COMPILE__)
+template <int A, int B, int NT>
+__device__ __forceinline__ bool wg_splitk_last(f32x4 (&acc)[A][B], float* part, uint32_t* counters, int ks,
+                                               int64_t unit, int split, int tid, uint32_t* arrived_lds) {
+  constexpr int kTileFloats = A * B * 4 * NT;
+  const Rsrc rp = make_rsrc(part + unit * ks * kTileFloats, (uint32_t)(ks * kTileFloats * 4));
+#pragma unroll
+  for (int g = 0; g < A; ++g)
+#pragma unroll
+    for (int j = 0; j < B; ++j)
+      bstore16_dev(rp, (uint32_t)(((split * A * B + B * g + j) * NT + tid) * 16), __builtin_bit_cast(u32x4, acc[g][j]));
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0): this wave's partial is at device scope
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __syncthreads();
+  if (tid == 0)
+    *arrived_lds = __hip_atomic_fetch_add(counters + unit, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (*arrived_lds != (uint32_t)(ks - 1)) return false;
+#pragma unroll
+  for (int g = 0; g < A; ++g)
+#pragma unroll
+    for (int j = 0; j < B; ++j) acc[g][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int sp = 0; sp < ks; ++sp) {
+#pragma unroll
+    for (int g = 0; g < A; ++g)
+#pragma unroll
+      for (int j = 0; j < B; ++j)
+        acc[g][j] += __builtin_bit_cast(f32x4, bload16_dev(rp, (uint32_t)(((sp * A * B + B * g + j) * NT + tid) * 16)));
+  }
+  if (tid == 0) __hip_atomic_store(counters + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return true;
+}
+#endif  // __HIP_DEVICE_COMPILE__
+
 // A kernel-uniform scalar read at this point of the program: the scalar load
 // is issued here and kept in a register, not sunk to its use (an epilogue
 // reading it after the main loop would wait there for a memory round trip).

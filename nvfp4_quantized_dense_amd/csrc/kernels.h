@@ -105,7 +105,13 @@ hipError_t launch_fp4_gemv(int epi, const GemmArgs& a, hipStream_t s);
 hipError_t launch_tiled_gemm(int mode, int epi, const GemmArgs& a, hipStream_t s);
 
 // W4A4 only; packed weight, activation codes and scales each < 2^31 bytes.
+// With ksplit > 1 (dense epilogues) only the tiles of the last, partial
+// round of one workgroup per CU are K-split: tiled2_tail(units) of them,
+// which must be nonzero; part and counters are sized for those.
 hipError_t launch_tiled2_gemm(int epi, const GemmArgs& a, hipStream_t s);
+TileShape tiled2_shape(int64_t M, int64_t N);
+constexpr int64_t kTiled2Slots = 256;  // workgroups resident at once: one per CU
+inline int64_t tiled2_tail(int64_t units) { return units > kTiled2Slots ? units % kTiled2Slots : 0; }
 // W4A16 only; packed weight and the activation rows (+256 of padding) each
 // < 2^31 bytes.
 hipError_t launch_tiled16_gemm(int epi, const GemmArgs& a, hipStream_t s);

@@ -9,13 +9,16 @@
 // Activations are read from global memory (they are small and stay in L2) in
 // their NVFP4 or bf16 form and dequantized in registers like the weights.
 //
-// Work split: a workgroup owns NG packed row groups (2 for the SwiGLU pair
-// gate/up) and NW waves divide the K tiles between them; each wave loads a
-// tile (weights and activations together, branch-free: past the last tile
-// the loads are out of range) and multiplies it. Partial sums are combined
-// through LDS in a fixed order (deterministic).
+// Work split: a workgroup owns G packed row groups (gate/up pairs for the
+// SwiGLU epilogues) and NW waves divide the K tiles between them; each wave
+// loads a tile (weights and activations together, branch-free: past the last
+// tile the loads are out of range) and multiplies it. Partial sums are
+// combined through LDS in a fixed order (deterministic). Several row groups
+// per workgroup read each activation slice once for all of them and keep more
+// weight bytes in flight per wave.
 #include "device_common.h"
 #include "kernels.h"
+#include "stream_groups.h"
 
 namespace nvfp4 {
 
@@ -133,10 +136,11 @@ __device__ __forceinline__ void stream_compute(f32x4 (&acc)[NG][NT], const Strea
 }  // namespace
 #endif  // __HIP_DEVICE_COMPILE__
 
-template <int MODE, int EPI, int NT, int NW>
+template <int MODE, int EPI, int NT, int NW, int G>
 __global__ __launch_bounds__(NW * 64) void k_stream(GemmArgs args) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  constexpr int NG = EpiTraits<EPI>::swiglu ? 2 : 1;
+  constexpr int NG = G;
+  static_assert(!EpiTraits<EPI>::swiglu || G % 2 == 0, "SwiGLU takes gate/up group pairs");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int q = lane >> 4;
@@ -221,16 +225,19 @@ __global__ __launch_bounds__(NW * 64) void k_stream(GemmArgs args) {
   if constexpr (!EpiTraits<EPI>::swiglu) {
     if (ks > 1) {
       const int64_t unit = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
-      if (!splitk_last<NT>(acc[0], args.part, args.counters, ks, unit, (int)blockIdx.z, lane)) return;
+      if (!splitk_last<NG * NT>(reinterpret_cast<f32x4(&)[NG * NT]>(acc), args.part, args.counters, ks, unit,
+                                (int)blockIdx.z, lane))
+        return;
     }
   }
   if constexpr (EpiTraits<EPI>::swiglu) {
     const int64_t I = args.N / 2;
-    const int64_t j0 = (int64_t)blockIdx.x * kTileRows;
 #pragma unroll
-    for (int j = 0; j < NT; ++j)
-      store_swiglu<EPI>(acc[0][j], acc[1][j], row_alpha(alpha, args.row_scale, tvalid[j], tok[j]), g2i,
-                        tvalid[j], tok[j], j0, lane, I, args.out, args.out_scales);
+    for (int pp = 0; pp < NG / 2; ++pp)
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+        store_swiglu<EPI>(acc[2 * pp][j], acc[2 * pp + 1][j], row_alpha(alpha, args.row_scale, tvalid[j], tok[j]),
+                          g2i, tvalid[j], tok[j], (rg0 / 2 + pp) * kTileRows, lane, I, args.out, args.out_scales);
   } else {
 #pragma unroll
     for (int g = 0; g < NG; ++g)
@@ -242,27 +249,33 @@ __global__ __launch_bounds__(NW * 64) void k_stream(GemmArgs args) {
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-template <int MODE, int EPI, int NT, int NW>
+template <int MODE, int EPI, int NT, int NW, int G>
 static hipError_t launch_nt_nw(const GemmArgs& a, hipStream_t s) {
-  constexpr int NG = EpiTraits<EPI>::swiglu ? 2 : 1;
-  dim3 grid((unsigned)(a.N / kTileRows / NG), (unsigned)((a.M + 16 * NT - 1) / (16 * NT)), (unsigned)a.ksplit);
-  k_stream<MODE, EPI, NT, NW><<<grid, NW * 64, 0, s>>>(a);
+  dim3 grid((unsigned)(a.N / kTileRows / G), (unsigned)((a.M + 16 * NT - 1) / (16 * NT)), (unsigned)a.ksplit);
+  k_stream<MODE, EPI, NT, NW, G><<<grid, NW * 64, 0, s>>>(a);
   return hipGetLastError();
 }
 
 // Waves per workgroup: 8 for one token group (measured best at M = 2..16
 // on the decode shapes), 4 for more token groups (their register sets leave
-// room for fewer waves per SIMD).
+// room for fewer waves per SIMD). Row groups per workgroup: stream_groups.
 template <int MODE, int EPI, int NT>
 static hipError_t launch_nt(const GemmArgs& a, hipStream_t s) {
-  if constexpr (NT == 1) return launch_nt_nw<MODE, EPI, NT, 8>(a, s);
-  return launch_nt_nw<MODE, EPI, NT, 4>(a, s);
+  constexpr bool sw = EpiTraits<EPI>::swiglu;
+  if constexpr (NT == 1) {
+    if constexpr (!sw) {
+      if (stream_groups(sw, a.M, a.N) == 1) return launch_nt_nw<MODE, EPI, NT, 8, 1>(a, s);
+    }
+    return launch_nt_nw<MODE, EPI, NT, 8, 2>(a, s);
+  }
+  return launch_nt_nw<MODE, EPI, NT, 4, sw ? 2 : 1>(a, s);
 }
 
 TileShape stream_shape(int64_t M, int64_t N) {
   int64_t groups = (M + 15) / 16;
   const int64_t nt = groups < 4 ? groups : 4;
-  return TileShape{N / kTileRows * ((M + 16 * nt - 1) / (16 * nt)), 256 * nt, nt == 1 ? 8 : 4};
+  const int64_t g = nt == 1 ? stream_groups(false, M, N) : 1;
+  return TileShape{N / kTileRows / g * ((M + 16 * nt - 1) / (16 * nt)), 256 * nt * g, nt == 1 ? 8 : 4};
 }
 
 template <int MODE, int EPI>

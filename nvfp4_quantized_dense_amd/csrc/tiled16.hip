@@ -135,45 +135,6 @@ __device__ __forceinline__ void compute_stage16(f32x4 (&acc)[2][8], const uint8_
   }
 }
 
-// Split-K combine of a workgroup tile (every thread holds 16 f32x4 of it):
-// the partial is stored with device-scope stores in thread-major order,
-// every wave waits for its stores to complete, then one thread counts the
-// workgroup's arrival. The workgroup that arrives last (of ks) adds the ks
-// partials in split order (the result does not depend on arrival order),
-// resets the count and returns true; the others return false.
-__device__ __forceinline__ bool tile_splitk_last(f32x4 (&acc)[2][8], float* part, uint32_t* counters, int ks,
-                                                 int64_t unit, int split, int tid, uint32_t* arrived_lds) {
-  constexpr int kTileFloats = kG16 * 16 * kTG16 * 16;
-  const Rsrc rp = make_rsrc(part + unit * ks * kTileFloats, (uint32_t)(ks * kTileFloats * 4));
-#pragma unroll
-  for (int g = 0; g < 2; ++g)
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      bstore16_dev(rp, (uint32_t)(((split * 16 + 8 * g + j) * (kNW16 * 64) + tid) * 16),
-                   __builtin_bit_cast(u32x4, acc[g][j]));
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0): this wave's partial is at device scope
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __syncthreads();
-  if (tid == 0)
-    *arrived_lds = __hip_atomic_fetch_add(counters + unit, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  if (*arrived_lds != (uint32_t)(ks - 1)) return false;
-#pragma unroll
-  for (int g = 0; g < 2; ++g)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[g][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int sp = 0; sp < ks; ++sp) {
-#pragma unroll
-    for (int g = 0; g < 2; ++g)
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        acc[g][j] += __builtin_bit_cast(
-            f32x4, bload16_dev(rp, (uint32_t)(((sp * 16 + 8 * g + j) * (kNW16 * 64) + tid) * 16)));
-  }
-  if (tid == 0) __hip_atomic_store(counters + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return true;
-}
 
 }  // namespace
 #endif  // __HIP_DEVICE_COMPILE__
@@ -237,7 +198,8 @@ __global__ __launch_bounds__(kNW16 * 64, 1) void k_tiled16(GemmArgs args, int64_
     __builtin_amdgcn_s_setprio(0);
   }
   if constexpr (SPLIT) {
-    if (!tile_splitk_last(acc, args.part, args.counters, ks, tile, split, (int)threadIdx.x, &arrived)) return;
+    if (!wg_splitk_last<2, 8, kNW16 * 64>(acc, args.part, args.counters, ks, tile, split, (int)threadIdx.x, &arrived))
+      return;
   }
 
 #pragma unroll

@@ -17,6 +17,14 @@
 // so XCD x is given a contiguous run of output tiles ordered weight-tile-
 // major; the workgroups resident on one XCD share a weight tile in its L2
 // while they sweep the token tiles.
+//
+// One workgroup fits a CU (two 72 KB stages of LDS), so output tiles run in
+// rounds of one per CU. When the last round would be at most half full (the
+// down projection at 8192 tokens, hidden 7168: 896 tiles, 3.5 rounds), a
+// dense GEMM given split-K buffers runs the whole rounds in one launch and
+// the tail tiles in a second one with K split over ks workgroups each, so
+// the tail takes 1 / ks of a round (the partials are combined by the last
+// workgroup of each tile, in split order).
 #include "device_common.h"
 #include "kernels.h"
 
@@ -158,17 +166,25 @@ __device__ __forceinline__ void compute_chunk(f32x4 (&acc)[GR][TG], const uint8_
 #endif  // __HIP_DEVICE_COMPILE__
 
 // NWR x NWT waves; wave (wr, wt) owns row groups GR*wr.. and token groups TG*wt..
-template <int EPI, int NWR, int NWT>
-__global__ __launch_bounds__(NWR * NWT * 64, 1) void k_tiled2(GemmArgs args, int64_t n_tiles,
-                                                              int64_t m_tiles, int64_t per_xcd) {
+// This launch covers output tiles [tile0, tile0 + count); with SPLIT (dense
+// epilogues, args.ksplit > 1) each of them as args.ksplit K splits.
+template <int EPI, int NWR, int NWT, bool SPLIT>
+__global__ __launch_bounds__(NWR * NWT * 64, 1) void k_tiled2(GemmArgs args, int64_t m_tiles, int64_t per_xcd,
+                                                              int64_t tile0, int64_t count) {
 #if defined(__HIP_DEVICE_COMPILE__)
   constexpr int NW = NWR * NWT;
   constexpr int GR = kG / NWR;
   constexpr int TG = kTG / NWT;
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStageBytes];
+  __shared__ uint32_t arrived;
+  clear_words(args.zero_ptr, args.zero_n);
+  const int ks = SPLIT ? args.ksplit : 1;
   const int64_t id = blockIdx.x;
-  const int64_t tile = (id & 7) * per_xcd + (id >> 3);
-  if (tile >= n_tiles * m_tiles) return;
+  const int64_t f = (id & 7) * per_xcd + (id >> 3);
+  if (f >= count * ks) return;
+  const int64_t local = f / ks;
+  const int split = (int)(f - local * ks);
+  const int64_t tile = tile0 + local;
   const int64_t n_tile = tile / m_tiles, m_tile = tile % m_tiles;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -185,16 +201,18 @@ __global__ __launch_bounds__(NWR * NWT * 64, 1) void k_tiled2(GemmArgs args, int
 #pragma unroll
     for (int j = 0; j < TG; ++j) acc[g][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // K tiles [t0, t1) of this split (all of them without a split).
+  const int64_t per = (T + ks - 1) / ks, t0 = split * per, t1 = min(T, t0 + per);
   const StageSrc<NW> src = stage_src<NW>(args, tok0, wave, lane);
-  issue_stage<NW>(src, smem, 0, T, rg0, ngroups, wave, lane);
-  for (int64_t t = 0; t < T; ++t) {
-    uint8_t* buf = smem + (t & 1) * kStageBytes;
+  issue_stage<NW>(src, smem, t0, T, rg0, ngroups, wave, lane);
+  for (int64_t t = t0; t < t1; ++t) {
+    uint8_t* buf = smem + ((t - t0) & 1) * kStageBytes;
     // This wave's loads of stage t are the only ones outstanding: wait for
     // them, then for every wave's (and for everyone to be done reading the
     // buffer the next stage overwrites).
     __builtin_amdgcn_s_waitcnt(0x3F70);  // vmcnt(0), other counters unchanged
     __builtin_amdgcn_s_barrier();
-    if (t + 1 < T) issue_stage<NW>(src, smem + ((t + 1) & 1) * kStageBytes, t + 1, T, rg0, ngroups, wave, lane);
+    if (t + 1 < t1) issue_stage<NW>(src, smem + ((t + 1 - t0) & 1) * kStageBytes, t + 1, T, rg0, ngroups, wave, lane);
     uint32_t wsd[GR], xsd[TG];
     const uint8_t* As = buf + kWBytes + kACodeBytes;
 #pragma unroll
@@ -215,6 +233,11 @@ __global__ __launch_bounds__(NWR * NWT * 64, 1) void k_tiled2(GemmArgs args, int
     __builtin_amdgcn_s_setprio(0);
   }
 
+  if constexpr (SPLIT) {
+    if (!wg_splitk_last<GR, TG, NW * 64>(acc, args.part, args.counters, ks, local, split, (int)threadIdx.x,
+                                         &arrived))
+      return;
+  }
   const float alpha = *args.alpha;
 #pragma unroll
   for (int j = 0; j < TG; ++j) {
@@ -241,21 +264,43 @@ __global__ __launch_bounds__(NWR * NWT * 64, 1) void k_tiled2(GemmArgs args, int
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
+template <int EPI, bool SPLIT>
+static hipError_t launch_range(const GemmArgs& a, int64_t m_tiles, int64_t tile0, int64_t count, int ks,
+                               hipStream_t s) {
+  constexpr int NWR = 2, NWT = 4;
+  const int64_t per_xcd = (count * ks + 7) / 8;
+  k_tiled2<EPI, NWR, NWT, SPLIT><<<(unsigned)(8 * per_xcd), NWR * NWT * 64, 0, s>>>(a, m_tiles, per_xcd, tile0, count);
+  return hipGetLastError();
+}
+
 template <int EPI>
 static hipError_t launch_e(const GemmArgs& a, hipStream_t s) {
-  constexpr int NWR = 2, NWT = 4;
-  const int64_t ngroups = a.N / kTileRows;
-  const int64_t n_tiles = (ngroups + kG - 1) / kG;
+  const TileShape ts = tiled2_shape(a.M, a.N);
   const int64_t m_tiles = (a.M + kTG * 16 - 1) / (kTG * 16);
-  const int64_t per_xcd = (n_tiles * m_tiles + 7) / 8;
-  k_tiled2<EPI, NWR, NWT><<<(unsigned)(8 * per_xcd), NWR * NWT * 64, 0, s>>>(a, n_tiles, m_tiles, per_xcd);
-  return hipGetLastError();
+  if constexpr (!EpiTraits<EPI>::swiglu) {
+    if (a.ksplit > 1) {
+      const int64_t tail = tiled2_tail(ts.units), whole = ts.units - tail;
+      if (tail == 0) return hipErrorInvalidValue;  // the split buffers are sized for the tail tiles
+      hipError_t e = hipSuccess;
+      if (whole > 0) e = launch_range<EPI, false>(a, m_tiles, 0, whole, 1, s);
+      if (e != hipSuccess) return e;
+      return launch_range<EPI, true>(a, m_tiles, whole, tail, a.ksplit, s);
+    }
+  }
+  return launch_range<EPI, false>(a, m_tiles, 0, ts.units, 1, s);
+}
+
+TileShape tiled2_shape(int64_t M, int64_t N) {
+  const int64_t n_tiles = (N / kTileRows + kG - 1) / kG;
+  const int64_t m_tiles = (M + kTG * 16 - 1) / (kTG * 16);
+  return TileShape{n_tiles * m_tiles, kG * 16 * kTG * 16, 8};
 }
 
 // W4A4 only. Needs the packed weight, codes and scales below 2^31 bytes each
 // (32-bit buffer offsets); the caller checks.
 hipError_t launch_tiled2_gemm(int epi, const GemmArgs& a, hipStream_t s) {
   if (a.M == 0) return hipSuccess;
+  if (!splitk_valid(a, epi)) return hipErrorInvalidValue;
   switch (epi) {
     case kOutF32: return launch_e<kOutF32>(a, s);
     case kOutBF16: return launch_e<kOutBF16>(a, s);

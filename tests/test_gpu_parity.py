@@ -437,6 +437,29 @@ def test_mlp_prefill_full_size_sampled_rows():
     _check_mlp("w4a4", 8192, 7168, 18432, rows=rows)
 
 
+def test_mlp_prefill_tail_split():
+    """W4A4 prefill whose down projection ends in a part-filled round of
+    tiles: hidden 4096 (16 weight tiles) x 4352 tokens (17 token tiles) is
+    272 output tiles, 16 past one per CU, so those 16 are K-split (3 ways at
+    intermediate 6144). Sampled rows (all but the first 256 tokens cross the
+    split tiles) against the oracle; a second call on the same workspace
+    (counters left at zero by the first) gives the same bytes."""
+    nv.set_path(nv.PATH_AUTO)
+    M, H, I = 4352, 4096, 6144
+    rows = np.unique(np.concatenate([np.random.default_rng(4352).choice(M, 24, replace=False), [0, 300, M - 1]]))
+    y = _check_mlp("w4a4", M, H, I, rows=rows)
+    w = mlp_weights(H, I, 0)
+    p_gu, p_d = packed_weights(H, I, 0)
+    x = synth.activations(0, M, H)
+    sc = calibrate_activation_scales(x[:64], w)
+    ws = torch.zeros(nv.mlp_workspace_bytes(0, M, H, I), dtype=torch.uint8, device=dev())
+    outs = []
+    for _ in range(2):
+        outs.append(to_host(nv.mlp_forward(0, to_dev(x), p_gu, scalar(sc["a_gu"]), p_d, scalar(sc["a_d"]), I,
+                                           g1_inv=scalar(sc["g1_inv"]), g2_inv=scalar(sc["g2_inv"]), ws=ws)))
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], y)
+
+
 @pytest.mark.parametrize("M", [1, 16, 256, 4096])
 def test_mlp_w4a16_full_size(M):
     nv.set_path(nv.PATH_AUTO)
