@@ -46,6 +46,9 @@ constexpr int kDecodeWaves = 4;
 constexpr int kDownSets = 4;         // weight tiles per wave in flight in a down unit
 constexpr int kPollWords = 8;        // record words per thread a down unit can poll
 constexpr int kSpinLimit = 1 << 20;  // polls of a wait (each at least a memory round trip)
+// K tiles per down split aimed at: all of a split's weight tiles in the
+// wave's registers (kDownSets per wave) before the wait for h.
+constexpr int kSplitTiles = kDownSets * kDecodeWaves;
 // Down units cover at most this many K tiles (48 record words per tile).
 constexpr int kMaxSplitTiles = kPollWords * kDecodeWaves * 64 / 48;
 
@@ -226,7 +229,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void k_decode_mlp(DecodeArgs d) 
 int decode_splits(int64_t H, int64_t I) {
   (void)H;
   const int64_t T = I / kTileK;
-  int64_t ks = (T + kDownSets * kDecodeWaves - 1) / (kDownSets * kDecodeWaves);
+  int64_t ks = (T + kSplitTiles - 1) / kSplitTiles;
   ks = ks < 1 ? 1 : (ks > kDecodeMaxSplits ? kDecodeMaxSplits : ks);
   while (ks > 1 && (ks - 1) * ((T + ks - 1) / ks) >= T) --ks;
   return (int)ks;
