@@ -83,16 +83,19 @@ __device__ __forceinline__ void stream_load(StreamTile<MODE, NG, NT>& d, const S
 template <int MODE, int NG, int NT>
 __device__ __forceinline__ void stream_compute(f32x4 (&acc)[NG][NT], const StreamTile<MODE, NG, NT>& d) {
   if constexpr (MODE == kW4A4) {
+    // E4M3 scale bytes to f16, two per instruction (exact).
     _Float16 ws[NG][4], xs[NT][4];
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
-      ws[g][0] = scale_f16<0>(d.wsd[g]); ws[g][1] = scale_f16<1>(d.wsd[g]);
-      ws[g][2] = scale_f16<2>(d.wsd[g]); ws[g][3] = scale_f16<3>(d.wsd[g]);
+      const f16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d.wsd[g], 1.0f, false);
+      const f16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d.wsd[g], 1.0f, true);
+      ws[g][0] = lo.x; ws[g][1] = lo.y; ws[g][2] = hi.x; ws[g][3] = hi.y;
     }
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-      xs[j][0] = scale_f16<0>(d.xsd[j][0]); xs[j][1] = scale_f16<1>(d.xsd[j][0]);
-      xs[j][2] = scale_f16<0>(d.xsd[j][1]); xs[j][3] = scale_f16<1>(d.xsd[j][1]);
+      const f16x2 a0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d.xsd[j][0], 1.0f, false);
+      const f16x2 a1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d.xsd[j][1], 1.0f, false);
+      xs[j][0] = a0.x; xs[j][1] = a0.y; xs[j][2] = a1.x; xs[j][3] = a1.y;
     }
 #pragma unroll
     for (int c = 0; c < 2; ++c)

@@ -118,10 +118,11 @@ __device__ __forceinline__ f16x8 deq8_f16x2(uint32_t w, f16x2 s2) {
   return r;
 }
 
-template <int SEL>
-__device__ __forceinline__ f16x2 scale_pair(uint32_t sdw) {
-  const _Float16 s = scale_f16<SEL>(sdw);
-  return f16x2{s, s};
+// E4M3 scale bytes 2 HI and 2 HI + 1 of a word as f16 {s0, s1}, one
+// instruction for both (E4M3 values are exact in f16).
+template <bool HI>
+__device__ __forceinline__ f16x2 scale_f16x2(uint32_t sdw) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sdw, 1.0f, HI);
 }
 
 // One 128-column chunk (C = 0, 1) of a staged K tile: 4 MFMA K-steps of 32.
@@ -139,13 +140,20 @@ __device__ __forceinline__ void compute_chunk(f32x4 (&acc)[GR][TG], const uint8_
 #pragma unroll
   for (int g = 0; g < GR; ++g)
     wc[g] = *reinterpret_cast<const u32x4*>(W + (g0 + g) * kTileBytes + C * 1024 + 16 * lane);
+  // Scales of this chunk's two 16-blocks (bytes 2C, 2C + 1 of each word),
+  // each multiplied as the pair {s, s} (a half-select the multiply encodes).
+  f16x2 xsp[TG], wsp[GR];
+#pragma unroll
+  for (int j = 0; j < TG; ++j) xsp[j] = scale_f16x2<C == 1>(xsd[j]);
+#pragma unroll
+  for (int g = 0; g < GR; ++g) wsp[g] = scale_f16x2<C == 1>(wsd[g]);
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
     f16x2 xs[TG], ws[GR];
 #pragma unroll
-    for (int j = 0; j < TG; ++j) xs[j] = blk ? scale_pair<2 * C + 1>(xsd[j]) : scale_pair<2 * C>(xsd[j]);
+    for (int j = 0; j < TG; ++j) xs[j] = blk ? f16x2{xsp[j].y, xsp[j].y} : f16x2{xsp[j].x, xsp[j].x};
 #pragma unroll
-    for (int g = 0; g < GR; ++g) ws[g] = blk ? scale_pair<2 * C + 1>(wsd[g]) : scale_pair<2 * C>(wsd[g]);
+    for (int g = 0; g < GR; ++g) ws[g] = blk ? f16x2{wsp[g].y, wsp[g].y} : f16x2{wsp[g].x, wsp[g].x};
 #pragma unroll
     for (int uu = 0; uu < 2; ++uu) {
       const int u = 2 * blk + uu;
