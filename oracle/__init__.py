@@ -21,6 +21,7 @@ _u8p = ctypes.POINTER(ctypes.c_uint8)
 _u16p = ctypes.POINTER(ctypes.c_uint16)
 _f32p = ctypes.POINTER(ctypes.c_float)
 _f64p = ctypes.POINTER(ctypes.c_double)
+_i32p = ctypes.POINTER(ctypes.c_int32)
 _i64 = ctypes.c_int64
 _f32 = ctypes.c_float
 
@@ -57,6 +58,8 @@ def _lib():
             "orc_mlp_w4a4_per_token": (None, [_u16p, _i64, _i64, _i64, _u8p, _u8p, _f32, _u8p, _u8p,
                                               _f32, _f32, _f32p, _u8p, _u8p, _f32p, _f32p, _f32p,
                                               _u8p, _u8p]),
+            "orc_silu_mul_quant_experts": (None, [_u16p, _i64, _i64, _i64, _i32p, _f32p, _u8p, _u8p,
+                                                  _f32p]),
             "orc_num_threads": (ctypes.c_int, []),
         }
         for name, (res, args) in sig.items():
@@ -198,6 +201,27 @@ def swiglu(gu: np.ndarray) -> np.ndarray:
     h = np.empty((M, I), np.float32)
     _lib().orc_swiglu(_p(gu, _f32p), M, I, _p(h, _f32p))
     return h
+
+
+def silu_mul_quant_experts(gate_up_bf16, masked_m, g_inv, codes=None, scales=None):
+    """Standalone SiLU(gate) * up + NVFP4 quantization of a bf16 gate_up
+    [E, M, 2I] by expert: rows t < masked_m[e] of expert e quantized with
+    g_inv[e]. Returns (codes [E, M, I/2], scales [E, M, I/16], h [E, M, I]);
+    rows past masked_m keep what codes/scales held (zeros if not given) and
+    their h is NaN."""
+    gu = _c(gate_up_bf16, np.uint16)
+    E, M, I2 = gu.shape
+    I = I2 // 2
+    assert I % 16 == 0
+    mm = _c(masked_m, np.int32)
+    gi = _c(g_inv, np.float32)
+    assert mm.shape == (E,) and gi.shape == (E,)
+    codes = np.zeros((E, M, I // 2), np.uint8) if codes is None else _c(codes, np.uint8).copy()
+    scales = np.zeros((E, M, I // 16), np.uint8) if scales is None else _c(scales, np.uint8).copy()
+    h = np.full((E, M, I), np.nan, np.float32)
+    _lib().orc_silu_mul_quant_experts(_p(gu, _u16p), E, M, I, _p(mm, _i32p), _p(gi, _f32p), _p(codes, _u8p),
+                                      _p(scales, _u8p), _p(h, _f32p))
+    return codes, scales, h
 
 
 # -- MLP -------------------------------------------------------------------

@@ -47,6 +47,14 @@
  *    quantized with g_inv_t, and the GEMM output of token t scaled by
  *    fl(g_t * g_w). A row of zeros has g_t = 0 and quantizes with g_inv = 0
  *    to zero codes and scales (the pages do not say; this keeps it finite).
+ *  - Standalone SiLU(gate) * up + NVFP4 quantization of a bf16 gate_up
+ *    output batched by expert with `masked_m`
+ *    (`silu_and_mul_scaled_nvfp4_experts_quantize(gate_up.unsqueeze(0),
+ *    masked_m, down_proj.input_scale_inv.reshape(1))`, sglang PR #34859
+ *    digest, key source snippets, qwen2_moe.py `_silu_fp4_quant_fused`):
+ *    gate_up is [E, M, 2I] bf16, expert e's first masked_m[e] rows are
+ *    valid and quantized with that expert's inverse global scale; the
+ *    reading used here leaves the rows past masked_m[e] unwritten.
  *
  * Arithmetic conventions:
  *  - Encoding steps are binary32 operations with round-to-nearest-even,
@@ -462,4 +470,30 @@ ORC_API int orc_num_threads(void) {
 #else
   return 1;
 #endif
+}
+
+/* Standalone SiLU(gate) * up + NVFP4 quantization by expert:
+ *   gate_up bf16 [E, M, 2I] (row = [gate | up]), masked_m[E] valid rows per
+ *   expert, g_inv[E] inverse global scale per expert.
+ *   For e < E, t < masked_m[e]:  h = SwiGLU(fp32(gate_up[e, t]))  (fp32 [I]),
+ *   then NVFP4(h) with g_inv[e] into codes [E, M, I/2], scales [E, M, I/16].
+ *   Rows t >= masked_m[e] are left as they are. h_out (NULL to skip) gets h
+ *   of the written rows, [E, M, I]. */
+ORC_API void orc_silu_mul_quant_experts(const uint16_t* gate_up, int64_t E, int64_t M, int64_t I,
+                                        const int32_t* masked_m, const float* g_inv, uint8_t* codes,
+                                        uint8_t* scales, float* h_out) {
+  float* gu = (float*)malloc(sizeof(float) * (size_t)(2 * I));
+  float* h = (float*)malloc(sizeof(float) * (size_t)I);
+  for (int64_t e = 0; e < E; ++e) {
+    int64_t rows = masked_m[e] < 0 ? 0 : (masked_m[e] > M ? M : masked_m[e]);
+    for (int64_t t = 0; t < rows; ++t) {
+      const int64_t row = e * M + t;
+      for (int64_t k = 0; k < 2 * I; ++k) gu[k] = orc_bf16_to_f32(gate_up[row * 2 * I + k]);
+      orc_swiglu(gu, 1, I, h);
+      orc_quantize(h, 1, I, g_inv[e], codes + row * (I / 2), scales + row * (I / 16));
+      if (h_out) memcpy(h_out + row * I, h, sizeof(float) * (size_t)I);
+    }
+  }
+  free(gu);
+  free(h);
 }

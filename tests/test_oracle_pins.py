@@ -459,3 +459,80 @@ def test_mlp_per_token_single_row_equals_static(orc):
         s = orc.mlp_w4a4(x[t:t + 1], wguc, wgus, orc.alpha(g1, ggu), wdc, wds, a_d, g1_inv, g2_inv)
         assert np.array_equal(r["out"][t:t + 1], s["out"])
         assert np.array_equal(r["xq"][t:t + 1], s["xq"]) and np.array_equal(r["hq"][t:t + 1], s["hq"])
+
+
+# -- standalone SiLU(gate) * up + NVFP4 quantize by expert (masked_m) --------
+
+def _bf16(a):
+    return synth.f32_to_bf16_bits(np.asarray(a, np.float32))
+
+
+def test_silu_quant_rows_past_masked_m_untouched(orc):
+    """Rows t >= masked_m[e] keep what the outputs held (masked_m clamped to
+    [0, M]); the other rows are written."""
+    rng = np.random.default_rng(21)
+    E, M, I = 4, 6, 64
+    gu = _bf16(rng.standard_normal((E, M, 2 * I)) * 2)
+    mm = np.array([0, 3, 9, -2], np.int32)
+    sc = np.full((E, M, I // 2), 0xAB, np.uint8)
+    ss = np.full((E, M, I // 16), 0xAB, np.uint8)
+    c, s, h = orc.silu_mul_quant_experts(gu, mm, np.ones(E, np.float32), sc, ss)
+    for e, rows in enumerate([0, 3, 6, 0]):
+        assert np.all(c[e, rows:] == 0xAB) and np.all(s[e, rows:] == 0xAB)
+        assert np.all(np.isnan(h[e, rows:])) and not np.any(np.isnan(h[e, :rows]))
+        assert not np.all(s[e, :rows] == 0xAB) if rows else True
+
+
+def test_silu_mul_closed_forms(orc):
+    """SiLU(g) * u against closed forms: g = 0 or u = 0 gives 0; g = 30 gives
+    30 u (sigmoid(30) = 1 - 9.4e-14, below half an ulp of the exact 30 u);
+    the gate is the first half of the row (swapping halves breaks the 30 u
+    case); h(g, u) - h(-g, u) = g u up to the two fp32 roundings."""
+    rng = np.random.default_rng(22)
+    I = 64
+    u = _bf16(rng.standard_normal(I))
+    g = _bf16(rng.standard_normal(I) * 3)
+    uf, gf = synth.bf16_bits_to_f32(u), synth.bf16_bits_to_f32(g)
+    rows = np.stack([
+        np.concatenate([_bf16(np.zeros(I)), u]),       # g = 0
+        np.concatenate([g, _bf16(np.zeros(I))]),       # u = 0
+        np.concatenate([_bf16(np.full(I, 30.0)), u]),  # g = 30
+        np.concatenate([g, u]),
+        np.concatenate([g ^ np.uint16(0x8000), u]),    # -g
+    ])[None]
+    _, _, h = orc.silu_mul_quant_experts(rows, np.array([5], np.int32), np.ones(1, np.float32))
+    h = h[0].astype(np.float64)
+    assert np.all(h[0] == 0) and np.all(h[1] == 0)
+    assert np.array_equal(h[2], (30.0 * uf).astype(np.float32).astype(np.float64))
+    ulp = np.spacing(np.abs(h[3]).astype(np.float32)).astype(np.float64) + \
+        np.spacing(np.abs(h[4]).astype(np.float32)).astype(np.float64)
+    assert np.all(np.abs(h[3] - h[4] - gf.astype(np.float64) * uf) <= ulp)
+
+
+def test_silu_quant_expert_scale_power_of_two(orc):
+    """The same rows under g_inv and 2 g_inv: identical codes, and every
+    normal, non-saturating scale byte one exponent step (+8) higher: each
+    expert uses its own g_inv."""
+    rng = np.random.default_rng(23)
+    M, I = 8, 256
+    gu1 = _bf16(rng.standard_normal((1, M, 2 * I)) * 4)
+    gu = np.concatenate([gu1, gu1])
+    c, s, h = orc.silu_mul_quant_experts(gu, np.array([M, M], np.int32), np.array([0.75, 1.5], np.float32))
+    assert np.array_equal(c[0], c[1]) and np.array_equal(h[0], h[1])
+    exp0 = (s[0] >> 3) & 15
+    ok = (exp0 >= 1) & (s[0] <= 0x76)
+    assert ok.sum() > 100
+    assert np.array_equal(s[1][ok], s[0][ok] + 8)
+
+
+def test_silu_quant_codes_are_the_quantizer_of_h(orc):
+    """Each written row's codes and scales are the quantizer's output for
+    that row's h with its expert's g_inv."""
+    rng = np.random.default_rng(24)
+    E, M, I = 2, 3, 128
+    gu = _bf16(rng.standard_normal((E, M, 2 * I)) * 2)
+    gi = np.array([0.5, 3.0], np.float32)
+    c, s, h = orc.silu_mul_quant_experts(gu, np.array([M, 2], np.int32), gi)
+    for e, rows in enumerate([M, 2]):
+        qc, qs = orc.quantize(h[e, :rows], gi[e])
+        assert np.array_equal(c[e, :rows], qc) and np.array_equal(s[e, :rows], qs)
