@@ -164,7 +164,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default="decode_w4a4", choices=list(WORKLOADS))
+    ap.add_argument("--workload", default="decode_w4a4", choices=list(WORKLOADS) + ["silu_quant"])
     ap.add_argument("--M", type=int, default=None, help="override the token count")
     ap.add_argument("--copies", type=int, default=None, help="weight copies rotated (default >= 1 GB)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
@@ -193,6 +193,9 @@ def main():
               "(this build has no multi-GPU path; see the sharding notes in DESIGN.md)")
         sys.exit(2)
 
+    if args.workload == "silu_quant":
+        print(json.dumps(run_silu_quant(args)), flush=True)
+        return
     M0, H, I, mode, outliers, n_seeds0, d_steps, d_warm = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     nv.set_path(args.path)
@@ -353,6 +356,76 @@ def run_one(args, dev, M, H, I, mode, outliers, n_seeds, steps, warmup, copies, 
         "cpu_baseline": cpu,
     }
     return res
+
+
+def run_silu_quant(args):
+    """The standalone SiLU(gate) * up + NVFP4 quantize of a bf16 gate_up (one
+    expert, all rows valid): M tokens (default 8192) of intermediate 18432,
+    the prefill MLP's h. HBM-bound: 4 bytes read and 0.5625 written per
+    output element. A step is one call; inputs rotate over copies of >= 1 GB
+    so the last-level cache cannot serve them."""
+    dev = torch.device("cuda:0")
+    M = args.M if args.M is not None else 8192
+    I = 18432
+    per_bytes = M * I * (4 + NVFP4_BYTES)
+    copies = max(2, int(np.ceil(1.0e9 / (M * I * 4))))
+    steps = args.steps if args.steps is not None else 200
+    warmup = args.warmup if args.warmup is not None else 10
+    log(f"[bench] workload silu_quant M={M} I={I} copies={copies} steps={steps} warmup={warmup}")
+    x = synth.activations(0, M, 2 * I)
+    gus = [bf16_tensor(x, dev).reshape(1, M, 2 * I)]
+    for _ in range(copies - 1):
+        gus.append(gus[0].clone())
+    g_inv = torch.tensor([np.float32(0.05)], device=dev)
+    mm = torch.tensor([M], dtype=torch.int32, device=dev)
+    codes = torch.empty((1, M, I // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((1, M, I // 16), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        nv.silu_mul_nvfp4_quant(gus[i % copies], g_inv, mm, codes=codes, scales=scales, stream=stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    k_us = e0.elapsed_time(e1) * 1e3 / steps
+    ms_per_step = dt * 1e3 / steps
+    achieved = per_bytes / (k_us * 1e-6) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        rows = 8
+        sub = x[:rows].reshape(1, rows, 2 * I)
+        n, t1 = 0, time.perf_counter()
+        while time.perf_counter() - t1 < args.cpu_budget:
+            oracle.silu_mul_quant_experts(sub, np.array([rows], np.int32), np.array([0.05], np.float32))
+            n += 1
+        cdt = time.perf_counter() - t1
+        cpu = {"value": per_bytes * rows / M * n / cdt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"{n} calls on {rows} of {M} rows, {cdt:.1f} s, scaled to algorithmic bytes"}
+    return {
+        "metric": "NVFP4 MLP TFLOPS + GB/s (% roofline), decode M=1..16 and prefill M=8192",
+        "value": per_bytes / (ms_per_step * 1e-3) / 1e9, "unit": "GB/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"silu_quant E=1 M={M} I={I}", "M": M, "intermediate": I, "experts": 1,
+                   "input_copies": copies},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "k_silu_mul_quant",
+                     "kernel_us": k_us, "launches_timed": steps, "algorithmic_bytes": per_bytes},
+        "cpu_baseline": cpu,
+    }
 
 
 if __name__ == "__main__":

@@ -238,6 +238,26 @@ int mlp_forward(int mode, const uint16_t* x, int64_t M, int64_t H, int64_t I,
                 const float* alpha_d, const float* g1_inv, const float* g2_inv, void* ws,
                 size_t ws_bytes, void* out, int out_dtype, void* stream);
 
+/*
+ * Standalone SiLU(gate) * up + NVFP4 quantization of a bf16 gate_up output
+ * batched by expert, `silu_and_mul_scaled_nvfp4_experts_quantize(gate_up,
+ * masked_m, input_scale_inv)` as the PR #34859 digest calls it (key source
+ * snippets, qwen2_moe.py `_silu_fp4_quant_fused`, with one expert for a dense
+ * MLP): for expert e and row t < masked_m[e]
+ *   h = SiLU(gate) * up in fp32 (gate = first I columns of the row),
+ *   codes/scales of the row = NVFP4(h) with g_inv[e] as nvfp4_quantize does.
+ * gate_up: bf16 [E, M, 2I] row-major, 16-byte aligned, I % 16 == 0.
+ * masked_m: device int32 [E], rows of expert e to process (clamped to
+ *   [0, M]); NULL processes all M rows of every expert.
+ * g_inv: device fp32 [E], inverse global scale per expert.
+ * codes: [E, M, I/2] out (16-byte aligned); scales: [E, M, I/16] out
+ *   (linear, one E4M3 byte per 16 elements). Rows past masked_m[e] are not
+ *   written. Errors: NVFP4_ERR_INVALID_ARG for bad sizes, alignment or null
+ *   pointers (nothing launched).
+ */
+int silu_mul_nvfp4_quant(const void* gate_up, int64_t E, int64_t M, int64_t I, const int32_t* masked_m,
+                         const float* g_inv, uint8_t* codes, uint8_t* scales, void* stream);
+
 /* Select the kernel class used by the GEMM entry points (NVFP4_PATH_*).
  * Process-wide; meant for tests and benchmarks. Returns the previous value,
  * or NVFP4_ERR_INVALID_ARG. */

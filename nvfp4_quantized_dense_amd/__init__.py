@@ -44,6 +44,7 @@ SIGNATURES = {
     "gemm_swiglu_nvfp4_quant_rowscale": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp,
                                                 _vp, _vp]),
     "gemm_swiglu": (_int, [_int, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _int, _vp]),
+    "silu_mul_nvfp4_quant": (_int, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp]),
     "mlp_workspace_bytes": (_sz, [_int, _i64, _i64, _i64]),
     "mlp_forward": (_int, [_int, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                            _vp, _int, _vp]),
@@ -247,6 +248,24 @@ def gemm_swiglu(mode, a, a_scales, w_gu_packed, I, K, alpha, h=None, h_dtype=tor
     _check("gemm_swiglu", lib().gemm_swiglu(int(mode), _ptr(a), _ptr(a_scales), _ptr(w_gu_packed), M, I, K,
                                             _ptr(alpha), _ptr(h), _dtype_code(h.dtype), _stream(stream)))
     return h
+
+
+def silu_mul_nvfp4_quant(gate_up, g_inv, masked_m=None, codes=None, scales=None, stream=None):
+    """gate_up bf16 [E, M, 2I] (or [M, 2I] as one expert) -> (codes [E, M, I/2],
+    scales [E, M, I/16]) of SiLU(gate) * up, expert e quantized with g_inv[e];
+    rows t >= masked_m[e] (int32 device tensor [E]) are not written."""
+    _dense(gate_up, "gate_up")
+    gu = gate_up if gate_up.dim() == 3 else gate_up.unsqueeze(0)
+    E, M, I2 = gu.shape
+    I = I2 // 2
+    if codes is None:
+        codes = torch.zeros((E, M, I // 2), dtype=torch.uint8, device=gu.device)
+    if scales is None:
+        scales = torch.zeros((E, M, I // 16), dtype=torch.uint8, device=gu.device)
+    _check("silu_mul_nvfp4_quant",
+           lib().silu_mul_nvfp4_quant(_ptr(gu), E, M, I, _ptr(masked_m), _ptr(g_inv), _ptr(codes), _ptr(scales),
+                                      _stream(stream)))
+    return codes, scales
 
 
 def mlp_workspace_bytes(mode, M, H, I) -> int:

@@ -301,6 +301,23 @@ int nvfp4_quantize_per_token(const void* x, int x_dtype, int64_t M, int64_t K, u
                     "quantize_per_token launch");
 }
 
+int silu_mul_nvfp4_quant(const void* gate_up, int64_t E, int64_t M, int64_t I, const int32_t* masked_m,
+                         const float* g_inv, uint8_t* codes, uint8_t* scales, void* stream) {
+  if (E < 0 || M < 0 || E >= 65536 || M >= 65536 || !dim_ok(I) || I < 0 || I % 16 != 0)
+    return fail(NVFP4_ERR_INVALID_ARG, "need 0 <= E, M < 65536 and I a multiple of 16 (E=%lld M=%lld I=%lld)",
+                (long long)E, (long long)M, (long long)I);
+  if (E * M * I == 0) { g_err[0] = '\0'; return NVFP4_OK; }
+  if (!gate_up || !g_inv || !codes || !scales) return fail(NVFP4_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(gate_up) || !aligned16(codes) || reinterpret_cast<uintptr_t>(g_inv) % 4 ||
+      reinterpret_cast<uintptr_t>(masked_m) % 4)
+    return fail(NVFP4_ERR_INVALID_ARG, "gate_up and codes must be 16-byte aligned, g_inv and masked_m 4-byte");
+  int st = check_device();
+  if (st) return st;
+  return hip_status(nvfp4::launch_silu_mul_quant(gate_up, E, M, I, masked_m, g_inv, codes, scales,
+                                                 as_stream(stream)),
+                    "silu_mul_nvfp4_quant launch");
+}
+
 size_t nvfp4_packed_bytes(int kind, int64_t R, int64_t C) {
   if (kind != NVFP4_REPACK_PLAIN && kind != NVFP4_REPACK_SWIGLU) return 0;
   if (R <= 0 || C <= 0 || R % 16 != 0 || C % 256 != 0 || R > kMaxDim || C > kMaxDim) return 0;

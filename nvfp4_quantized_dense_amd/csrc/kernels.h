@@ -23,6 +23,12 @@ hipError_t launch_quantize(const void* x, bool f32_in, int64_t M, int64_t K, con
 hipError_t launch_quantize_per_token(const void* x, bool f32_in, int64_t M, int64_t K, uint8_t* codes,
                                      uint8_t* scales, float* row_g, hipStream_t s);
 
+// silu_quant.hip: SiLU(gate) * up of a bf16 gate_up [E, M, 2I] quantized
+// to NVFP4 with g_inv[e], rows t < masked_m[e] (all rows if masked_m is
+// null); grid (I / 2048, M, E) within the launch limits (M, E < 65536).
+hipError_t launch_silu_mul_quant(const void* gate_up, int64_t E, int64_t M, int64_t I, const int32_t* masked_m,
+                                 const float* g_inv, uint8_t* codes, uint8_t* scales, hipStream_t s);
+
 // repack.hip
 hipError_t launch_repack(int kind, const uint8_t* codes, const uint8_t* scales, int64_t R,
                          int64_t C, uint8_t* packed, bool unpack, uint8_t* out_codes,

@@ -102,6 +102,12 @@ def test_invalid_arguments_are_rejected_on_the_host():
     assert lib.mlp_forward(2, P, 4, 256, 512, P, P, P, P, P, P, P, ws, P, 1, N) == INV  # DYN + g1
     assert b"per token" in lib.nvfp4_last_error()
     assert lib.mlp_forward(2, P, 4, 256, 512, P, P, P, P, N, N, P, ws, P, 1, N) == INV  # DYN no g2
+    # standalone SiLU * mul + NVFP4 quantize
+    assert lib.silu_mul_nvfp4_quant(P, 1, 4, 24, N, P, P, P, N) == INV        # I % 16
+    assert lib.silu_mul_nvfp4_quant(P, 1, 70000, 32, N, P, P, P, N) == INV    # M too large
+    assert lib.silu_mul_nvfp4_quant(P, 1, 4, 32, N, N, P, P, N) == INV        # null g_inv
+    assert lib.silu_mul_nvfp4_quant(U, 1, 4, 32, N, P, P, P, N) == INV        # misaligned gate_up
+    assert lib.silu_mul_nvfp4_quant(N, 0, 4, 32, N, N, N, N, N) == nv.NVFP4_OK  # empty
     assert lib.nvfp4_set_path(9) == INV
 
 
