@@ -65,6 +65,27 @@ __device__ __forceinline__ uint32_t e2m1_from_f32(float y) {
   return c | ((__float_as_uint(y) >> 28) & 8u);
 }
 
+// Pairs of fp32 values to E2M1 codes with the hardware conversion (unit
+// scale): round to nearest even, saturating at 6, sign kept, exactly the
+// rules of e2m1_from_f32 (checked on the GPU against it on every tie, the
+// neighbours of every tie and grid point, a dense sweep of [-8, 8], zeros,
+// subnormals and values far past 6). The first of a pair goes to the low
+// nibble; pair k fills byte k.
+__device__ __forceinline__ uint32_t e2m1_pack8(const float (&y)[8]) {
+  uint32_t w = 0;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[0], y[1], 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[2], y[3], 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[4], y[5], 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[6], y[7], 1.0f, 3);
+  return w;
+}
+__device__ __forceinline__ uint32_t e2m1_pack4(float y0, float y1, float y2, float y3) {
+  uint32_t w = 0;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y0, y1, 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y2, y3, 1.0f, 1);
+  return w;
+}
+
 // One NVFP4 block: scale byte and the per-element multiplier r = g_inv / s.
 struct BlockScale {
   uint32_t byte;
@@ -323,8 +344,7 @@ __device__ __forceinline__ SwigluBlock swiglu_nvfp4(const f32x4& gate, const f32
   amax = __builtin_fmaxf(amax, __shfl_xor(amax, 32));
   BlockScale bs = block_scale(amax, g2_inv);
   SwigluBlock b;
-  b.codes = e2m1_from_f32(h[0] * bs.r) | (e2m1_from_f32(h[1] * bs.r) << 4) |
-            (e2m1_from_f32(h[2] * bs.r) << 8) | (e2m1_from_f32(h[3] * bs.r) << 12);
+  b.codes = e2m1_pack4(h[0] * bs.r, h[1] * bs.r, h[2] * bs.r, h[3] * bs.r);
   b.scale = bs.byte;
   return b;
 }

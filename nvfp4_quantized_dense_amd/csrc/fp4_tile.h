@@ -257,9 +257,10 @@ __device__ __forceinline__ void f4_gemv_acc(const GemmArgs& args, int64_t rg0, i
           for (int k = 0; k < 8; ++k) mx = max(mx, __float_as_uint(e[k]) & 0x7FFFFFFFu);
           mx = max(mx, (uint32_t)__shfl_xor((int)mx, 1));
           const BlockScale bs = block_scale(__uint_as_float(mx), gi);
-          uint32_t packed = 0;
+          float y[8];
 #pragma unroll
-          for (int k = 0; k < 8; ++k) packed |= e2m1_from_f32(e[k] * bs.r) << (4 * k);
+          for (int k = 0; k < 8; ++k) y[k] = e[k] * bs.r;
+          const uint32_t packed = e2m1_pack8(y);
           if (i < xchunks) {
             const int m = i / row8, j = i - m * row8;
             *reinterpret_cast<uint32_t*>(xl + m * Ki / 2 + t0 * 128 + 4 * j) = packed;

@@ -41,9 +41,10 @@ __global__ __launch_bounds__(256) void k_quantize(const void* __restrict__ x, in
   for (int i = 0; i < 8; ++i) m = max(m, __float_as_uint(v[i]) & 0x7FFFFFFFu);
   m = max(m, (uint32_t)__shfl_xor((int)m, 1));
   const BlockScale bs = block_scale(__uint_as_float(m), *g_inv_p);
-  uint32_t packed = 0;
+  float y[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) packed |= e2m1_from_f32(v[i] * bs.r) << (4 * i);
+  for (int i = 0; i < 8; ++i) y[i] = v[i] * bs.r;
+  const uint32_t packed = e2m1_pack8(y);
   if (live) {
     codes[t] = packed;
     if ((t & 1) == 0) scales[t >> 1] = (uint8_t)bs.byte;
@@ -102,9 +103,10 @@ __global__ __launch_bounds__(256) void k_quantize_per_token(const void* __restri
     for (int i = 0; i < 8; ++i) bm = max(bm, __float_as_uint(v[i]) & 0x7FFFFFFFu);
     bm = max(bm, (uint32_t)__shfl_xor((int)bm, 1));
     const BlockScale bs = block_scale(__uint_as_float(bm), g_inv);
-    uint32_t packed = 0;
+    float y[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) packed |= e2m1_from_f32(v[i] * bs.r) << (4 * i);
+    for (int i = 0; i < 8; ++i) y[i] = v[i] * bs.r;
+    const uint32_t packed = e2m1_pack8(y);
     codes[row * n8 + c] = packed;
     if ((c & 1) == 0) scales[row * (K / 16) + (c >> 1)] = (uint8_t)bs.byte;
   }

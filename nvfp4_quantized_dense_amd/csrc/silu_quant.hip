@@ -8,7 +8,7 @@
 // chunks of the gate and up halves; chunks 2b and 2b + 1 (neighbouring
 // lanes) form 16-block b and exchange their amax. The SiLU * mul and the
 // block encoder are the ones of the fused GEMM epilogue (silu_mul,
-// block_scale, e2m1_from_f32), so the codes match the fused path's for the
+// block_scale, e2m1_pack8), so the codes match the fused path's for the
 // same fp32 h. Rows past masked_m are skipped by whole workgroups.
 #include "device_common.h"
 #include "kernels.h"
@@ -32,9 +32,10 @@ __device__ __forceinline__ void silu_quant_chunk(const u32x4& gw, const u32x4& u
   for (int i = 0; i < 8; ++i) m = max(m, __float_as_uint(h[i]) & 0x7FFFFFFFu);
   m = max(m, (uint32_t)__shfl_xor((int)m, 1));
   const BlockScale bs = block_scale(__uint_as_float(m), gi);
-  uint32_t packed = 0;
+  float y[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) packed |= e2m1_from_f32(h[i] * bs.r) << (4 * i);
+  for (int i = 0; i < 8; ++i) y[i] = h[i] * bs.r;
+  const uint32_t packed = e2m1_pack8(y);
   if (live) {
     codes[c] = packed;
     if ((c & 1) == 0) scales[c >> 1] = (uint8_t)bs.byte;
