@@ -153,8 +153,6 @@ hipError_t run_gemm(int path, int mode, int epi, const nvfp4::GemmArgs& a, hipSt
 // wave. (At M = 16 on hidden 5120: W4A4 down 21.2 -> 19-20 us, W4A16 40.8 ->
 // 30.7 us. The decode GEMVs measured no gain from it and do not split.)
 constexpr int64_t kSplitTargetWaves = 8192;
-// The W4A16 tiled kernel splits K below this many output tiles (the CU count).
-constexpr int64_t kTiledSplitBelow = 256;
 
 struct SplitPlan {
   int ways = 1;
@@ -162,38 +160,50 @@ struct SplitPlan {
   size_t part_bytes = 0, counter_bytes = 0;
 };
 
-SplitPlan split_plan(Kernel k, int mode, int64_t M, int64_t N, int64_t K) {
+// Tail split of a tiled kernel's grid: when its last round of one
+// workgroup per CU is at most half full, the tail tiles are K-split into as
+// many splits as fill that round (at most 8, at least min_tiles K tiles
+// each).
+static SplitPlan tail_split(const nvfp4::TileShape& ts, int64_t K, int64_t min_tiles) {
+  SplitPlan p;
+  const int64_t tail = nvfp4::tiled_tail(ts.units), T = K / 256;
+  if (tail == 0 || 2 * tail > nvfp4::kTiledSlots) return p;
+  int64_t ks = std::min<int64_t>(nvfp4::kTiledSlots / tail, 8);
+  while (ks > 1 && ((ks - 1) * ((T + ks - 1) / ks) >= T || (T + ks - 1) / ks < min_tiles)) --ks;
+  if (ks <= 1) return p;
+  p.ways = (int)ks;
+  p.units = tail;
+  p.part_bytes = align256((size_t)(tail * ks * ts.tile_floats) * sizeof(float));
+  p.counter_bytes = align256((size_t)tail * sizeof(uint32_t));
+  return p;
+}
+
+// Split-K plan of a GEMM of mlp_forward (swiglu: the gate_up GEMM).
+SplitPlan split_plan(Kernel k, int mode, int64_t M, int64_t N, int64_t K, bool swiglu) {
   SplitPlan p;
   if (M <= 0) return p;
   (void)mode;
-  if (k == kTiled2) {
-    // The W4A4 tiled kernel splits only the tiles of a last round that is
-    // at most half full (one workgroup per CU): into as many K splits as
-    // fill that round, at least 8 K tiles each.
-    const nvfp4::TileShape ts = nvfp4::tiled2_shape(M, N);
-    const int64_t tail = nvfp4::tiled2_tail(ts.units), T = K / 256;
-    if (tail == 0 || 2 * tail > nvfp4::kTiled2Slots) return p;
-    int64_t ks = std::min<int64_t>(nvfp4::kTiled2Slots / tail, 8);
-    while (ks > 1 && ((ks - 1) * ((T + ks - 1) / ks) >= T || (T + ks - 1) / ks < 8)) --ks;
-    if (ks <= 1) return p;
-    p.ways = (int)ks;
-    p.units = tail;
-    p.part_bytes = align256((size_t)(tail * ks * ts.tile_floats) * sizeof(float));
-    p.counter_bytes = align256((size_t)tail * sizeof(uint32_t));
+  // The W4A4 tiled kernel: the tail tiles, at least 8 K tiles per split.
+  if (k == kTiled2) return tail_split(nvfp4::tiled2_shape(M, N), K, 8);
+  if (k == kTiled16) {
+    // The W4A16 tiled kernel (one 8-wave workgroup per CU): a grid of less
+    // than one round (dense epilogues: the down projection at a few hundred
+    // tokens) to about 2 workgroups per CU, at least 4 K tiles per split;
+    // a larger grid in its tail tiles (the gate_up at 256 tokens: 272 tiles).
+    const nvfp4::TileShape ts = nvfp4::tiled16_shape(M, N);
+    if (ts.units >= nvfp4::kTiledSlots) return tail_split(ts, K, 4);
+    if (swiglu) return p;
+    p.ways = nvfp4::splitk_ways(ts.units, K / 256, 2 * nvfp4::kTiledSlots, 4);
+    if (p.ways > 1) {
+      p.units = ts.units;
+      p.part_bytes = align256((size_t)(ts.units * p.ways * ts.tile_floats) * sizeof(float));
+      p.counter_bytes = align256((size_t)ts.units * sizeof(uint32_t));
+    }
     return p;
   }
-  if (k != kStream && k != kTiled16) return p;
-  nvfp4::TileShape ts;
-  if (k == kStream) {
-    ts = nvfp4::stream_shape(M, N);
-    p.ways = nvfp4::splitk_ways(ts.units, K / 256, kSplitTargetWaves / ts.waves, ts.waves);
-  } else {
-    // The W4A16 tiled kernel (one 8-wave workgroup per CU) splits only
-    // grids of less than one workgroup per CU: to about 2 per CU, at least
-    // 4 K tiles per split (the down projection at a few hundred tokens).
-    ts = nvfp4::tiled16_shape(M, N);
-    p.ways = ts.units < kTiledSplitBelow ? nvfp4::splitk_ways(ts.units, K / 256, 2 * kTiledSplitBelow, 4) : 1;
-  }
+  if (k != kStream || swiglu) return p;
+  const nvfp4::TileShape ts = nvfp4::stream_shape(M, N);
+  p.ways = nvfp4::splitk_ways(ts.units, K / 256, kSplitTargetWaves / ts.waves, ts.waves);
   if (p.ways > 1) {
     p.units = ts.units;
     p.part_bytes = align256((size_t)(ts.units * p.ways * ts.tile_floats) * sizeof(float));
@@ -460,8 +470,11 @@ static size_t decode_bytes(int64_t H, int64_t I) {
 static size_t mlp_split_bytes(int mode, int64_t M, int64_t H, int64_t I, bool decode) {
   size_t most = 0;
   for (int path : {NVFP4_PATH_GEMV, NVFP4_PATH_STREAM, NVFP4_PATH_TILED}) {
-    const SplitPlan p = split_plan(mlp_kernel(path, mode, M, H, I), mode, M, H, I);
-    most = std::max(most, p.part_bytes + p.counter_bytes);
+    // The two GEMMs share the partials region (they run one after the
+    // other) and have counters of their own.
+    const SplitPlan d = split_plan(mlp_kernel(path, mode, M, H, I), mode, M, H, I, false);
+    const SplitPlan g = split_plan(mlp_kernel(path, mode, M, 2 * I, H), mode, M, 2 * I, H, true);
+    most = std::max(most, std::max(d.part_bytes, g.part_bytes) + d.counter_bytes + g.counter_bytes);
   }
   if (decode && M == 1 && nvfp4::decode_supported(H, I)) most = std::max(most, decode_bytes(H, I));
   return most;
@@ -511,22 +524,36 @@ int mlp_forward(int mode, const uint16_t* x, int64_t M, int64_t H, int64_t I, co
   uint8_t* base = static_cast<uint8_t*>(ws);
   const size_t m = static_cast<size_t>(M);
 
-  // Split-K of the down projection (partials and counters after the
-  // activations); the gate_up kernel clears the counters before it runs.
+  // Split-K (partials, then the counters of the down projection, then those
+  // of the gate_up GEMM, after the activations). The gate_up's first launch
+  // clears both counter sets before it runs (a split gate_up runs its whole
+  // rounds first and its K-split tail tiles in a second launch); every split
+  // GEMM also leaves its counters at zero.
   const Kernel k_gu = mlp_kernel(path, mode, M, 2 * I, H);
   const Kernel k_d = mlp_kernel(path, mode, M, H, I);
-  SplitPlan sp = split_plan(k_d, mode, M, H, I);
+  SplitPlan sp = split_plan(k_d, mode, M, H, I, false);
+  SplitPlan sg = split_plan(k_gu, mode, M, 2 * I, H, true);
   if (!clears_counters(k_gu)) sp = SplitPlan{};
+  if (!clears_counters(k_d)) sg = SplitPlan{};
   uint8_t* split_base = base + mlp_act_bytes(dyn ? NVFP4_MODE_W4A4_DYN : mode, m, H, I);
   float* part = reinterpret_cast<float*>(split_base);
-  uint32_t* counters = reinterpret_cast<uint32_t*>(split_base + sp.part_bytes);
+  uint32_t* counters = reinterpret_cast<uint32_t*>(split_base + std::max(sp.part_bytes, sg.part_bytes));
+  uint32_t* counters_gu = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(counters) + sp.counter_bytes);
   auto with_split = [&](nvfp4::GemmArgs& gu, nvfp4::GemmArgs& dn) {
-    if (sp.ways <= 1) return;
-    gu.zero_ptr = counters;
-    gu.zero_n = (int)sp.units;
-    dn.part = part;
-    dn.counters = counters;
-    dn.ksplit = sp.ways;
+    if (sp.ways > 1 || sg.ways > 1) {
+      gu.zero_ptr = counters;
+      gu.zero_n = (int)((sp.counter_bytes + sg.counter_bytes) / sizeof(uint32_t));
+    }
+    if (sp.ways > 1) {
+      dn.part = part;
+      dn.counters = counters;
+      dn.ksplit = sp.ways;
+    }
+    if (sg.ways > 1) {
+      gu.part = part;
+      gu.counters = counters_gu;
+      gu.ksplit = sg.ways;
+    }
   };
 
   hipError_t e;

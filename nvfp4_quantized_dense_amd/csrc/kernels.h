@@ -71,13 +71,14 @@ struct GemmArgs {
   const float* a_g_inv = nullptr;
 };
 
-// Split-K is valid for the dense epilogues, with the buffers given and every
-// split non-empty: tiles per split ceil(T / ksplit), (ksplit - 1) of them
-// fewer than T.
-inline bool splitk_valid(const GemmArgs& a, int epi) {
+// Split-K is valid with the buffers given and every split non-empty: tiles
+// per split ceil(T / ksplit), (ksplit - 1) of them fewer than T; for the
+// dense epilogues, or any epilogue where the kernel combines the partial
+// sums before it (the tiled kernels: swiglu_ok).
+inline bool splitk_valid(const GemmArgs& a, int epi, bool swiglu_ok = false) {
   if (a.ksplit == 1) return true;
   const int64_t T = a.K / 256, per = (T + a.ksplit - 1) / a.ksplit;
-  return a.ksplit > 1 && (epi == kOutF32 || epi == kOutBF16) && a.part && a.counters &&
+  return a.ksplit > 1 && (swiglu_ok || epi == kOutF32 || epi == kOutBF16) && a.part && a.counters &&
          (a.ksplit - 1) * per < T;
 }
 // Launch shape of the weight-streaming kernel's dense GEMM: output tiles
@@ -110,16 +111,22 @@ bool fp4_gemv_supported(int64_t M, int64_t K);
 hipError_t launch_fp4_gemv(int epi, const GemmArgs& a, hipStream_t s);
 hipError_t launch_tiled_gemm(int mode, int epi, const GemmArgs& a, hipStream_t s);
 
+// The tiled kernels run one workgroup per CU, so output tiles go in rounds
+// of kTiledSlots; tiled_tail(units) is the tile count of the last, partial
+// round of a grid of more than one round (0 if none).
+constexpr int64_t kTiledSlots = 256;
+inline int64_t tiled_tail(int64_t units) { return units > kTiledSlots ? units % kTiledSlots : 0; }
+
 // W4A4 only; packed weight, activation codes and scales each < 2^31 bytes.
-// With ksplit > 1 (dense epilogues) only the tiles of the last, partial
-// round of one workgroup per CU are K-split: tiled2_tail(units) of them,
-// which must be nonzero; part and counters are sized for those.
+// With ksplit > 1 only the tiles of the last, partial round are K-split:
+// tiled_tail(units) of them, which must be nonzero; part and counters are
+// sized for those (any epilogue: the partials are combined before it).
 hipError_t launch_tiled2_gemm(int epi, const GemmArgs& a, hipStream_t s);
 TileShape tiled2_shape(int64_t M, int64_t N);
-constexpr int64_t kTiled2Slots = 256;  // workgroups resident at once: one per CU
-inline int64_t tiled2_tail(int64_t units) { return units > kTiled2Slots ? units % kTiled2Slots : 0; }
 // W4A16 only; packed weight and the activation rows (+256 of padding) each
-// < 2^31 bytes.
+// < 2^31 bytes. With ksplit > 1: a grid of less than one round (dense
+// epilogues) splits every tile; a larger one splits only its tiled_tail
+// tiles (any epilogue). part and counters are sized for the split tiles.
 hipError_t launch_tiled16_gemm(int epi, const GemmArgs& a, hipStream_t s);
 
 // decode.hip: the W4A4 MLP forward of one token in one launch (gate_up

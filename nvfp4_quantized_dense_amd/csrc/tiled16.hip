@@ -143,9 +143,11 @@ __device__ __forceinline__ void compute_stage16(f32x4 (&acc)[2][8], const uint8_
 // A separate instantiation: with the combine merely present, the main loop
 // of the unsplit down projection compiled 23% slower (861 against 699 us at
 // 4096 tokens, hidden 5120).
+// This launch covers output tiles [tile0, tile0 + count); with SPLIT each of
+// them as args.ksplit K splits.
 template <int EPI, bool SPLIT>
-__global__ __launch_bounds__(kNW16 * 64, 1) void k_tiled16(GemmArgs args, int64_t n_tiles, int64_t m_tiles,
-                                                           int64_t per_xcd) {
+__global__ __launch_bounds__(kNW16 * 64, 1) void k_tiled16(GemmArgs args, int64_t n_tiles, int64_t per_xcd,
+                                                           int64_t tile0, int64_t count) {
 #if defined(__HIP_DEVICE_COMPILE__)
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage16];
   __shared__ uint32_t arrived;
@@ -153,14 +155,15 @@ __global__ __launch_bounds__(kNW16 * 64, 1) void k_tiled16(GemmArgs args, int64_
   // XCD-aware order: workgroup ids are dealt round-robin to the 8 XCDs, so
   // XCD x takes a contiguous run of output tiles, token-tile-major; its
   // resident workgroups share an activation tile in its L2 while sweeping
-  // weight tiles. With a K split (dense epilogues), the ks splits of an
-  // output tile are consecutive.
+  // weight tiles. With a K split, the ks splits of an output tile are
+  // consecutive.
   const int ks = SPLIT ? args.ksplit : 1;
   const int64_t id = blockIdx.x;
   const int64_t f = (id & 7) * per_xcd + (id >> 3);
-  if (f >= n_tiles * m_tiles * ks) return;
-  const int64_t tile = f / ks;
-  const int split = (int)(f - tile * ks);
+  if (f >= count * ks) return;
+  const int64_t local = f / ks;
+  const int split = (int)(f - local * ks);
+  const int64_t tile = tile0 + local;
   const int64_t m_tile = tile / n_tiles, n_tile = tile % n_tiles;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -198,7 +201,7 @@ __global__ __launch_bounds__(kNW16 * 64, 1) void k_tiled16(GemmArgs args, int64_
     __builtin_amdgcn_s_setprio(0);
   }
   if constexpr (SPLIT) {
-    if (!wg_splitk_last<2, 8, kNW16 * 64>(acc, args.part, args.counters, ks, tile, split, (int)threadIdx.x, &arrived))
+    if (!wg_splitk_last<2, 8, kNW16 * 64>(acc, args.part, args.counters, ks, local, split, (int)threadIdx.x, &arrived))
       return;
   }
 
@@ -227,20 +230,35 @@ TileShape tiled16_shape(int64_t M, int64_t N) {
   return TileShape{n_tiles * m_tiles, kG16 * 16 * kTG16 * 16, kNW16};
 }
 
+template <int EPI, bool SPLIT>
+static hipError_t launch16_range(const GemmArgs& a, int64_t n_tiles, int64_t tile0, int64_t count, int ks,
+                                 hipStream_t s) {
+  const int64_t per_xcd = (count * ks + 7) / 8;
+  k_tiled16<EPI, SPLIT><<<(unsigned)(8 * per_xcd), kNW16 * 64, 0, s>>>(a, n_tiles, per_xcd, tile0, count);
+  return hipGetLastError();
+}
+
 template <int EPI>
 static hipError_t launch16_e(const GemmArgs& a, hipStream_t s) {
-  const int64_t ngroups = a.N / kTileRows;
-  const int64_t n_tiles = (ngroups + kG16 - 1) / kG16;
-  const int64_t m_tiles = (a.M + kTG16 * 16 - 1) / (kTG16 * 16);
-  const int64_t per_xcd = (n_tiles * m_tiles * a.ksplit + 7) / 8;
-  if constexpr (!EpiTraits<EPI>::swiglu) {
-    if (a.ksplit > 1) {
-      k_tiled16<EPI, true><<<(unsigned)(8 * per_xcd), kNW16 * 64, 0, s>>>(a, n_tiles, m_tiles, per_xcd);
-      return hipGetLastError();
+  const int64_t n_tiles = (a.N / kTileRows + kG16 - 1) / kG16;
+  const int64_t units = tiled16_shape(a.M, a.N).units;
+  if (a.ksplit > 1) {
+    // Less than a round (dense epilogues): every tile split. More: the whole
+    // rounds unsplit, then the tail tiles split.
+    if (units < kTiledSlots) {
+      if constexpr (EpiTraits<EPI>::swiglu) return hipErrorInvalidValue;
+      return launch16_range<EPI, true>(a, n_tiles, 0, units, a.ksplit, s);
     }
+    const int64_t tail = tiled_tail(units), whole = units - tail;
+    if (tail == 0) return hipErrorInvalidValue;  // the split buffers are sized for the tail tiles
+    hipError_t e = launch16_range<EPI, false>(a, n_tiles, 0, whole, 1, s);
+    if (e != hipSuccess) return e;
+    GemmArgs t = a;  // counters to clear are cleared by the first launch only
+    t.zero_ptr = nullptr;
+    t.zero_n = 0;
+    return launch16_range<EPI, true>(t, n_tiles, whole, tail, a.ksplit, s);
   }
-  k_tiled16<EPI, false><<<(unsigned)(8 * per_xcd), kNW16 * 64, 0, s>>>(a, n_tiles, m_tiles, per_xcd);
-  return hipGetLastError();
+  return launch16_range<EPI, false>(a, n_tiles, 0, units, 1, s);
 }
 
 // W4A16 only. Needs the packed weight below 2^31 bytes and the activation
@@ -248,7 +266,7 @@ static hipError_t launch16_e(const GemmArgs& a, hipStream_t s) {
 // offsets); the caller checks.
 hipError_t launch_tiled16_gemm(int epi, const GemmArgs& a, hipStream_t s) {
   if (a.M == 0) return hipSuccess;
-  if (!splitk_valid(a, epi)) return hipErrorInvalidValue;
+  if (!splitk_valid(a, epi, true)) return hipErrorInvalidValue;
   switch (epi) {
     case kOutF32: return launch16_e<kOutF32>(a, s);
     case kOutBF16: return launch16_e<kOutBF16>(a, s);

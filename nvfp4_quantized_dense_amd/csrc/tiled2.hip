@@ -21,10 +21,10 @@
 // One workgroup fits a CU (two 72 KB stages of LDS), so output tiles run in
 // rounds of one per CU. When the last round would be at most half full (the
 // down projection at 8192 tokens, hidden 7168: 896 tiles, 3.5 rounds), a
-// dense GEMM given split-K buffers runs the whole rounds in one launch and
-// the tail tiles in a second one with K split over ks workgroups each, so
-// the tail takes 1 / ks of a round (the partials are combined by the last
-// workgroup of each tile, in split order).
+// GEMM given split-K buffers runs the whole rounds in one launch and the
+// tail tiles in a second one with K split over ks workgroups each, so the
+// tail takes 1 / ks of a round (the partials are combined by the last
+// workgroup of each tile, in split order, before the epilogue).
 #include "device_common.h"
 #include "kernels.h"
 
@@ -285,15 +285,15 @@ template <int EPI>
 static hipError_t launch_e(const GemmArgs& a, hipStream_t s) {
   const TileShape ts = tiled2_shape(a.M, a.N);
   const int64_t m_tiles = (a.M + kTG * 16 - 1) / (kTG * 16);
-  if constexpr (!EpiTraits<EPI>::swiglu) {
-    if (a.ksplit > 1) {
-      const int64_t tail = tiled2_tail(ts.units), whole = ts.units - tail;
-      if (tail == 0) return hipErrorInvalidValue;  // the split buffers are sized for the tail tiles
-      hipError_t e = hipSuccess;
-      if (whole > 0) e = launch_range<EPI, false>(a, m_tiles, 0, whole, 1, s);
-      if (e != hipSuccess) return e;
-      return launch_range<EPI, true>(a, m_tiles, whole, tail, a.ksplit, s);
-    }
+  if (a.ksplit > 1) {
+    const int64_t tail = tiled_tail(ts.units), whole = ts.units - tail;
+    if (tail == 0) return hipErrorInvalidValue;  // the split buffers are sized for the tail tiles
+    hipError_t e = launch_range<EPI, false>(a, m_tiles, 0, whole, 1, s);
+    if (e != hipSuccess) return e;
+    GemmArgs t = a;  // counters to clear are cleared by the first launch only
+    t.zero_ptr = nullptr;
+    t.zero_n = 0;
+    return launch_range<EPI, true>(t, m_tiles, whole, tail, a.ksplit, s);
   }
   return launch_range<EPI, false>(a, m_tiles, 0, ts.units, 1, s);
 }
@@ -308,7 +308,7 @@ TileShape tiled2_shape(int64_t M, int64_t N) {
 // (32-bit buffer offsets); the caller checks.
 hipError_t launch_tiled2_gemm(int epi, const GemmArgs& a, hipStream_t s) {
   if (a.M == 0) return hipSuccess;
-  if (!splitk_valid(a, epi)) return hipErrorInvalidValue;
+  if (!splitk_valid(a, epi, true)) return hipErrorInvalidValue;
   switch (epi) {
     case kOutF32: return launch_e<kOutF32>(a, s);
     case kOutBF16: return launch_e<kOutBF16>(a, s);

@@ -460,6 +460,26 @@ def test_mlp_prefill_tail_split():
     assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], y)
 
 
+def test_mlp_w4a16_gate_up_tail_split():
+    """W4A16 at 256 tokens, intermediate 17408: the gate_up GEMM has 272
+    tiles, 16 past one round, whose K is split (its SwiGLU epilogue runs on
+    the combined sums). Hidden 512 keeps the oracle cheap. The workspace
+    starts as 0xFF bytes (the gate_up's first launch clears every split
+    counter) and a second call on it gives the same bytes."""
+    nv.set_path(nv.PATH_AUTO)
+    M, H, I = 256, 512, 17408
+    w = mlp_weights(H, I, 0)
+    p_gu, p_d = packed_weights(H, I, 0)
+    x = synth.activations(11, M, H)
+    ws = torch.full((nv.mlp_workspace_bytes(1, M, H, I),), 0xFF, dtype=torch.uint8, device=dev())
+    ys = [to_host(nv.mlp_forward(1, to_dev(x), p_gu, scalar(w["g_gu"]), p_d, scalar(w["g_d"]), I, ws=ws))
+          for _ in range(2)]
+    rows = np.arange(120, 256, 3)  # the split tiles hold tokens 128..255
+    r = oracle.mlp_w4a16(x[rows], w["c_gu"], w["s_gu"], w["g_gu"], w["c_d"], w["s_d"], w["g_d"])
+    gemm_close(ys[0][rows], r["out"], "w4a16 gate_up tail split")
+    assert np.array_equal(ys[0], ys[1])
+
+
 @pytest.mark.parametrize("M", [1, 16, 256, 4096])
 def test_mlp_w4a16_full_size(M):
     nv.set_path(nv.PATH_AUTO)
