@@ -60,6 +60,9 @@ def _lib():
                                               _u8p, _u8p]),
             "orc_silu_mul_quant_experts": (None, [_u16p, _i64, _i64, _i64, _i32p, _f32p, _u8p, _u8p,
                                                   _f32p]),
+            "orc_prescale_bf16": (None, [_u16p, _u16p, _i64, _i64, _u16p]),
+            "orc_mlp_w4a16_awq": (None, [_u16p, _i64, _i64, _i64, _u8p, _u8p, _f32, _u16p, _u8p, _u8p, _f32,
+                                         _u16p, _f32p, _u16p, _u16p]),
             "orc_num_threads": (ctypes.c_int, []),
         }
         for name, (res, args) in sig.items():
@@ -301,4 +304,35 @@ def mlp_w4a16(x_bf16, wgu_codes, wgu_scales, alpha_gu, wd_codes, wd_scales, alph
                          float(alpha_gu), _p(wd_codes, _u8p), _p(wd_scales, _u8p),
                          float(alpha_d), _p(r["out"], _f32p), _p(r["gu"], _f32p),
                          _p(r["h"], _u16p))
+    return r
+
+
+def prescale_bf16(x_bf16, s_bf16) -> np.ndarray:
+    """AWQ pre-quant scaling: bf16(x * s) per input channel (bf16 bits in and out)."""
+    x = _c(x_bf16, np.uint16)
+    sv = _c(s_bf16, np.uint16)
+    M, K = x.shape
+    assert sv.shape == (K,)
+    out = np.empty((M, K), np.uint16)
+    _lib().orc_prescale_bf16(_p(x, _u16p), _p(sv, _u16p), M, K, _p(out, _u16p))
+    return out
+
+
+def mlp_w4a16_awq(x_bf16, wgu_codes, wgu_scales, alpha_gu, s_gu, wd_codes, wd_scales, alpha_d, s_d) -> dict:
+    """W4A16 forward with AWQ pre-quant scales s_gu [H] and s_d [I] (bf16 bits)
+    on the inputs of the two GEMMs; returns out (fp32), xs and hs (the scaled
+    GEMM inputs, bf16 bits)."""
+    x = _c(x_bf16, np.uint16)
+    M, H = x.shape
+    I = wd_codes.shape[1] * 2
+    assert wgu_codes.shape == (2 * I, H // 2) and wd_codes.shape == (H, I // 2)
+    sg, sd = _c(s_gu, np.uint16), _c(s_d, np.uint16)
+    assert sg.shape == (H,) and sd.shape == (I,)
+    wgu_codes, wgu_scales = _c(wgu_codes, np.uint8), _c(wgu_scales, np.uint8)
+    wd_codes, wd_scales = _c(wd_codes, np.uint8), _c(wd_scales, np.uint8)
+    r = {"out": np.empty((M, H), np.float32), "xs": np.empty((M, H), np.uint16),
+         "hs": np.empty((M, I), np.uint16)}
+    _lib().orc_mlp_w4a16_awq(_p(x, _u16p), M, H, I, _p(wgu_codes, _u8p), _p(wgu_scales, _u8p), float(alpha_gu),
+                             _p(sg, _u16p), _p(wd_codes, _u8p), _p(wd_scales, _u8p), float(alpha_d),
+                             _p(sd, _u16p), _p(r["out"], _f32p), _p(r["xs"], _u16p), _p(r["hs"], _u16p))
     return r

@@ -55,6 +55,14 @@
  *    gate_up is [E, M, 2I] bf16, expert e's first masked_m[e] rows are
  *    valid and quantized with that expert's inverse global scale; the
  *    reading used here leaves the rows past masked_m[e] unwritten.
+ *  - AWQ pre-quant scales of the W4A16 mode: the W4A16 branch of a linear
+ *    layer's `apply` pre-scales its bf16 input by the layer's per-input-
+ *    channel `pre_quant_scale` before calling the W4A16 GEMM (sglang
+ *    PR #35120 report, implementation breakdown item 2). Read here as the
+ *    bf16 elementwise product x' = bf16(x * s) (the fp32 product of two bf16
+ *    values is exact; one rounding to nearest even), applied to the input
+ *    of both GEMMs of the MLP: x with the gate_up layer's scale over H and
+ *    the bf16 h with the down layer's scale over I.
  *
  * Arithmetic conventions:
  *  - Encoding steps are binary32 operations with round-to-nearest-even,
@@ -496,4 +504,39 @@ ORC_API void orc_silu_mul_quant_experts(const uint16_t* gate_up, int64_t E, int6
   }
   free(gu);
   free(h);
+}
+
+/* AWQ pre-quant scaling of a bf16 input: out[m, k] = bf16(x[m, k] * s[k]),
+ * x [M, K] and s [K] bf16 (the product is exact in fp32, then rounded to
+ * nearest even). */
+ORC_API void orc_prescale_bf16(const uint16_t* x, const uint16_t* s, int64_t M, int64_t K, uint16_t* out) {
+  for (int64_t m = 0; m < M; ++m)
+    for (int64_t k = 0; k < K; ++k)
+      out[m * K + k] = orc_f32_to_bf16(orc_bf16_to_f32(x[m * K + k]) * orc_bf16_to_f32(s[k]));
+}
+
+/* W4A16 MLP forward with AWQ pre-quant scales on both GEMM inputs:
+ *   x' = prescale(x, s_gu);  gu = fl32(alpha_gu * x' @ Wgu^T);
+ *   h  = bf16(SwiGLU(gu));   h' = prescale(h, s_d);
+ *   out = fl32(alpha_d * h' @ Wd^T).
+ * Optional stage outputs (NULL to skip): x', h' (bf16 bits). */
+ORC_API void orc_mlp_w4a16_awq(const uint16_t* x, int64_t M, int64_t H, int64_t I,
+                               const uint8_t* wgu_codes, const uint8_t* wgu_scales, float alpha_gu,
+                               const uint16_t* s_gu, const uint8_t* wd_codes, const uint8_t* wd_scales,
+                               float alpha_d, const uint16_t* s_d, float* out, uint16_t* xs_out,
+                               uint16_t* hs_out) {
+  uint16_t* xs = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(M * H));
+  float* gu = (float*)malloc(sizeof(float) * (size_t)(M * 2 * I));
+  float* h = (float*)malloc(sizeof(float) * (size_t)(M * I));
+  uint16_t* hb = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(M * I));
+  uint16_t* hs = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(M * I));
+  orc_prescale_bf16(x, s_gu, M, H, xs);
+  orc_gemm_w4a16(xs, wgu_codes, wgu_scales, M, 2 * I, H, alpha_gu, gu);
+  orc_swiglu(gu, M, I, h);
+  for (int64_t t = 0; t < M * I; ++t) hb[t] = orc_f32_to_bf16(h[t]);
+  orc_prescale_bf16(hb, s_d, M, I, hs);
+  orc_gemm_w4a16(hs, wd_codes, wd_scales, M, H, I, alpha_d, out);
+  if (xs_out) memcpy(xs_out, xs, sizeof(uint16_t) * (size_t)(M * H));
+  if (hs_out) memcpy(hs_out, hs, sizeof(uint16_t) * (size_t)(M * I));
+  free(xs); free(gu); free(h); free(hb); free(hs);
 }

@@ -536,3 +536,56 @@ def test_silu_quant_codes_are_the_quantizer_of_h(orc):
     for e, rows in enumerate([M, 2]):
         qc, qs = orc.quantize(h[e, :rows], gi[e])
         assert np.array_equal(c[e, :rows], qc) and np.array_equal(s[e, :rows], qs)
+
+
+# -- W4A16 AWQ pre-quant scales -------------------------------------------------
+
+def test_prescale_rounds_to_nearest_even_bf16(orc):
+    """bf16(x * s): a product below half an ulp rounds down, an exact tie
+    goes to the even mantissa, a product past the tie rounds up, s = 1 is the
+    identity and a power of two scales exactly."""
+    f = lambda v: int(synth.f32_to_bf16_bits(np.array([v], np.float32))[0])
+    x = np.array([[f(3.0), f(1.0625), f(1.0625), f(-2.5), f(1.0078125)]], np.uint16)
+    s = np.array([f(0.333984375), f(1.0625), f(1.0703125), f(1.0), f(0.25)], np.uint16)
+    y = synth.bf16_bits_to_f32(orc.prescale_bf16(x, s))[0]
+    # 3 * 0.333984375 = 1.001953125 -> 1.0; 1.0625^2 = 1.12890625 is the tie
+    # between 1.125 (even) and 1.1328125; 1.0625 * 1.0703125 = 1.13720703125
+    # -> 1.140625; identity; exact quarter.
+    assert list(y) == [1.0, 1.125, 1.140625, -2.5, 0.251953125]
+
+
+def _awq_case(orc, M=3, H=256, I=512, seed=31):
+    rng = np.random.default_rng(seed)
+    x = synth.activations(seed, M, H)
+    wguc = rng.integers(0, 256, (2 * I, H // 2), dtype=np.uint8)
+    wgus = rng.integers(0x28, 0x48, (2 * I, H // 16), dtype=np.uint8)
+    wdc = rng.integers(0, 256, (H, I // 2), dtype=np.uint8)
+    wds = rng.integers(0x28, 0x48, (H, I // 16), dtype=np.uint8)
+    return rng, x, wguc, wgus, wdc, wds
+
+
+def test_awq_unit_scales_are_the_plain_w4a16_forward(orc):
+    rng, x, wguc, wgus, wdc, wds = _awq_case(orc)
+    one = lambda n: synth.f32_to_bf16_bits(np.ones(n, np.float32))
+    a = orc.mlp_w4a16_awq(x, wguc, wgus, np.float32(0.01), one(256), wdc, wds, np.float32(0.02), one(512))
+    b = orc.mlp_w4a16(x, wguc, wgus, np.float32(0.01), wdc, wds, np.float32(0.02))
+    assert np.array_equal(a["out"], b["out"]) and np.array_equal(a["xs"], x) and np.array_equal(a["hs"], b["h"])
+
+
+def test_awq_invariance_with_compensated_weight_scales(orc):
+    """AWQ's identity x W^T = (x diag(s)) (W diag(1/s))^T, exact for
+    power-of-two s constant over each 16-block: the weight's E4M3 block scale
+    moves by the opposite exponent steps (8 per step) and the codes stay, so
+    the pre-scaled forward equals the plain one bit for bit."""
+    rng, x, wguc, wgus, wdc, wds = _awq_case(orc)
+    H, I = 256, 512
+    eg = rng.integers(-1, 2, H // 16)   # exponent per block of x's channels
+    ed = rng.integers(-1, 2, I // 16)   # per block of h's channels
+    s_gu = synth.f32_to_bf16_bits(np.repeat(2.0 ** eg, 16).astype(np.float32))
+    s_d = synth.f32_to_bf16_bits(np.repeat(2.0 ** ed, 16).astype(np.float32))
+    wgus2 = (wgus.astype(np.int64) - 8 * eg[None, :]).astype(np.uint8)
+    wds2 = (wds.astype(np.int64) - 8 * ed[None, :]).astype(np.uint8)
+    a = orc.mlp_w4a16_awq(x, wguc, wgus2, np.float32(0.01), s_gu, wdc, wds2, np.float32(0.02), s_d)
+    b = orc.mlp_w4a16(x, wguc, wgus, np.float32(0.01), wdc, wds, np.float32(0.02))
+    assert np.array_equal(a["out"], b["out"])
+    assert not np.array_equal(a["xs"], x)
