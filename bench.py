@@ -115,7 +115,8 @@ def prepare_weights(H, I, dev, copies):
     return out[0], out[1], gs[0], gs[1]
 
 
-def cpu_baseline(M, H, I, mode, outliers, per_step_bytes, per_step_flops, budget_s, use_flops, dyn=False):
+def cpu_baseline(M, H, I, mode, outliers, per_step_bytes, per_step_flops, budget_s, use_flops, dyn=False,
+                 awq=False):
     """The CPU oracle on a bounded sample of the workload's steps."""
     import oracle
     wgu = synth.weights(0, 2 * I, H, synth.TENSOR_W_GATE_UP)
@@ -128,6 +129,10 @@ def cpu_baseline(M, H, I, mode, outliers, per_step_bytes, per_step_flops, budget
     del wd
     rows = min(M, 8)
     x0 = synth.activations(0, M, H, outliers=outliers)[:rows]
+    if awq:
+        rs = np.random.default_rng(7)
+        sc_gu = synth.f32_to_bf16_bits(np.exp(0.6 * rs.standard_normal(H)).astype(np.float32))
+        sc_d = synth.f32_to_bf16_bits(np.exp(0.6 * rs.standard_normal(I)).astype(np.float32))
     if mode == "w4a4":
         g1, g1_inv = oracle.global_scale(x0)
         a_gu = oracle.alpha(g1, g_gu)
@@ -142,6 +147,8 @@ def cpu_baseline(M, H, I, mode, outliers, per_step_bytes, per_step_flops, budget
             oracle.mlp_w4a4_per_token(x, c_gu, s_gu, g_gu, c_d, s_d, a_d, g2_inv)
         elif mode == "w4a4":
             oracle.mlp_w4a4(x, c_gu, s_gu, a_gu, c_d, s_d, a_d, g1_inv, g2_inv)
+        elif awq:
+            oracle.mlp_w4a16_awq(x, c_gu, s_gu, g_gu, sc_gu, c_d, s_d, g_d, sc_d)
         else:
             oracle.mlp_w4a16(x, c_gu, s_gu, g_gu, c_d, s_d, g_d)
         n += 1
@@ -170,6 +177,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--path", type=int, default=0, help="kernel class override (0 = auto)")
+    ap.add_argument("--awq", action="store_true",
+                    help="W4A16 with AWQ pre-quant scales on both GEMM inputs")
     ap.add_argument("--per-token", action="store_true",
                     help="W4A4 with per-token dynamic activation scales for x")
     ap.add_argument("--sweep", default=None,
@@ -225,7 +234,9 @@ def run_one(args, dev, M, H, I, mode, outliers, n_seeds, steps, warmup, copies, 
     # Static activation scales, calibrated on the seed-0 input: g1 from x,
     # g2 from the fused kernel's own fp32 h for that x.
     dyn = mode == "w4a4" and args.per_token
-    qmode = nv.MODE_W4A4_DYN if dyn else (nv.MODE_W4A4 if mode == "w4a4" else nv.MODE_W4A16)
+    awq = mode == "w4a16" and args.awq
+    qmode = nv.MODE_W4A4_DYN if dyn else (nv.MODE_W4A4 if mode == "w4a4" else
+                                          (nv.MODE_W4A16_AWQ if awq else nv.MODE_W4A16))
     ws = torch.zeros(max(1, nv.mlp_workspace_bytes(qmode, M, H, I)), dtype=torch.uint8, device=dev)
     out = torch.empty((M, H), dtype=out_dtype, device=dev)
     if mode == "w4a4":
@@ -247,6 +258,11 @@ def run_one(args, dev, M, H, I, mode, outliers, n_seeds, steps, warmup, copies, 
     else:
         a_gu, a_d = g_gu, g_d
         hb = torch.empty((M, I), dtype=torch.bfloat16, device=dev)
+        if awq:
+            # synthetic per-channel pre-quant scales, AWQ's typical spread
+            rs = np.random.default_rng(7)
+            s_gu = bf16_tensor(synth.f32_to_bf16_bits(np.exp(0.6 * rs.standard_normal(H)).astype(np.float32)), dev)
+            s_d = bf16_tensor(synth.f32_to_bf16_bits(np.exp(0.6 * rs.standard_normal(I)).astype(np.float32)), dev)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
@@ -273,6 +289,8 @@ def run_one(args, dev, M, H, I, mode, outliers, n_seeds, steps, warmup, copies, 
         elif mode == "w4a4":
             nv.mlp_forward(0, x, p_gu[r], a_gu, p_d[r], a_d, I, g1_inv=g1_inv, g2_inv=g2_inv,
                            ws=ws, out=out, stream=stream)
+        elif awq:
+            nv.mlp_forward_w4a16_awq(x, p_gu[r], a_gu, s_gu, p_d[r], a_d, s_d, I, ws=ws, out=out, stream=stream)
         else:
             nv.mlp_forward(1, x, p_gu[r], a_gu, p_d[r], a_d, I, ws=ws, out=out, stream=stream)
 
@@ -333,7 +351,7 @@ def run_one(args, dev, M, H, I, mode, outliers, n_seeds, steps, warmup, copies, 
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle")
         cpu = cpu_baseline(M, H, I, mode, outliers, alg["total"], alg["flops"], args.cpu_budget, prefill,
-                           dyn)
+                           dyn, awq)
 
     res = {
         "metric": "NVFP4 MLP TFLOPS + GB/s (% roofline), decode M=1..16 and prefill M=8192",
@@ -348,8 +366,9 @@ def run_one(args, dev, M, H, I, mode, outliers, n_seeds, steps, warmup, copies, 
         "vs_baseline": None,
         "dtype": "f16" if mode == "w4a4" else "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{args.workload}{' per-token' if dyn else ''} M={M} H={H} I={I}", "M": M,
-                   "hidden": H, "intermediate": I, "mode": "w4a4_per_token" if dyn else mode, "seeds": n_seeds, "weight_copies": copies,
+        "config": {"workload": f"{args.workload}{' per-token' if dyn else ''}{' awq' if awq else ''} M={M} H={H} I={I}",
+                   "M": M, "hidden": H, "intermediate": I,
+                   "mode": "w4a4_per_token" if dyn else ("w4a16_awq" if awq else mode), "seeds": n_seeds, "weight_copies": copies,
                    "out_dtype": "bf16", "tflops": alg["flops"] / (ms_per_step * 1e-3) / 1e12,
                    "gbs": alg["total"] / (ms_per_step * 1e-3) / 1e9},
         "roofline": roof,

@@ -66,6 +66,7 @@ extern "C" {
 #define NVFP4_MODE_W4A4 0  /* NVFP4 activations x NVFP4 weights */
 #define NVFP4_MODE_W4A16 1 /* bf16 activations x NVFP4 weights */
 #define NVFP4_MODE_W4A4_DYN 2 /* W4A4 with per-token dynamic scales for x (mlp_forward only) */
+#define NVFP4_MODE_W4A16_AWQ 3 /* W4A16 with AWQ pre-quant scales (mlp_forward_w4a16_awq, workspace size) */
 
 /* Repack kinds. */
 #define NVFP4_REPACK_PLAIN 0  /* any [R, C] weight, e.g. down_proj */
@@ -257,6 +258,32 @@ int mlp_forward(int mode, const uint16_t* x, int64_t M, int64_t H, int64_t I,
  */
 int silu_mul_nvfp4_quant(const void* gate_up, int64_t E, int64_t M, int64_t I, const int32_t* masked_m,
                          const float* g_inv, uint8_t* codes, uint8_t* scales, void* stream);
+
+/*
+ * AWQ pre-quant scaling of a W4A16 layer's bf16 input: the W4A16 branch of
+ * a linear layer's apply multiplies its input by the layer's per-input-
+ * channel `pre_quant_scale` before the W4A16 GEMM (PR #35120 report,
+ * implementation breakdown item 2):
+ *   out[m, k] = bf16(x[m, k] * s[k])   (exact fp32 product, rounded to nearest even)
+ * x, out: bf16 [M, K] (out may be x); s: bf16 [K]; K % 8 == 0; all 16-byte
+ * aligned. Feed out to nvfp4_gemm(NVFP4_MODE_W4A16, ...).
+ */
+int nvfp4_prescale_bf16(const void* x, const void* s, int64_t M, int64_t K, void* out, void* stream);
+
+/*
+ * W4A16 MLP forward with AWQ pre-quant scales on the inputs of both GEMMs
+ * (the same reading applied to the gate_up layer and the down layer):
+ *   x' = bf16(x * s_gu);  h = bf16(SiLU(gate) * up) of the W4A16 gate_up of x';
+ *   h' = bf16(h * s_d);   out = W4A16 down projection of h'.
+ * As mlp_forward(NVFP4_MODE_W4A16, ...) otherwise (g_gu, g_d: the weights'
+ * global scales as alpha). s_gu: bf16 [H]; s_d: bf16 [I]; both 16-byte
+ * aligned device memory. Workspace: mlp_workspace_bytes(NVFP4_MODE_W4A16_AWQ,
+ * M, H, I) (it also holds x'). x' is one more launch before the gate_up GEMM;
+ * h' is applied in the gate_up epilogue.
+ */
+int mlp_forward_w4a16_awq(const uint16_t* x, int64_t M, int64_t H, int64_t I, const void* w_gu_packed,
+                          const float* g_gu, const uint16_t* s_gu, const void* w_d_packed, const float* g_d,
+                          const uint16_t* s_d, void* ws, size_t ws_bytes, void* out, int out_dtype, void* stream);
 
 /* Select the kernel class used by the GEMM entry points (NVFP4_PATH_*).
  * Process-wide; meant for tests and benchmarks. Returns the previous value,

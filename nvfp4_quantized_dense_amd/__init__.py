@@ -19,7 +19,7 @@ NVFP4_ERR_INVALID_ARG = -1
 NVFP4_ERR_UNSUPPORTED = -2
 NVFP4_ERR_HIP = -3
 DTYPE_BF16, DTYPE_F32 = 0, 1
-MODE_W4A4, MODE_W4A16, MODE_W4A4_DYN = 0, 1, 2
+MODE_W4A4, MODE_W4A16, MODE_W4A4_DYN, MODE_W4A16_AWQ = 0, 1, 2, 3
 REPACK_PLAIN, REPACK_SWIGLU = 0, 1
 PATH_AUTO, PATH_GEMV, PATH_STREAM, PATH_TILED = 0, 1, 2, 3
 
@@ -45,6 +45,9 @@ SIGNATURES = {
                                                 _vp, _vp]),
     "gemm_swiglu": (_int, [_int, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _vp, _int, _vp]),
     "silu_mul_nvfp4_quant": (_int, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp]),
+    "nvfp4_prescale_bf16": (_int, [_vp, _vp, _i64, _i64, _vp, _vp]),
+    "mlp_forward_w4a16_awq": (_int, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _int,
+                                     _vp]),
     "mlp_workspace_bytes": (_sz, [_int, _i64, _i64, _i64]),
     "mlp_forward": (_int, [_int, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                            _vp, _int, _vp]),
@@ -286,4 +289,31 @@ def mlp_forward(mode, x, w_gu_packed, alpha_gu, w_d_packed, alpha_d, I, g1_inv=N
                                             _ptr(w_d_packed), _ptr(alpha_d), _ptr(g1_inv), _ptr(g2_inv),
                                             _ptr(ws), ws.numel() * ws.element_size(), _ptr(out),
                                             _dtype_code(out.dtype), _stream(stream)))
+    return out
+
+
+def nvfp4_prescale_bf16(x, s, out=None, stream=None):
+    """AWQ pre-quant scaling: bf16(x * s) per input channel; x bf16 [M, K], s bf16 [K]."""
+    _dense(x, "x"); _dense(s, "s")
+    M, K = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    _check("nvfp4_prescale_bf16", lib().nvfp4_prescale_bf16(_ptr(x), _ptr(s), M, K, _ptr(out), _stream(stream)))
+    return out
+
+
+def mlp_forward_w4a16_awq(x, w_gu_packed, g_gu, s_gu, w_d_packed, g_d, s_d, I, ws=None, out=None,
+                          out_dtype=torch.float32, stream=None):
+    """W4A16 MLP forward with AWQ pre-quant scales s_gu [H] and s_d [I] (bf16)."""
+    _dense(x, "x")
+    M, H = x.shape
+    nws = mlp_workspace_bytes(MODE_W4A16_AWQ, M, H, I)
+    if ws is None:
+        ws = torch.zeros(max(nws, 1), dtype=torch.uint8, device=x.device)
+    if out is None:
+        out = torch.empty((M, H), dtype=out_dtype, device=x.device)
+    _check("mlp_forward_w4a16_awq",
+           lib().mlp_forward_w4a16_awq(_ptr(x), M, H, I, _ptr(w_gu_packed), _ptr(g_gu), _ptr(s_gu), _ptr(w_d_packed),
+                                       _ptr(g_d), _ptr(s_d), _ptr(ws), ws.numel() * ws.element_size(), _ptr(out),
+                                       _dtype_code(out.dtype), _stream(stream)))
     return out

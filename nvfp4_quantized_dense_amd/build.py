@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libnvfp4_mi355x.so")
-SOURCES = ["api.cpp", "quantize.hip", "repack.hip", "stream.hip", "gemv.hip", "fp4gemv.hip", "decode.hip", "tiled.hip", "tiled2.hip", "tiled16.hip", "silu_quant.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "repack.hip", "stream.hip", "gemv.hip", "fp4gemv.hip", "decode.hip", "tiled.hip", "tiled2.hip", "tiled16.hip", "silu_quant.hip", "prescale.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-Wall",

@@ -454,6 +454,7 @@ static size_t mlp_act_bytes(int mode, size_t m, int64_t H, int64_t I) {
   const size_t nvfp4 = align256(m * H / 2) + align256(m * H / 16) + align256(m * I / 2) + align256(m * I / 16);
   if (mode == NVFP4_MODE_W4A4) return nvfp4;
   if (mode == NVFP4_MODE_W4A4_DYN) return nvfp4 + align256(m * sizeof(float));
+  if (mode == NVFP4_MODE_W4A16_AWQ) return align256(m * I * 2) + align256(m * H * 2);  // h, then x'
   return align256(m * I * 2);
 }
 
@@ -482,17 +483,26 @@ static size_t mlp_split_bytes(int mode, int64_t M, int64_t H, int64_t I, bool de
 
 size_t mlp_workspace_bytes(int mode, int64_t M, int64_t H, int64_t I) {
   if (M < 0 || H <= 0 || I <= 0 || !dim_ok(M) || !dim_ok(H) || !dim_ok(I)) return 0;
-  if (mode != NVFP4_MODE_W4A4 && mode != NVFP4_MODE_W4A16 && mode != NVFP4_MODE_W4A4_DYN) return 0;
-  // W4A4_DYN runs the W4A4 GEMM kernels, never the single-launch decode one.
-  const int kmode = mode == NVFP4_MODE_W4A16 ? NVFP4_MODE_W4A16 : NVFP4_MODE_W4A4;
+  if (mode != NVFP4_MODE_W4A4 && mode != NVFP4_MODE_W4A16 && mode != NVFP4_MODE_W4A4_DYN &&
+      mode != NVFP4_MODE_W4A16_AWQ)
+    return 0;
+  // W4A4_DYN runs the W4A4 GEMM kernels, never the single-launch decode
+  // one; W4A16_AWQ the W4A16 ones.
+  const int kmode = (mode == NVFP4_MODE_W4A16 || mode == NVFP4_MODE_W4A16_AWQ) ? NVFP4_MODE_W4A16 : NVFP4_MODE_W4A4;
   return mlp_act_bytes(mode, static_cast<size_t>(M), H, I) +
          mlp_split_bytes(kmode, M, H, I, mode == NVFP4_MODE_W4A4);
 }
 
-int mlp_forward(int mode, const uint16_t* x, int64_t M, int64_t H, int64_t I, const void* w_gu_packed,
-                const float* alpha_gu, const void* w_d_packed, const float* alpha_d, const float* g1_inv,
-                const float* g2_inv, void* ws, size_t ws_bytes, void* out, int out_dtype, void* stream) {
-  if (mode != NVFP4_MODE_W4A4 && mode != NVFP4_MODE_W4A16 && mode != NVFP4_MODE_W4A4_DYN)
+}  // extern "C"
+
+// The MLP forward of every mode; s_gu / s_d are the AWQ pre-quant scales of
+// NVFP4_MODE_W4A16_AWQ (null otherwise).
+static int mlp_forward_impl(int mode, const uint16_t* x, int64_t M, int64_t H, int64_t I, const void* w_gu_packed,
+                            const float* alpha_gu, const void* w_d_packed, const float* alpha_d,
+                            const float* g1_inv, const float* g2_inv, const uint16_t* s_gu, const uint16_t* s_d,
+                            void* ws, size_t ws_bytes, void* out, int out_dtype, void* stream) {
+  if (mode != NVFP4_MODE_W4A4 && mode != NVFP4_MODE_W4A16 && mode != NVFP4_MODE_W4A4_DYN &&
+      mode != NVFP4_MODE_W4A16_AWQ)
     return fail(NVFP4_ERR_INVALID_ARG, "unsupported quant mode %d", mode);
   if (!dim_ok(M) || !dim_ok(H) || !dim_ok(I)) return fail(NVFP4_ERR_INVALID_ARG, "dimension out of range");
   if (H <= 0 || H % 256 != 0 || I <= 0 || I % 256 != 0)
@@ -500,8 +510,10 @@ int mlp_forward(int mode, const uint16_t* x, int64_t M, int64_t H, int64_t I, co
                 (long long)H, (long long)I);
   if (out_dtype != NVFP4_DTYPE_F32 && out_dtype != NVFP4_DTYPE_BF16)
     return fail(NVFP4_ERR_INVALID_ARG, "out_dtype must be F32 or BF16");
-  if (mode == NVFP4_MODE_W4A16 && (g1_inv || g2_inv))
+  if ((mode == NVFP4_MODE_W4A16 || mode == NVFP4_MODE_W4A16_AWQ) && (g1_inv || g2_inv))
     return fail(NVFP4_ERR_INVALID_ARG, "W4A16 takes no activation scales: g1_inv and g2_inv must be NULL");
+  if (mode == NVFP4_MODE_W4A16_AWQ && M > 0 && (!s_gu || !s_d || !aligned16(s_gu) || !aligned16(s_d)))
+    return fail(NVFP4_ERR_INVALID_ARG, "W4A16_AWQ needs 16-byte aligned pre-quant scales s_gu [H] and s_d [I]");
   if (M == 0) { g_err[0] = '\0'; return NVFP4_OK; }
   if (!x || !w_gu_packed || !alpha_gu || !w_d_packed || !alpha_d || !out || !ws)
     return fail(NVFP4_ERR_INVALID_ARG, "null pointer argument");
@@ -517,8 +529,10 @@ int mlp_forward(int mode, const uint16_t* x, int64_t M, int64_t H, int64_t I, co
   int st = check_device();
   if (st) return st;
   hipStream_t s = as_stream(stream);
+  const int ws_mode = mode;
   const bool dyn = mode == NVFP4_MODE_W4A4_DYN;
   if (dyn) mode = NVFP4_MODE_W4A4;  // the W4A4 kernels, x quantized per token
+  if (mode == NVFP4_MODE_W4A16_AWQ) mode = NVFP4_MODE_W4A16;  // the W4A16 kernels on pre-scaled inputs
   const int path = choose_path(mode, M);
   const int epi_out = out_dtype == NVFP4_DTYPE_F32 ? nvfp4::kOutF32 : nvfp4::kOutBF16;
   uint8_t* base = static_cast<uint8_t*>(ws);
@@ -535,7 +549,7 @@ int mlp_forward(int mode, const uint16_t* x, int64_t M, int64_t H, int64_t I, co
   SplitPlan sg = split_plan(k_gu, mode, M, 2 * I, H, true);
   if (!clears_counters(k_gu)) sp = SplitPlan{};
   if (!clears_counters(k_d)) sg = SplitPlan{};
-  uint8_t* split_base = base + mlp_act_bytes(dyn ? NVFP4_MODE_W4A4_DYN : mode, m, H, I);
+  uint8_t* split_base = base + mlp_act_bytes(ws_mode, m, H, I);
   float* part = reinterpret_cast<float*>(split_base);
   uint32_t* counters = reinterpret_cast<uint32_t*>(split_base + std::max(sp.part_bytes, sg.part_bytes));
   uint32_t* counters_gu = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(counters) + sp.counter_bytes);
@@ -606,13 +620,54 @@ int mlp_forward(int mode, const uint16_t* x, int64_t M, int64_t H, int64_t I, co
     return hip_status(e, "mlp_forward down");
   }
   uint8_t* hb = base;
-  nvfp4::GemmArgs g1{x, nullptr, static_cast<const uint8_t*>(w_gu_packed), M, 2 * I, H, alpha_gu, nullptr, hb, nullptr};
+  const void* xin = x;
+  if (s_gu) {
+    // AWQ: x' = bf16(x * s_gu) into the workspace; h gets s_d in the gate_up
+    // epilogue.
+    uint8_t* xs = base + align256(m * I * 2);
+    e = nvfp4::launch_prescale_bf16(x, s_gu, M, H, xs, s);
+    if (e != hipSuccess) return hip_status(e, "mlp_forward prescale");
+    xin = xs;
+  }
+  nvfp4::GemmArgs g1{xin, nullptr, static_cast<const uint8_t*>(w_gu_packed), M, 2 * I, H, alpha_gu, nullptr, hb, nullptr};
+  g1.h_prescale = s_d;
   nvfp4::GemmArgs g2{hb, nullptr, static_cast<const uint8_t*>(w_d_packed), M, H, I, alpha_d, nullptr, out, nullptr};
   with_split(g1, g2);
   e = run_gemm(path, NVFP4_MODE_W4A16, nvfp4::kSwigluBF16, g1, s);
   if (e != hipSuccess) return hip_status(e, "mlp_forward gate_up");
   e = run_gemm(path, NVFP4_MODE_W4A16, epi_out, g2, s);
   return hip_status(e, "mlp_forward down");
+}
+
+extern "C" {
+
+int mlp_forward(int mode, const uint16_t* x, int64_t M, int64_t H, int64_t I, const void* w_gu_packed,
+                const float* alpha_gu, const void* w_d_packed, const float* alpha_d, const float* g1_inv,
+                const float* g2_inv, void* ws, size_t ws_bytes, void* out, int out_dtype, void* stream) {
+  if (mode == NVFP4_MODE_W4A16_AWQ)
+    return fail(NVFP4_ERR_INVALID_ARG, "W4A16_AWQ takes its pre-quant scales: call mlp_forward_w4a16_awq");
+  return mlp_forward_impl(mode, x, M, H, I, w_gu_packed, alpha_gu, w_d_packed, alpha_d, g1_inv, g2_inv, nullptr,
+                          nullptr, ws, ws_bytes, out, out_dtype, stream);
+}
+
+int mlp_forward_w4a16_awq(const uint16_t* x, int64_t M, int64_t H, int64_t I, const void* w_gu_packed,
+                          const float* g_gu, const uint16_t* s_gu, const void* w_d_packed, const float* g_d,
+                          const uint16_t* s_d, void* ws, size_t ws_bytes, void* out, int out_dtype, void* stream) {
+  return mlp_forward_impl(NVFP4_MODE_W4A16_AWQ, x, M, H, I, w_gu_packed, g_gu, w_d_packed, g_d, nullptr, nullptr,
+                          s_gu, s_d, ws, ws_bytes, out, out_dtype, stream);
+}
+
+int nvfp4_prescale_bf16(const void* x, const void* s, int64_t M, int64_t K, void* out, void* stream) {
+  if (!dim_ok(M) || K < 0 || K > (int64_t(1) << 30) || K % 8 != 0)
+    return fail(NVFP4_ERR_INVALID_ARG, "need 0 <= M and K a multiple of 8 (M=%lld K=%lld)", (long long)M,
+                (long long)K);
+  if (M * K == 0) { g_err[0] = '\0'; return NVFP4_OK; }
+  if (!x || !s || !out) return fail(NVFP4_ERR_INVALID_ARG, "null pointer argument");
+  if (!aligned16(x) || !aligned16(s) || !aligned16(out))
+    return fail(NVFP4_ERR_INVALID_ARG, "x, s and out must be 16-byte aligned");
+  int st = check_device();
+  if (st) return st;
+  return hip_status(nvfp4::launch_prescale_bf16(x, s, M, K, out, as_stream(stream)), "prescale launch");
 }
 
 }  // extern "C"

@@ -354,7 +354,8 @@ __device__ __forceinline__ SwigluBlock swiglu_nvfp4(const f32x4& gate, const f32
 template <int E>
 __device__ __forceinline__ void store_swiglu(const f32x4& gate, const f32x4& up, float alpha,
                                              float g2_inv, bool valid, int64_t token, int64_t j0,
-                                             int lane, int64_t I, void* out, uint8_t* out_scales) {
+                                             int lane, int64_t I, void* out, uint8_t* out_scales,
+                                             const uint16_t* h_scale = nullptr) {
   const int q = lane >> 4;
   const int64_t j = j0 + 4 * q;
   if constexpr (E == kSwigluF32 || E == kSwigluBF16) {
@@ -368,6 +369,14 @@ __device__ __forceinline__ void store_swiglu(const f32x4& gate, const f32x4& up,
       } else {
         typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
         bf16x4 b = {(__bf16)h[0], (__bf16)h[1], (__bf16)h[2], (__bf16)h[3]};
+        if (h_scale != nullptr) {
+          // The next layer's AWQ pre-quant scale: bf16(bf16(h) * s).
+          const uint2 sw = *reinterpret_cast<const uint2*>(h_scale + j);
+          const float s4[4] = {__uint_as_float(sw.x << 16), __uint_as_float(sw.x & 0xFFFF0000u),
+                               __uint_as_float(sw.y << 16), __uint_as_float(sw.y & 0xFFFF0000u)};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) b[r] = (__bf16)((float)b[r] * s4[r]);
+        }
         *reinterpret_cast<bf16x4*>(reinterpret_cast<__bf16*>(out) + token * I + j) = b;
       }
     }

@@ -242,7 +242,7 @@ __global__ __launch_bounds__(NW * 64) void k_valu_gemv(GemmArgs args) {
   const int64_t token = tok0 + tl;
   if constexpr (EpiTraits<EPI>::swiglu) {
     store_swiglu<EPI>(res[0], res[1], alpha, g2i, lvalid, token, (int64_t)blockIdx.x * kTileRows,
-                      lane, args.N / 2, args.out, args.out_scales);
+                      lane, args.N / 2, args.out, args.out_scales, args.h_prescale);
   } else {
     store_dense<EPI>(res[0], alpha, lvalid, token, rg0 * kTileRows + 4 * q, args.N, args.out);
   }

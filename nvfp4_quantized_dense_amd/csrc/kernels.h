@@ -29,6 +29,10 @@ hipError_t launch_quantize_per_token(const void* x, bool f32_in, int64_t M, int6
 hipError_t launch_silu_mul_quant(const void* gate_up, int64_t E, int64_t M, int64_t I, const int32_t* masked_m,
                                  const float* g_inv, uint8_t* codes, uint8_t* scales, hipStream_t s);
 
+// prescale.hip: AWQ pre-quant scaling out[m, k] = bf16(x[m, k] * s[k]) of
+// bf16 x [M, K], K % 8 == 0 (out may be x).
+hipError_t launch_prescale_bf16(const void* x, const void* s, int64_t M, int64_t K, void* out, hipStream_t st);
+
 // repack.hip
 hipError_t launch_repack(int kind, const uint8_t* codes, const uint8_t* scales, int64_t R,
                          int64_t C, uint8_t* packed, bool unpack, uint8_t* out_codes,
@@ -64,6 +68,9 @@ struct GemmArgs {
   // is scaled by alpha * row_scale[t] (row_scale[t] = the token's global
   // scale, alpha = the weight's).
   const float* row_scale = nullptr;
+  // W4A16 SwiGLU epilogue with bf16 h: when set, h is multiplied by the
+  // next layer's AWQ pre-quant scale (bf16 [I]) and rounded again to bf16.
+  const uint16_t* h_prescale = nullptr;
   // W4A4 decode GEMV with the SwiGLU-NVFP4 epilogue at M = 1 only: when
   // set, `a` is bf16 [M, K] and each workgroup quantizes it to NVFP4 with
   // this global scale inverse as it stages it (the same arithmetic as

@@ -240,7 +240,8 @@ __global__ __launch_bounds__(NW * 64) void k_stream(GemmArgs args) {
 #pragma unroll
       for (int j = 0; j < NT; ++j)
         store_swiglu<EPI>(acc[2 * pp][j], acc[2 * pp + 1][j], row_alpha(alpha, args.row_scale, tvalid[j], tok[j]),
-                          g2i, tvalid[j], tok[j], (rg0 / 2 + pp) * kTileRows, lane, I, args.out, args.out_scales);
+                          g2i, tvalid[j], tok[j], (rg0 / 2 + pp) * kTileRows, lane, I, args.out, args.out_scales,
+                          args.h_prescale);
   } else {
 #pragma unroll
     for (int g = 0; g < NG; ++g)

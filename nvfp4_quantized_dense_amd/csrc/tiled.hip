@@ -178,7 +178,7 @@ __global__ __launch_bounds__(256) void k_tiled(GemmArgs args) {
       for (int g = 0; g < 4; g += 2) {
         const int64_t grp = rg0 + 4 * wr + g;  // gate group (even), up group grp + 1
         store_swiglu<EPI>(acc[g][j], acc[g + 1][j], at, g2i, tv && grp < ngroups, token,
-                          (grp >> 1) * kTileRows, lane, N / 2, args.out, args.out_scales);
+                          (grp >> 1) * kTileRows, lane, N / 2, args.out, args.out_scales, args.h_prescale);
       }
     } else {
 #pragma unroll

@@ -212,7 +212,7 @@ __global__ __launch_bounds__(kNW16 * 64, 1) void k_tiled16(GemmArgs args, int64_
     if constexpr (EpiTraits<EPI>::swiglu) {
       const int64_t grp = rg0 + 2 * wave;  // gate group (even), up group grp + 1
       store_swiglu<EPI>(acc[0][j], acc[1][j], alpha, g2i, tv && grp < ngroups, token,
-                        (grp >> 1) * kTileRows, lane, N / 2, args.out, args.out_scales);
+                        (grp >> 1) * kTileRows, lane, N / 2, args.out, args.out_scales, args.h_prescale);
     } else {
 #pragma unroll
       for (int g = 0; g < 2; ++g) {

@@ -108,6 +108,15 @@ def test_invalid_arguments_are_rejected_on_the_host():
     assert lib.silu_mul_nvfp4_quant(P, 1, 4, 32, N, N, P, P, N) == INV        # null g_inv
     assert lib.silu_mul_nvfp4_quant(U, 1, 4, 32, N, P, P, P, N) == INV        # misaligned gate_up
     assert lib.silu_mul_nvfp4_quant(N, 0, 4, 32, N, N, N, N, N) == nv.NVFP4_OK  # empty
+    # AWQ pre-quant scales
+    assert lib.nvfp4_prescale_bf16(P, P, 4, 12, P, N) == INV                  # K % 8
+    assert lib.nvfp4_prescale_bf16(P, N, 4, 16, P, N) == INV                  # null s
+    assert lib.nvfp4_prescale_bf16(P, U, 4, 16, P, N) == INV                  # misaligned s
+    assert lib.nvfp4_prescale_bf16(N, N, 0, 16, N, N) == nv.NVFP4_OK          # empty
+    assert lib.mlp_forward_w4a16_awq(P, 4, 256, 512, P, P, N, P, P, P, P, ws, P, 1, N) == INV  # null s_gu
+    assert lib.mlp_forward_w4a16_awq(P, 4, 256, 512, P, P, P, P, P, U, P, ws, P, 1, N) == INV  # misaligned s_d
+    assert lib.mlp_forward(3, P, 4, 256, 512, P, P, P, P, N, N, P, ws, P, 1, N) == INV  # AWQ through mlp_forward
+    assert nv.mlp_workspace_bytes(nv.MODE_W4A16_AWQ, 4, 256, 512) == 4 * 512 * 2 + 4 * 256 * 2
     assert lib.nvfp4_set_path(9) == INV
 
 
