@@ -63,6 +63,8 @@ def _lib():
             "orc_prescale_bf16": (None, [_u16p, _u16p, _i64, _i64, _u16p]),
             "orc_mlp_w4a16_awq": (None, [_u16p, _i64, _i64, _i64, _u8p, _u8p, _f32, _u16p, _u8p, _u8p, _f32,
                                          _u16p, _f32p, _u16p, _u16p]),
+            "orc_grouped_gemm": (None, [ctypes.c_int, _u8p, _u8p, _u16p, _u8p, _u8p, _i64, _i64, _i64, _i64,
+                                        _i32p, _f32p, _f32p]),
             "orc_num_threads": (ctypes.c_int, []),
         }
         for name, (res, args) in sig.items():
@@ -336,3 +338,25 @@ def mlp_w4a16_awq(x_bf16, wgu_codes, wgu_scales, alpha_gu, s_gu, wd_codes, wd_sc
                              _p(sg, _u16p), _p(wd_codes, _u8p), _p(wd_scales, _u8p), float(alpha_d),
                              _p(sd, _u16p), _p(r["out"], _f32p), _p(r["xs"], _u16p), _p(r["hs"], _u16p))
     return r
+
+
+def grouped_gemm(mode, a, a_scales, w_codes, w_scales, masked_m, alpha, out=None) -> np.ndarray:
+    """Grouped (expert) GEMM: expert e's first masked_m[e] rows of a[e]
+    against its own weight (w_codes[e], w_scales[e]) with alpha[e]. mode 0:
+    a = codes [E, M, K/2] + a_scales; mode 1: a = bf16 bits [E, M, K].
+    Rows past masked_m keep what out held (NaN if not given)."""
+    w_codes, w_scales = _c(w_codes, np.uint8), _c(w_scales, np.uint8)
+    E, N, K2 = w_codes.shape
+    K = K2 * 2
+    if mode == 0:
+        ac, asc, ab = _c(a, np.uint8), _c(a_scales, np.uint8), np.zeros(1, np.uint16)
+        M = ac.shape[1]
+    else:
+        ab, ac, asc = _c(a, np.uint16), np.zeros(1, np.uint8), np.zeros(1, np.uint8)
+        M = ab.shape[1]
+    mm, al = _c(masked_m, np.int32), _c(alpha, np.float32)
+    assert mm.shape == (E,) and al.shape == (E,)
+    o = np.full((E, M, N), np.nan, np.float32) if out is None else _c(out, np.float32).copy()
+    _lib().orc_grouped_gemm(int(mode), _p(ac, _u8p), _p(asc, _u8p), _p(ab, _u16p), _p(w_codes, _u8p),
+                            _p(w_scales, _u8p), E, M, N, K, _p(mm, _i32p), _p(al, _f32p), _p(o, _f32p))
+    return o

@@ -55,6 +55,13 @@
  *    gate_up is [E, M, 2I] bf16, expert e's first masked_m[e] rows are
  *    valid and quantized with that expert's inverse global scale; the
  *    reading used here leaves the rows past masked_m[e] unwritten.
+ *  - Grouped (expert) NVFP4 GEMMs with masked_m: the MoE path runs W4A4 or
+ *    W4A16 GEMMs per expert with each expert's own weights and alpha, over
+ *    the expert's valid token rows (sglang PR #35120 report, implementation
+ *    breakdown item 3; masked_m as in the PR #34859 digest's
+ *    `_silu_fp4_quant_fused`). Read here as: expert e's first masked_m[e]
+ *    rows of its activation block get that expert's GEMM; the other rows of
+ *    the output are left unwritten. Routing is not part of it.
  *  - AWQ pre-quant scales of the W4A16 mode: the W4A16 branch of a linear
  *    layer's `apply` pre-scales its bf16 input by the layer's per-input-
  *    channel `pre_quant_scale` before calling the W4A16 GEMM (sglang
@@ -539,4 +546,26 @@ ORC_API void orc_mlp_w4a16_awq(const uint16_t* x, int64_t M, int64_t H, int64_t 
   if (xs_out) memcpy(xs_out, xs, sizeof(uint16_t) * (size_t)(M * H));
   if (hs_out) memcpy(hs_out, hs, sizeof(uint16_t) * (size_t)(M * I));
   free(xs); free(gu); free(h); free(hb); free(hs);
+}
+
+/* Grouped (expert) GEMM with masked rows:
+ *   for e < E, t < clamp(masked_m[e], 0, M):
+ *     out[e, t, :] = GEMM(a[e, t, :], W_e) with alpha[e]
+ * mode 0 (W4A4): a_codes [E, M, K/2], a_scales [E, M, K/16]; mode 1 (W4A16):
+ * a_bf16 [E, M, K]. W_e: codes [E, N, K/2], scales [E, N, K/16]. out
+ * [E, M, N]; rows past masked_m are left as they are. */
+ORC_API void orc_grouped_gemm(int mode, const uint8_t* a_codes, const uint8_t* a_scales, const uint16_t* a_bf16,
+                              const uint8_t* w_codes, const uint8_t* w_scales, int64_t E, int64_t M, int64_t N,
+                              int64_t K, const int32_t* masked_m, const float* alpha, float* out) {
+  for (int64_t e = 0; e < E; ++e) {
+    const int64_t rows = masked_m[e] < 0 ? 0 : (masked_m[e] > M ? M : masked_m[e]);
+    if (rows == 0) continue;
+    const uint8_t* wc = w_codes + e * N * (K / 2);
+    const uint8_t* ws = w_scales + e * N * (K / 16);
+    float* o = out + e * M * N;
+    if (mode == 0)
+      orc_gemm_w4a4(a_codes + e * M * (K / 2), a_scales + e * M * (K / 16), wc, ws, rows, N, K, alpha[e], o);
+    else
+      orc_gemm_w4a16(a_bf16 + e * M * K, wc, ws, rows, N, K, alpha[e], o);
+  }
 }

@@ -589,3 +589,48 @@ def test_awq_invariance_with_compensated_weight_scales(orc):
     b = orc.mlp_w4a16(x, wguc, wgus, np.float32(0.01), wdc, wds, np.float32(0.02))
     assert np.array_equal(a["out"], b["out"])
     assert not np.array_equal(a["xs"], x)
+
+
+# -- grouped (expert) GEMM with masked_m --------------------------------------
+
+def _grouped_case(rng, E, M, N, K):
+    ac = rng.integers(0, 256, (E, M, K // 2), dtype=np.uint8)
+    asc = rng.integers(0x28, 0x48, (E, M, K // 16), dtype=np.uint8)
+    xb = synth.f32_to_bf16_bits(rng.standard_normal((E, M, K)).astype(np.float32))
+    wc = rng.integers(0, 256, (E, N, K // 2), dtype=np.uint8)
+    ws = rng.integers(0x28, 0x48, (E, N, K // 16), dtype=np.uint8)
+    return ac, asc, xb, wc, ws
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_grouped_gemm_masking_and_expert_independence(orc, mode):
+    """Rows past masked_m[e] (clamped to [0, M]) keep their contents; each
+    expert's rows depend only on its own activations, weight and alpha:
+    swapping two experts swaps their outputs, and a power-of-two alpha
+    scales an expert's rows exactly."""
+    rng = np.random.default_rng(41 + mode)
+    E, M, N, K = 3, 5, 32, 256
+    ac, asc, xb, wc, ws = _grouped_case(rng, E, M, N, K)
+    a, sc = (ac, asc) if mode == 0 else (xb, None)
+    mm = np.array([5, 2, 0], np.int32)
+    al = np.array([0.5, 0.25, 1.0], np.float32)
+    y = orc.grouped_gemm(mode, a, sc, wc, ws, mm, al)
+    assert np.all(np.isnan(y[1, 2:])) and np.all(np.isnan(y[2])) and not np.any(np.isnan(y[0]))
+    perm = [1, 0, 2]
+    yp = orc.grouped_gemm(mode, a[perm], None if sc is None else sc[perm], wc[perm], ws[perm], mm[perm], al[perm])
+    assert np.array_equal(yp[0, :2], y[1, :2]) and np.array_equal(yp[1], y[0])
+    y2 = orc.grouped_gemm(mode, a, sc, wc, ws, np.array([5, 9, -1], np.int32), np.array([0.5, 1.0, 1.0], np.float32))
+    assert np.array_equal(y2[1, :2], 4 * y[1, :2]) and np.all(np.isnan(y2[2]))
+
+
+def test_grouped_gemm_rows_are_plain_gemms(orc):
+    """Each expert's valid rows equal the float64 product of its decoded
+    operands times its alpha (W4A4), within the oracle's final fp32 rounding."""
+    rng = np.random.default_rng(43)
+    E, M, N, K = 2, 4, 16, 512
+    ac, asc, _, wc, ws = _grouped_case(rng, E, M, N, K)
+    al = np.array([0.125, 0.0625], np.float32)
+    y = orc.grouped_gemm(0, ac, asc, wc, ws, np.array([4, 3], np.int32), al)
+    for e, rows in enumerate([4, 3]):
+        ref = ref_dequant(ac[e, :rows], asc[e, :rows]) @ ref_dequant(wc[e], ws[e]).T * float(al[e])
+        assert np.allclose(y[e, :rows], ref, rtol=1e-6, atol=0)
