@@ -260,6 +260,26 @@ int silu_mul_nvfp4_quant(const void* gate_up, int64_t E, int64_t M, int64_t I, c
                          const float* g_inv, uint8_t* codes, uint8_t* scales, void* stream);
 
 /*
+ * Grouped (expert) NVFP4 GEMM with masked rows, the per-expert GEMMs of the
+ * MoE path (PR #35120 report, implementation breakdown item 3; `masked_m` as
+ * in the PR #34859 digest, qwen2_moe.py `_silu_fp4_quant_fused`). Routing
+ * is not part of it. For expert e and row t < clamp(masked_m[e], 0, M):
+ *   out[e, t, :] = alpha[e] * a[e, t, :] @ W_e^T   (as nvfp4_gemm in `mode`)
+ * a: W4A4 codes [E, M, K/2] with a_scales [E, M, K/16]; W4A16 bf16 [E, M, K]
+ *   (a_scales NULL).
+ * w_packed: E packed PLAIN weights [N, K] back to back, each
+ *   nvfp4_packed_bytes(NVFP4_REPACK_PLAIN, N, K) bytes.
+ * masked_m: device int32 [E] (NULL: every row valid); alpha: device fp32 [E].
+ * out: [E, M, N] of out_dtype; rows past masked_m[e] are not written.
+ * One launch per expert (weight-streaming kernel for M <= 64, tiled above),
+ * each reading its row count on the device. Errors as nvfp4_gemm;
+ * NVFP4_ERR_UNSUPPORTED when one expert's operands reach 2^31 bytes.
+ */
+int nvfp4_grouped_gemm(int mode, const void* a, const uint8_t* a_scales, const void* w_packed, int64_t E,
+                       int64_t M, int64_t N, int64_t K, const int32_t* masked_m, const float* alpha, void* out,
+                       int out_dtype, void* stream);
+
+/*
  * AWQ pre-quant scaling of a W4A16 layer's bf16 input: the W4A16 branch of
  * a linear layer's apply multiplies its input by the layer's per-input-
  * channel `pre_quant_scale` before the W4A16 GEMM (PR #35120 report,

@@ -48,6 +48,7 @@ SIGNATURES = {
     "nvfp4_prescale_bf16": (_int, [_vp, _vp, _i64, _i64, _vp, _vp]),
     "mlp_forward_w4a16_awq": (_int, [_vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _int,
                                      _vp]),
+    "nvfp4_grouped_gemm": (_int, [_int, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _int, _vp]),
     "mlp_workspace_bytes": (_sz, [_int, _i64, _i64, _i64]),
     "mlp_forward": (_int, [_int, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                            _vp, _int, _vp]),
@@ -316,4 +317,20 @@ def mlp_forward_w4a16_awq(x, w_gu_packed, g_gu, s_gu, w_d_packed, g_d, s_d, I, w
            lib().mlp_forward_w4a16_awq(_ptr(x), M, H, I, _ptr(w_gu_packed), _ptr(g_gu), _ptr(s_gu), _ptr(w_d_packed),
                                        _ptr(g_d), _ptr(s_d), _ptr(ws), ws.numel() * ws.element_size(), _ptr(out),
                                        _dtype_code(out.dtype), _stream(stream)))
+    return out
+
+
+def nvfp4_grouped_gemm(mode, a, a_scales, w_packed, N, K, alpha, masked_m=None, out=None, out_dtype=torch.float32,
+                       stream=None):
+    """Grouped (expert) GEMM: a [E, M, K/2] codes (+ a_scales [E, M, K/16]) or
+    bf16 [E, M, K]; w_packed: E packed [N, K] weights back to back; alpha [E];
+    masked_m int32 [E] or None. Returns out [E, M, N] (rows past masked_m
+    keep what out held)."""
+    _dense(a, "a")
+    E, M = a.shape[0], a.shape[1]
+    if out is None:
+        out = torch.empty((E, M, N), dtype=out_dtype, device=a.device)
+    _check("nvfp4_grouped_gemm",
+           lib().nvfp4_grouped_gemm(int(mode), _ptr(a), _ptr(a_scales), _ptr(w_packed), E, M, N, K, _ptr(masked_m),
+                                    _ptr(alpha), _ptr(out), _dtype_code(out.dtype), _stream(stream)))
     return out

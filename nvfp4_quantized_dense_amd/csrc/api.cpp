@@ -657,6 +657,47 @@ int mlp_forward_w4a16_awq(const uint16_t* x, int64_t M, int64_t H, int64_t I, co
                           s_gu, s_d, ws, ws_bytes, out, out_dtype, stream);
 }
 
+int nvfp4_grouped_gemm(int mode, const void* a, const uint8_t* a_scales, const void* w_packed, int64_t E,
+                       int64_t M, int64_t N, int64_t K, const int32_t* masked_m, const float* alpha, void* out,
+                       int out_dtype, void* stream) {
+  if (E < 0 || !dim_ok(E)) return fail(NVFP4_ERR_INVALID_ARG, "bad expert count %lld", (long long)E);
+  int st = check_gemm(mode, a, a_scales, w_packed, E == 0 ? 0 : M, N, K, alpha, out);
+  if (st) return st;
+  if (out_dtype != NVFP4_DTYPE_F32 && out_dtype != NVFP4_DTYPE_BF16)
+    return fail(NVFP4_ERR_INVALID_ARG, "out_dtype must be F32 or BF16");
+  if (reinterpret_cast<uintptr_t>(masked_m) % 4) return fail(NVFP4_ERR_INVALID_ARG, "masked_m must be 4-byte aligned");
+  if (M == 0 || E == 0) { g_err[0] = '\0'; return NVFP4_OK; }
+  const size_t wbytes = nvfp4_packed_bytes(NVFP4_REPACK_PLAIN, N, K);
+  nvfp4::GemmArgs probe{};
+  probe.M = M;
+  probe.N = N;
+  probe.K = K;
+  if (!fits_buffers(probe, mode))
+    return fail(NVFP4_ERR_UNSUPPORTED, "grouped GEMM needs each expert's operands below 2^31 bytes");
+  st = check_device();
+  if (st) return st;
+  // One launch per expert on the weight-streaming kernel (M <= 64) or the
+  // tiled kernel, each reading its valid row count from masked_m[e].
+  const Kernel k = M <= 64 ? kStream : (mode == NVFP4_MODE_W4A4 ? kTiled2 : kTiled16);
+  const int epi = out_dtype == NVFP4_DTYPE_F32 ? nvfp4::kOutF32 : nvfp4::kOutBF16;
+  const size_t out_row = (size_t)N * (out_dtype == NVFP4_DTYPE_F32 ? 4 : 2);
+  const size_t a_row = mode == NVFP4_MODE_W4A4 ? (size_t)K / 2 : (size_t)K * 2;
+  hipStream_t sm = as_stream(stream);
+  for (int64_t e = 0; e < E; ++e) {
+    nvfp4::GemmArgs g{static_cast<const uint8_t*>(a) + (size_t)e * M * a_row,
+                      a_scales ? a_scales + (size_t)e * M * (K / 16) : nullptr,
+                      static_cast<const uint8_t*>(w_packed) + (size_t)e * wbytes,
+                      M, N, K, alpha + e, nullptr, static_cast<uint8_t*>(out) + (size_t)e * M * out_row, nullptr};
+    g.m_dev = masked_m ? masked_m + e : nullptr;
+    hipError_t err = k == kStream ? nvfp4::launch_stream_gemm(mode, epi, g, sm)
+                     : k == kTiled2 ? nvfp4::launch_tiled2_gemm(epi, g, sm)
+                                    : nvfp4::launch_tiled16_gemm(epi, g, sm);
+    if (err != hipSuccess) return hip_status(err, "grouped_gemm launch");
+  }
+  g_err[0] = '\0';
+  return NVFP4_OK;
+}
+
 int nvfp4_prescale_bf16(const void* x, const void* s, int64_t M, int64_t K, void* out, void* stream) {
   if (!dim_ok(M) || K < 0 || K > (int64_t(1) << 30) || K % 8 != 0)
     return fail(NVFP4_ERR_INVALID_ARG, "need 0 <= M and K a multiple of 8 (M=%lld K=%lld)", (long long)M,

@@ -279,6 +279,14 @@ __device__ __forceinline__ float uniform_now(const float* p) {
   return __int_as_float(v);
 }
 
+// Valid token rows of a GEMM (the device-side masked row count of a grouped
+// GEMM, else M).
+__device__ __forceinline__ int64_t valid_rows(const GemmArgs& a) {
+  if (a.m_dev == nullptr) return a.M;
+  const int64_t r = (int64_t)__builtin_amdgcn_readfirstlane(*a.m_dev);
+  return r < 0 ? 0 : (r > a.M ? a.M : r);
+}
+
 // Workgroup (0, 0, 0) clears n words at p (the next GEMM's split-K counters).
 __device__ __forceinline__ void clear_words(uint32_t* p, int n) {
   if (p != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0)

@@ -68,6 +68,11 @@ struct GemmArgs {
   // is scaled by alpha * row_scale[t] (row_scale[t] = the token's global
   // scale, alpha = the weight's).
   const float* row_scale = nullptr;
+  // Grouped (expert) GEMMs: when set, only the first clamp(*m_dev, 0, M)
+  // token rows are valid (read as zeros past them, never stored); a
+  // workgroup with no valid row exits at once. Weight-streaming and tiled
+  // kernels, ksplit = 1.
+  const int32_t* m_dev = nullptr;
   // W4A16 SwiGLU epilogue with bf16 h: when set, h is multiplied by the
   // next layer's AWQ pre-quant scale (bf16 [I]) and rounded again to bf16.
   const uint16_t* h_prescale = nullptr;

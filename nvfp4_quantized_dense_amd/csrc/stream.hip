@@ -154,13 +154,14 @@ __global__ __launch_bounds__(NW * 64) void k_stream(GemmArgs args) {
   const float alpha = uniform_now(args.alpha);
   const float g2i = EPI == kSwigluNvfp4 ? uniform_now(args.g2_inv) : 0.0f;
 
+  const int64_t M = valid_rows(args);
   StreamSrc<MODE, NT> src;
   src.w = make_rsrc(args.w, (uint32_t)(args.N / kTileRows * T * kTileBytes));
   if constexpr (MODE == kW4A4) {
-    src.a = make_rsrc(args.a, (uint32_t)(args.M * (K / 2)));
-    src.s = make_rsrc(args.a_scales, (uint32_t)(args.M * (K / 16)));
+    src.a = make_rsrc(args.a, (uint32_t)(M * (K / 2)));
+    src.s = make_rsrc(args.a_scales, (uint32_t)(M * (K / 16)));
   } else {
-    src.a = make_rsrc(args.a, (uint32_t)(args.M * K * 2));
+    src.a = make_rsrc(args.a, (uint32_t)(M * K * 2));
     src.s = src.a;
   }
   int64_t tok[NT];
@@ -168,7 +169,7 @@ __global__ __launch_bounds__(NW * 64) void k_stream(GemmArgs args) {
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
     tok[j] = tok0 + 16 * j + tl;
-    tvalid[j] = tok[j] < args.M;
+    tvalid[j] = tok[j] < M;
     src.a_row[j] = (uint32_t)(tok[j] * (MODE == kW4A4 ? K / 2 : K * 2));  // past M: out of range
     src.s_row[j] = (uint32_t)(tok[j] * (K / 16));
   }
@@ -185,6 +186,7 @@ __global__ __launch_bounds__(NW * 64) void k_stream(GemmArgs args) {
   // barriers keep the arithmetic after the wait for its tile and the next
   // tile's loads after the arithmetic.
   clear_words(args.zero_ptr, args.zero_n);
+  if (args.m_dev != nullptr && tok0 >= M) return;  // no valid row (grouped GEMMs run unsplit)
   // K tiles [t0, t1) of this workgroup's split (all of them without split-K).
   const int nt = (int)T;
   const int ks = args.ksplit;

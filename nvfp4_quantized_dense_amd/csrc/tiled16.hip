@@ -63,11 +63,11 @@ struct Stage16Src {
   uint32_t a_voff[4];  // lane offset of this lane's activation chunk, by copy index % 4
 };
 
-__device__ __forceinline__ Stage16Src stage16_src(const GemmArgs& a, int lane) {
+__device__ __forceinline__ Stage16Src stage16_src(const GemmArgs& a, int64_t M, int lane) {
   Stage16Src o;
   const int64_t T = a.K / kTileK;
   o.w = make_rsrc(a.w, (uint32_t)((a.N / kTileRows) * T * kTileBytes));
-  o.a = make_rsrc(a.a, (uint32_t)(a.M * a.K * 2));
+  o.a = make_rsrc(a.a, (uint32_t)(M * a.K * 2));
   // Copy i of a wave moves 4 token rows (4 (4 w + i) + lane / 16); lane l
   // fills slot l % 16 of its row, i.e. chunk (l % 16) ^ key(row % 16), and
   // row % 16 = 4 i + l / 16, so key = i ^ 4 (l / 16).
@@ -96,8 +96,11 @@ __device__ __forceinline__ void issue_stage16(const Stage16Src& src, uint8_t* bu
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int blk = 4 * wave + i;  // rows 4 blk .. 4 blk + 3 of the tile
-    const uint32_t soff = (uint32_t)((tok0 + 4 * blk) * K * 2 + t * 512 + c * 256);
-    NVFP4_DMA16(src.a, 16, src.a_voff[i & 3], soff, abuf + blk * 1024);
+    // The whole offset, token row included, goes into the per-lane offset,
+    // which the buffer range check covers: rows past the valid ones read
+    // zeros and nothing past the end of the activations is touched.
+    const uint32_t voff = src.a_voff[i & 3] + (uint32_t)((tok0 + 4 * blk) * K * 2 + t * 512 + c * 256);
+    NVFP4_DMA16(src.a, 16, voff, 0u, abuf + blk * 1024);
   }
 }
 
@@ -168,7 +171,7 @@ __global__ __launch_bounds__(kNW16 * 64, 1) void k_tiled16(GemmArgs args, int64_
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int q = lane >> 4, tl = lane & 15;
-  const int64_t M = args.M, N = args.N, K = args.K, T = K / kTileK;
+  const int64_t M = valid_rows(args), N = args.N, K = args.K, T = K / kTileK;
   const int64_t ngroups = N / kTileRows;
   const int64_t rg0 = n_tile * kG16;
   const int64_t tok0 = m_tile * (kTG16 * 16);
@@ -183,7 +186,8 @@ __global__ __launch_bounds__(kNW16 * 64, 1) void k_tiled16(GemmArgs args, int64_
 
   // K tiles [t0, t1) of this split (all of them without a split).
   const int64_t per = (T + ks - 1) / ks, t0 = split * per, t1 = min(T, t0 + per);
-  const Stage16Src src = stage16_src(args, lane);
+  if (args.m_dev != nullptr && tok0 >= M) return;  // no valid row (grouped GEMMs run unsplit)
+  const Stage16Src src = stage16_src(args, M, lane);
   issue_stage16(src, smem, 2 * t0, T, K, rg0, ngroups, tok0, wave, lane);
   for (int64_t s = 2 * t0; s < 2 * t1; s += 2) {
     // Two halves per trip (C = 0 in stage buffer 0, C = 1 in buffer 1).

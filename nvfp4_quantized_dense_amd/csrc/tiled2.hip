@@ -66,12 +66,12 @@ struct StageSrc {
 };
 
 template <int NW>
-__device__ __forceinline__ StageSrc<NW> stage_src(const GemmArgs& a, int64_t tok0, int wave, int lane) {
+__device__ __forceinline__ StageSrc<NW> stage_src(const GemmArgs& a, int64_t M, int64_t tok0, int wave, int lane) {
   StageSrc<NW> o;
   const int64_t T = a.K / kTileK;
   o.w = make_rsrc(a.w, (uint32_t)((a.N / kTileRows) * T * kTileBytes));
-  o.a = make_rsrc(a.a, (uint32_t)(a.M * (a.K / 2)));
-  o.s = make_rsrc(a.a_scales, (uint32_t)(a.M * (a.K / 16)));
+  o.a = make_rsrc(a.a, (uint32_t)(M * (a.K / 2)));
+  o.s = make_rsrc(a.a_scales, (uint32_t)(M * (a.K / 16)));
   const int q = lane >> 4, tl = lane & 15;
 #pragma unroll
   for (int i = 0; i < StageSrc<NW>::kTGPerWave; ++i)
@@ -198,7 +198,7 @@ __global__ __launch_bounds__(NWR * NWT * 64, 1) void k_tiled2(GemmArgs args, int
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wr = wave / NWT, wt = wave % NWT;
   const int q = lane >> 4, tl = lane & 15;
-  const int64_t M = args.M, N = args.N, T = args.K / kTileK;
+  const int64_t M = valid_rows(args), N = args.N, T = args.K / kTileK;
   const int64_t ngroups = N / kTileRows;
   const int64_t rg0 = n_tile * kG;
   const int64_t tok0 = m_tile * (kTG * 16);
@@ -211,7 +211,8 @@ __global__ __launch_bounds__(NWR * NWT * 64, 1) void k_tiled2(GemmArgs args, int
 
   // K tiles [t0, t1) of this split (all of them without a split).
   const int64_t per = (T + ks - 1) / ks, t0 = split * per, t1 = min(T, t0 + per);
-  const StageSrc<NW> src = stage_src<NW>(args, tok0, wave, lane);
+  if (args.m_dev != nullptr && tok0 >= M) return;  // no valid row (grouped GEMMs run unsplit)
+  const StageSrc<NW> src = stage_src<NW>(args, M, tok0, wave, lane);
   issue_stage<NW>(src, smem, t0, T, rg0, ngroups, wave, lane);
   for (int64_t t = t0; t < t1; ++t) {
     uint8_t* buf = smem + ((t - t0) & 1) * kStageBytes;

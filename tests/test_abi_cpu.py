@@ -117,6 +117,12 @@ def test_invalid_arguments_are_rejected_on_the_host():
     assert lib.mlp_forward_w4a16_awq(P, 4, 256, 512, P, P, P, P, P, U, P, ws, P, 1, N) == INV  # misaligned s_d
     assert lib.mlp_forward(3, P, 4, 256, 512, P, P, P, P, N, N, P, ws, P, 1, N) == INV  # AWQ through mlp_forward
     assert nv.mlp_workspace_bytes(nv.MODE_W4A16_AWQ, 4, 256, 512) == 4 * 512 * 2 + 4 * 256 * 2
+    # grouped GEMM
+    assert lib.nvfp4_grouped_gemm(0, P, P, P, 2, 4, 24, 256, N, P, P, 1, N) == INV   # N % 16
+    assert lib.nvfp4_grouped_gemm(0, P, N, P, 2, 4, 32, 256, N, P, P, 1, N) == INV   # W4A4 needs scales
+    assert lib.nvfp4_grouped_gemm(1, P, N, P, 2, 4, 32, 256, U, P, P, 1, N) == INV   # misaligned masked_m
+    assert lib.nvfp4_grouped_gemm(0, P, P, P, -1, 4, 32, 256, N, P, P, 1, N) == INV  # E < 0
+    assert lib.nvfp4_grouped_gemm(0, N, N, N, 0, 4, 32, 256, N, N, N, 1, N) == nv.NVFP4_OK  # no experts
     assert lib.nvfp4_set_path(9) == INV
 
 
