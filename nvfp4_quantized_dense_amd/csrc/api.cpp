@@ -182,7 +182,6 @@ static SplitPlan tail_split(const nvfp4::TileShape& ts, int64_t K, int64_t min_t
 SplitPlan split_plan(Kernel k, int mode, int64_t M, int64_t N, int64_t K, bool swiglu) {
   SplitPlan p;
   if (M <= 0) return p;
-  (void)mode;
   // The W4A4 tiled kernel: the tail tiles, at least 8 K tiles per split.
   if (k == kTiled2) return tail_split(nvfp4::tiled2_shape(M, N), K, 8);
   if (k == kTiled16) {
@@ -202,7 +201,7 @@ SplitPlan split_plan(Kernel k, int mode, int64_t M, int64_t N, int64_t K, bool s
     return p;
   }
   if (k != kStream || swiglu) return p;
-  const nvfp4::TileShape ts = nvfp4::stream_shape(M, N);
+  const nvfp4::TileShape ts = nvfp4::stream_shape(mode, M, N);
   p.ways = nvfp4::splitk_ways(ts.units, K / 256, kSplitTargetWaves / ts.waves, ts.waves);
   if (p.ways > 1) {
     p.units = ts.units;

@@ -99,7 +99,7 @@ inline bool splitk_valid(const GemmArgs& a, int epi, bool swiglu_ok = false) {
 struct TileShape {
   int64_t units, tile_floats, waves;
 };
-TileShape stream_shape(int64_t M, int64_t N);
+TileShape stream_shape(int mode, int64_t M, int64_t N);
 TileShape tiled16_shape(int64_t M, int64_t N);
 
 // The number of K splits that brings a dense GEMM of `units` output tiles to

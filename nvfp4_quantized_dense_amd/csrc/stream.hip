@@ -269,18 +269,22 @@ template <int MODE, int EPI, int NT>
 static hipError_t launch_nt(const GemmArgs& a, hipStream_t s) {
   constexpr bool sw = EpiTraits<EPI>::swiglu;
   if constexpr (NT == 1) {
-    if constexpr (!sw) {
-      if (stream_groups(sw, a.M, a.N) == 1) return launch_nt_nw<MODE, EPI, NT, 8, 1>(a, s);
+    switch (stream_groups(MODE, sw, a.M, a.N)) {
+      case 1:
+        if constexpr (!sw) return launch_nt_nw<MODE, EPI, NT, 8, 1>(a, s);
+        break;
+      case 2: return launch_nt_nw<MODE, EPI, NT, 8, 2>(a, s);
+      case 4: return launch_nt_nw<MODE, EPI, NT, 8, 4>(a, s);
     }
-    return launch_nt_nw<MODE, EPI, NT, 8, 2>(a, s);
+    return hipErrorInvalidValue;
   }
   return launch_nt_nw<MODE, EPI, NT, 4, sw ? 2 : 1>(a, s);
 }
 
-TileShape stream_shape(int64_t M, int64_t N) {
+TileShape stream_shape(int mode, int64_t M, int64_t N) {
   int64_t groups = (M + 15) / 16;
   const int64_t nt = groups < 4 ? groups : 4;
-  const int64_t g = nt == 1 ? stream_groups(false, M, N) : 1;
+  const int64_t g = nt == 1 ? stream_groups(mode, false, M, N) : 1;
   return TileShape{N / kTileRows / g * ((M + 16 * nt - 1) / (16 * nt)), 256 * nt * g, nt == 1 ? 8 : 4};
 }
 

@@ -1,19 +1,28 @@
 // stream_groups.h -- packed row groups (16 weight rows each) per workgroup of
 // the weight-streaming kernel at one token group (M <= 16).
 //
-// SwiGLU epilogues take one gate/up pair (2 groups). Dense epilogues take 2
-// groups where N / 16 is even: each activation slice then serves two weight
-// tiles (MLP forward at 16 tokens: W4A4 hidden 7168 62.4 -> 59.1 us, W4A16
-// hidden 5120 69.8 -> 65.8 us; 4 groups, or 2 gate/up pairs, were slower).
+// SwiGLU epilogues take whole gate/up pairs (2 or 4 groups), dense ones 1,
+// 2 or 4; the count must divide N / 16 (else it halves). More groups let
+// each activation slice a workgroup loads serve more weight tiles.
+// W4A4 (NVFP4 activations, a slice as many bytes as a weight tile at 16
+// tokens): dense 2, SwiGLU 2 (MLP forward at 16 tokens: hidden 7168
+// 62.4 -> 59.1 us with dense 2; 4 groups, or 2 gate/up pairs, were slower).
 #pragma once
 #include <stdint.h>
 
+#include "kernels.h"
+
 namespace nvfp4 {
 
-inline int stream_groups(bool swiglu, int64_t M, int64_t N) {
-  (void)M;
-  if (swiglu) return 2;
-  return (N / 16) % 2 == 0 ? 2 : 1;
+// W4A16 (bf16 activations: at 16 tokens a slice is 3.6 times the bytes of
+// the weight tile it multiplies): dense 2; SwiGLU 2 pairs above 8 tokens
+// (gate_up at 16 tokens, hidden 5120: 39.8 -> 35.5 us), one pair below (at
+// 2 and 4 tokens two pairs took 28.7 against 24.2 us; dense 4 was slower
+// at 2 and 4 tokens and even at 16).
+inline int stream_groups(int mode, bool swiglu, int64_t M, int64_t N) {
+  int g = mode == kW4A16 && swiglu && M > 8 ? 4 : 2;
+  while (g > (swiglu ? 2 : 1) && (N / 16) % g != 0) g /= 2;
+  return g;
 }
 
 }  // namespace nvfp4

@@ -491,7 +491,7 @@ def test_mlp_w4a16_full_size(M):
 
 # 17, 513 and 1025 row groups select 16-, 8- and 4-wave workgroups.
 WAVE_N = [272, 8208, 16400]
-M_FOR = {"gemv": [1, 2, 3], "stream": [5, 20, 40, 60]}
+M_FOR = {"gemv": [1, 2, 3], "stream": [5, 12, 16, 20, 40, 60]}
 
 
 @pytest.mark.parametrize("kpath", ["gemv", "stream"])
