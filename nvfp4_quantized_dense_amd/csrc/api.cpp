@@ -164,12 +164,19 @@ struct SplitPlan {
 // workgroup per CU is at most half full, the tail tiles are K-split into as
 // many splits as fill that round (at most 8, at least min_tiles K tiles
 // each).
+// K splits that put `units` tiles into one round of the tiled kernels (at
+// most 8, every split non-empty and at least min_tiles of the T K tiles).
+static int64_t round_ways(int64_t units, int64_t T, int64_t min_tiles) {
+  int64_t ks = std::min<int64_t>(nvfp4::kTiledSlots / units, 8);
+  while (ks > 1 && ((ks - 1) * ((T + ks - 1) / ks) >= T || (T + ks - 1) / ks < min_tiles)) --ks;
+  return std::max<int64_t>(ks, 1);
+}
+
 static SplitPlan tail_split(const nvfp4::TileShape& ts, int64_t K, int64_t min_tiles) {
   SplitPlan p;
-  const int64_t tail = nvfp4::tiled_tail(ts.units), T = K / 256;
+  const int64_t tail = nvfp4::tiled_tail(ts.units);
   if (tail == 0 || 2 * tail > nvfp4::kTiledSlots) return p;
-  int64_t ks = std::min<int64_t>(nvfp4::kTiledSlots / tail, 8);
-  while (ks > 1 && ((ks - 1) * ((T + ks - 1) / ks) >= T || (T + ks - 1) / ks < min_tiles)) --ks;
+  const int64_t ks = round_ways(tail, K / 256, min_tiles);
   if (ks <= 1) return p;
   p.ways = (int)ks;
   p.units = tail;
@@ -182,17 +189,32 @@ static SplitPlan tail_split(const nvfp4::TileShape& ts, int64_t K, int64_t min_t
 SplitPlan split_plan(Kernel k, int mode, int64_t M, int64_t N, int64_t K, bool swiglu) {
   SplitPlan p;
   if (M <= 0) return p;
-  // The W4A4 tiled kernel: the tail tiles, at least 8 K tiles per split.
-  if (k == kTiled2) return tail_split(nvfp4::tiled2_shape(M, N), K, 8);
+  // The W4A4 tiled kernel: a grid of less than one round (dense epilogues:
+  // the down projection at a few hundred tokens) into as many K splits as
+  // fill one round, else the tail tiles; at least 8 K tiles per split.
+  if (k == kTiled2) {
+    const nvfp4::TileShape ts = nvfp4::tiled2_shape(M, N);
+    if (ts.units >= nvfp4::kTiledSlots) return tail_split(ts, K, 8);
+    if (swiglu) return p;
+    p.ways = (int)round_ways(ts.units, K / 256, 8);
+    if (p.ways > 1) {
+      p.units = ts.units;
+      p.part_bytes = align256((size_t)(ts.units * p.ways * ts.tile_floats) * sizeof(float));
+      p.counter_bytes = align256((size_t)ts.units * sizeof(uint32_t));
+    }
+    return p;
+  }
   if (k == kTiled16) {
     // The W4A16 tiled kernel (one 8-wave workgroup per CU): a grid of less
     // than one round (dense epilogues: the down projection at a few hundred
-    // tokens) to about 2 workgroups per CU, at least 4 K tiles per split;
-    // a larger grid in its tail tiles (the gate_up at 256 tokens: 272 tiles).
+    // tokens) into as many K splits as fill one round, at least 4 K tiles
+    // each (forward at 256 tokens, hidden 5120: 216 -> 183 us against
+    // splitting to about two rounds); a larger grid in its tail tiles (the
+    // gate_up at 256 tokens: 272 tiles).
     const nvfp4::TileShape ts = nvfp4::tiled16_shape(M, N);
     if (ts.units >= nvfp4::kTiledSlots) return tail_split(ts, K, 4);
     if (swiglu) return p;
-    p.ways = nvfp4::splitk_ways(ts.units, K / 256, 2 * nvfp4::kTiledSlots, 4);
+    p.ways = (int)round_ways(ts.units, K / 256, 4);
     if (p.ways > 1) {
       p.units = ts.units;
       p.part_bytes = align256((size_t)(ts.units * p.ways * ts.tile_floats) * sizeof(float));

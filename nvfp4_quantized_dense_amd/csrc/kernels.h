@@ -50,13 +50,14 @@ struct GemmArgs {
   const float* g2_inv;       // SwiGLU + NVFP4 output only
   void* out;                 // [M, N] dense, or h [M, I] (dense or codes)
   uint8_t* out_scales;       // h scales [M, I/16]
-  // Split-K (weight-streaming and W4A16 tiled kernels, dense epilogues):
-  // ksplit > 1 divides the K tiles over that many workgroups per output
-  // tile. Each workgroup stores its partial result tile to part (tile u,
-  // split s at ((u * ksplit + s) * tile_floats)); the last of the ksplit
-  // workgroups of a tile to finish (counted in counters[u], which must be
-  // zero at launch and are left zero) adds the partials in split order and
-  // runs the epilogue.
+  // Split-K (weight-streaming kernel: dense epilogues; tiled kernels: any
+  // epilogue, on the tiles their launcher splits): ksplit > 1 divides the K
+  // tiles over that many workgroups per output tile. Each workgroup stores
+  // its partial result tile to part (split tile u, split s at
+  // ((u * ksplit + s) * tile_floats)); the last of the ksplit workgroups of
+  // a tile to finish (counted in counters[u], which must be zero at launch
+  // and are left zero) adds the partials in split order and runs the
+  // epilogue.
   float* part = nullptr;
   uint32_t* counters = nullptr;
   int ksplit = 1;
@@ -130,9 +131,10 @@ constexpr int64_t kTiledSlots = 256;
 inline int64_t tiled_tail(int64_t units) { return units > kTiledSlots ? units % kTiledSlots : 0; }
 
 // W4A4 only; packed weight, activation codes and scales each < 2^31 bytes.
-// With ksplit > 1 only the tiles of the last, partial round are K-split:
-// tiled_tail(units) of them, which must be nonzero; part and counters are
-// sized for those (any epilogue: the partials are combined before it).
+// With ksplit > 1: a grid of less than one round (dense epilogues) splits
+// every tile; a larger one splits only its tiled_tail tiles (any epilogue:
+// the partials are combined before it). part and counters are sized for
+// the split tiles.
 hipError_t launch_tiled2_gemm(int epi, const GemmArgs& a, hipStream_t s);
 TileShape tiled2_shape(int64_t M, int64_t N);
 // W4A16 only; packed weight and the activation rows (+256 of padding) each

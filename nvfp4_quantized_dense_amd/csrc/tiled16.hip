@@ -142,12 +142,11 @@ __device__ __forceinline__ void compute_stage16(f32x4 (&acc)[2][8], const uint8_
 }  // namespace
 #endif  // __HIP_DEVICE_COMPILE__
 
-// SPLIT: compiled with the K-split combine (dense epilogues, ksplit > 1).
-// A separate instantiation: with the combine merely present, the main loop
-// of the unsplit down projection compiled 23% slower (861 against 699 us at
-// 4096 tokens, hidden 5120).
-// This launch covers output tiles [tile0, tile0 + count); with SPLIT each of
-// them as args.ksplit K splits.
+// SPLIT: compiled with the K-split combine (ksplit > 1). A separate
+// instantiation: with the combine merely present, the main loop of the
+// unsplit down projection compiled 23% slower (861 against 699 us at 4096
+// tokens, hidden 5120). This launch covers output tiles [tile0, tile0 +
+// count); with SPLIT each of them as args.ksplit K splits.
 template <int EPI, bool SPLIT>
 __global__ __launch_bounds__(kNW16 * 64, 1) void k_tiled16(GemmArgs args, int64_t n_tiles, int64_t per_xcd,
                                                            int64_t tile0, int64_t count) {

@@ -287,6 +287,12 @@ static hipError_t launch_e(const GemmArgs& a, hipStream_t s) {
   const TileShape ts = tiled2_shape(a.M, a.N);
   const int64_t m_tiles = (a.M + kTG * 16 - 1) / (kTG * 16);
   if (a.ksplit > 1) {
+    // Less than a round (dense epilogues): every tile split. More: the whole
+    // rounds unsplit, then the tail tiles split.
+    if (ts.units < kTiledSlots) {
+      if constexpr (EpiTraits<EPI>::swiglu) return hipErrorInvalidValue;
+      return launch_range<EPI, true>(a, m_tiles, 0, ts.units, a.ksplit, s);
+    }
     const int64_t tail = tiled_tail(ts.units), whole = ts.units - tail;
     if (tail == 0) return hipErrorInvalidValue;  // the split buffers are sized for the tail tiles
     hipError_t e = launch_range<EPI, false>(a, m_tiles, 0, whole, 1, s);

@@ -460,6 +460,36 @@ def test_mlp_prefill_tail_split():
     assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], y)
 
 
+@pytest.mark.parametrize("mode", ["w4a4", "w4a16"])
+@pytest.mark.parametrize("M", [128, 200])
+def test_mlp_tiled_small_grid_split(mode, M):
+    """Tiled kernels, down projection of fewer tiles than CUs (hidden 1024:
+    4 weight tiles x 1-2 token tiles), K split to fill one round
+    (intermediate 4096: 16 K tiles). The workspace starts as 0xFF bytes and
+    a second call on it gives the same bytes."""
+    nv.set_path(nv.PATH_AUTO)
+    H, I = 1024, 4096
+    w = mlp_weights(H, I, 0)
+    p_gu, p_d = packed_weights(H, I, 0)
+    x = synth.activations(M, M, H)
+    qm = 0 if mode == "w4a4" else 1
+    ws = torch.full((nv.mlp_workspace_bytes(qm, M, H, I),), 0xFF, dtype=torch.uint8, device=dev())
+    if mode == "w4a4":
+        sc = calibrate_activation_scales(x[:64], w)
+        run = lambda: nv.mlp_forward(0, to_dev(x), p_gu, scalar(sc["a_gu"]), p_d, scalar(sc["a_d"]), I,
+                                     g1_inv=scalar(sc["g1_inv"]), g2_inv=scalar(sc["g2_inv"]), ws=ws)
+    else:
+        run = lambda: nv.mlp_forward(1, to_dev(x), p_gu, scalar(w["g_gu"]), p_d, scalar(w["g_d"]), I, ws=ws)
+    ys = [to_host(run()) for _ in range(2)]
+    if mode == "w4a4":
+        r = oracle.mlp_w4a4(x, w["c_gu"], w["s_gu"], sc["a_gu"], w["c_d"], w["s_d"], sc["a_d"], sc["g1_inv"],
+                            sc["g2_inv"])
+    else:
+        r = oracle.mlp_w4a16(x, w["c_gu"], w["s_gu"], w["g_gu"], w["c_d"], w["s_d"], w["g_d"])
+    gemm_close(ys[0], r["out"], f"{mode} small-grid split M={M}")
+    assert np.array_equal(ys[0], ys[1])
+
+
 def test_mlp_w4a16_gate_up_tail_split():
     """W4A16 at 256 tokens, intermediate 17408: the gate_up GEMM has 272
     tiles, 16 past one round, whose K is split (its SwiGLU epilogue runs on
