@@ -209,10 +209,14 @@ int gemm_swiglu(int mode, const void* a, const uint8_t* a_scales, const void* w_
                 int64_t M, int64_t I, int64_t K, const float* alpha, void* h, int h_dtype,
                 void* stream);
 
-/* Workspace bytes mlp_forward needs: W4A4 holds x and h in NVFP4 (W4A4_DYN
- * also x's per-token scales); W4A16 holds h in bf16. Each region starts
- * 256-byte aligned. At W4A4 M = 1 it also holds the single-launch decode
- * kernel's records (see mlp_forward). */
+/* Workspace bytes mlp_forward (or mlp_forward_w4a16_awq, mode
+ * NVFP4_MODE_W4A16_AWQ) needs: W4A4 holds x and h in NVFP4 (W4A4_DYN also
+ * x's per-token scales); W4A16 holds h in bf16 (W4A16_AWQ also x', the
+ * pre-scaled x). Then the split-K partial tiles and two sets of arrival
+ * counters (down projection, gate_up), sized for the largest plan over the
+ * kernel paths. Each region starts 256-byte aligned. At W4A4 M = 1 the
+ * split region holds the single-launch decode kernel's records instead (see
+ * mlp_forward). Returns 0 for an unknown mode or bad sizes. */
 size_t mlp_workspace_bytes(int mode, int64_t M, int64_t H, int64_t I);
 
 /*
@@ -232,7 +236,10 @@ size_t mlp_workspace_bytes(int mode, int64_t M, int64_t H, int64_t I);
  * 32-bit number new to the call. The workspace must therefore hold zeros the
  * first time it is used this way (every call leaves it ready for the next;
  * memory with other contents could hold a current tag by chance). Calls that
- * share a workspace must not overlap (the same holds on every path).
+ * share a workspace must not overlap (the same holds on every path). On the
+ * other paths the workspace may hold anything: the split-K counters are
+ * cleared by the gate_up GEMM's first launch. NVFP4_MODE_W4A16_AWQ is not
+ * accepted here (mlp_forward_w4a16_awq takes its scales).
  */
 int mlp_forward(int mode, const uint16_t* x, int64_t M, int64_t H, int64_t I,
                 const void* w_gu_packed, const float* alpha_gu, const void* w_d_packed,
