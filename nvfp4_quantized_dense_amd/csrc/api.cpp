@@ -568,8 +568,7 @@ static int mlp_forward_impl(int mode, const uint16_t* x, int64_t M, int64_t H, i
   const Kernel k_d = mlp_kernel(path, mode, M, H, I);
   SplitPlan sp = split_plan(k_d, mode, M, H, I, false);
   SplitPlan sg = split_plan(k_gu, mode, M, 2 * I, H, true);
-  if (!clears_counters(k_gu)) sp = SplitPlan{};
-  if (!clears_counters(k_d)) sg = SplitPlan{};
+  if (!clears_counters(k_gu)) sp = sg = SplitPlan{};
   uint8_t* split_base = base + mlp_act_bytes(ws_mode, m, H, I);
   float* part = reinterpret_cast<float*>(split_base);
   uint32_t* counters = reinterpret_cast<uint32_t*>(split_base + std::max(sp.part_bytes, sg.part_bytes));
