@@ -147,12 +147,19 @@ hipError_t run_gemm(int path, int mode, int epi, const nvfp4::GemmArgs& a, hipSt
   }
 }
 
-// Split-K of a dense GEMM on the weight-streaming kernel: K is split until
-// about kSplitTargetWaves waves run (the down projection has few output
-// tiles, H / 16 per token group), each split keeping at least one tile per
-// wave. (At M = 16 on hidden 5120: W4A4 down 21.2 -> 19-20 us, W4A16 40.8 ->
-// 30.7 us. The decode GEMVs measured no gain from it and do not split.)
-constexpr int64_t kSplitTargetWaves = 8192;
+// Split-K of a dense GEMM on the weight-streaming kernel: only a grid of
+// fewer output tiles than a quarter of the CUs is split, into at most as
+// many ways as keep one workgroup per CU, at least 4 K tiles per split.
+// Larger grids run unsplit: with 2 row groups x 8 waves per workgroup the
+// down projection at 4 and 16 tokens (160 tiles at hidden 5120, 224 at
+// 7168) measured 14.4 / 16.0 us unsplit against 16.4 / 19.0 (2 ways),
+// 14.7 / 16.4 (3 ways) and 19.9 / 21.3 (7 ways), and 17.5 against 24.5 us
+// at 16 tokens on hidden 7168: the dense kernel's register use leaves 2
+// such workgroups per CU, and the partial-sum exchange adds three
+// dependent memory round trips to every tile. (The decode GEMVs do not
+// split either.)
+constexpr int64_t kStreamSplitMaxUnits = 64;
+constexpr int64_t kStreamSplitTargetWgs = 256;
 
 struct SplitPlan {
   int ways = 1;
@@ -224,7 +231,8 @@ SplitPlan split_plan(Kernel k, int mode, int64_t M, int64_t N, int64_t K, bool s
   }
   if (k != kStream || swiglu) return p;
   const nvfp4::TileShape ts = nvfp4::stream_shape(mode, M, N);
-  p.ways = nvfp4::splitk_ways(ts.units, K / 256, kSplitTargetWaves / ts.waves, ts.waves);
+  if (ts.units >= kStreamSplitMaxUnits) return p;
+  p.ways = nvfp4::splitk_ways(ts.units, K / 256, kStreamSplitTargetWgs, 4);
   if (p.ways > 1) {
     p.units = ts.units;
     p.part_bytes = align256((size_t)(ts.units * p.ways * ts.tile_floats) * sizeof(float));
