@@ -263,18 +263,24 @@ static hipError_t launch_nt_nw(const GemmArgs& a, hipStream_t s) {
 }
 
 // Waves per workgroup: 8 for one token group (measured best at M = 2..16
-// on the decode shapes), 4 for more token groups (their register sets leave
-// room for fewer waves per SIMD). Row groups per workgroup: stream_groups.
+// on the decode shapes), except the W4A16 SwiGLU kernels: their register
+// sets (95 VGPRs with one gate/up pair, 155 with two) leave room for 5 or 3
+// waves per SIMD, so 8-wave workgroups ran their 1088 or 544 workgroups in
+// over two rounds; 4-wave ones fit one round (gate_up at 2 / 4 / 16 tokens,
+// hidden 5120: 24.8 / 25.7 / 36.0 -> 24.3 / 25.0 / 33.9 us). 4 waves for
+// more token groups (their register sets leave room for fewer waves per
+// SIMD). Row groups per workgroup: stream_groups.
 template <int MODE, int EPI, int NT>
 static hipError_t launch_nt(const GemmArgs& a, hipStream_t s) {
   constexpr bool sw = EpiTraits<EPI>::swiglu;
   if constexpr (NT == 1) {
+    constexpr int kNW = MODE == kW4A16 && sw ? 4 : 8;
     switch (stream_groups(MODE, sw, a.M, a.N)) {
       case 1:
         if constexpr (!sw) return launch_nt_nw<MODE, EPI, NT, 8, 1>(a, s);
         break;
-      case 2: return launch_nt_nw<MODE, EPI, NT, 8, 2>(a, s);
-      case 4: return launch_nt_nw<MODE, EPI, NT, 8, 4>(a, s);
+      case 2: return launch_nt_nw<MODE, EPI, NT, kNW, 2>(a, s);
+      case 4: return launch_nt_nw<MODE, EPI, NT, kNW, 4>(a, s);
     }
     return hipErrorInvalidValue;
   }
