@@ -287,6 +287,23 @@ __device__ __forceinline__ int64_t valid_rows(const GemmArgs& a) {
   return r < 0 ? 0 : (r > a.M ? a.M : r);
 }
 
+// Output tile `tile` of a grid of outer_n x inner_n tiles in bands of
+// `band` outer tiles: within a band the tiles run inner-major with the
+// band's outer tiles fastest (the last band may be narrower), a bijection
+// onto [0, outer_n) x [0, inner_n). A run of consecutive tiles (one XCD's
+// resident workgroups) then spans about band outer tiles by run / band inner
+// tiles, so it reads that many operand panels of each kind instead of one
+// of the first kind and a whole operand of the second.
+__device__ __forceinline__ void banded_tile(int64_t tile, int64_t outer_n, int64_t inner_n, int64_t band,
+                                            int64_t& outer, int64_t& inner) {
+  const int64_t span = band * inner_n;
+  const int64_t b = tile / span, within = tile - b * span;
+  const int64_t rest = outer_n - b * band;
+  const int64_t bw = rest < band ? rest : band;
+  outer = b * band + within % bw;
+  inner = within / bw;
+}
+
 // Workgroup (0, 0, 0) clears n words at p (the next GEMM's split-K counters).
 __device__ __forceinline__ void clear_words(uint32_t* p, int n) {
   if (p != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0)

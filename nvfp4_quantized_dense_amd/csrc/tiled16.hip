@@ -19,10 +19,12 @@
 // of two LDS stages (52 KB each) while the other is multiplied (three
 // stages measured slower). Token rows past M lie past the end of the
 // activation buffer and load as zeros; row groups past N are clamped to the
-// last group and never stored. Output tiles are ordered token-tile-major
-// within each XCD, so the XCD's resident workgroups share one activation
-// tile in its L2 while sweeping weight tiles (the bf16 activation tile is
-// 3.6x the bytes of a weight tile per K column).
+// last group and never stored. Output tiles are dealt to each XCD in bands
+// of 4 token tiles swept weight-tile-major, so the XCD's 32 resident
+// workgroups cover 4 token tiles x 8 weight tiles and read 12 operand
+// panels through its L2 per round, not 1 activation panel and 32 weight
+// panels (the bf16 activation tile is 3.6x the bytes of a weight tile per K
+// column).
 //
 // Activation layout in LDS: token row r takes 256 bytes, its sixteen 16-byte
 // chunks (8 columns each) stored at slot chunk ^ key(r % 16), where key swaps
@@ -46,6 +48,7 @@ constexpr int kW16Bytes = kG16 * 1024;           // code halves of the weight ti
 constexpr int kS16Bytes = kG16 * 256;            // scale blocks of the weight tiles
 constexpr int kA16Bytes = kTG16 * 16 * 256;      // 128 tokens x 128 bf16
 constexpr int kStage16 = kW16Bytes + kS16Bytes + kA16Bytes;
+constexpr int64_t kBandTokenTiles = 4;           // tile order: token tiles per band
 }  // namespace
 
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -155,9 +158,8 @@ __global__ __launch_bounds__(kNW16 * 64, 1) void k_tiled16(GemmArgs args, int64_
   __shared__ uint32_t arrived;
   clear_words(args.zero_ptr, args.zero_n);
   // XCD-aware order: workgroup ids are dealt round-robin to the 8 XCDs, so
-  // XCD x takes a contiguous run of output tiles, token-tile-major; its
-  // resident workgroups share an activation tile in its L2 while sweeping
-  // weight tiles. With a K split, the ks splits of an output tile are
+  // XCD x takes a contiguous run of output tiles, in bands of 4 token tiles
+  // (banded_tile). With a K split, the ks splits of an output tile are
   // consecutive.
   const int ks = SPLIT ? args.ksplit : 1;
   const int64_t id = blockIdx.x;
@@ -166,7 +168,8 @@ __global__ __launch_bounds__(kNW16 * 64, 1) void k_tiled16(GemmArgs args, int64_
   const int64_t local = f / ks;
   const int split = (int)(f - local * ks);
   const int64_t tile = tile0 + local;
-  const int64_t m_tile = tile / n_tiles, n_tile = tile % n_tiles;
+  int64_t m_tile, n_tile;
+  banded_tile(tile, (args.M + kTG16 * 16 - 1) / (kTG16 * 16), n_tiles, kBandTokenTiles, m_tile, n_tile);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int q = lane >> 4, tl = lane & 15;

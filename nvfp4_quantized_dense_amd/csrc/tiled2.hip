@@ -14,9 +14,11 @@
 // packed f16 multiply by the E4M3 scale).
 //
 // Tile order is XCD-aware: workgroup ids are dealt round-robin to the 8 XCDs,
-// so XCD x is given a contiguous run of output tiles ordered weight-tile-
-// major; the workgroups resident on one XCD share a weight tile in its L2
-// while they sweep the token tiles.
+// so XCD x is given a contiguous run of output tiles, in bands of 4 weight
+// tiles swept token-tile-major: the 32 workgroups resident on one XCD cover
+// 4 weight tiles x 8 token tiles and read 12 operand panels through its L2
+// per round of tiles, not 1 weight panel and all 32 activation panels (all
+// of x at 8192 tokens) as a weight-tile-major order does.
 //
 // One workgroup fits a CU (two 72 KB stages of LDS), so output tiles run in
 // rounds of one per CU. When the last round would be at most half full (the
@@ -36,6 +38,7 @@ constexpr int kWBytes = kG * kTileBytes;             // packed weight tiles
 constexpr int kACodeBytes = kTG * 2 * 1024;          // activation codes, lane order
 constexpr int kAScaleBytes = kTG * 16 * 16;          // 16 scale bytes per token
 constexpr int kStageBytes = kWBytes + kACodeBytes + kAScaleBytes;
+constexpr int64_t kBandWeightTiles = 4;              // tile order: weight tiles per band
 
 // The buffer-resource type exists only for the device; the host pass sees the
 // kernel's signature alone (for its launch stub).
@@ -193,7 +196,8 @@ __global__ __launch_bounds__(NWR * NWT * 64, 1) void k_tiled2(GemmArgs args, int
   const int64_t local = f / ks;
   const int split = (int)(f - local * ks);
   const int64_t tile = tile0 + local;
-  const int64_t n_tile = tile / m_tiles, m_tile = tile % m_tiles;
+  int64_t n_tile, m_tile;
+  banded_tile(tile, (args.N / kTileRows + kG - 1) / kG, m_tiles, kBandWeightTiles, n_tile, m_tile);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wr = wave / NWT, wt = wave % NWT;
