@@ -12,7 +12,17 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libnvfp4_mi355x.so")
-SOURCES = ["api.cpp", "quantize.hip", "repack.hip", "stream.hip", "gemv.hip", "fp4gemv.hip", "decode.hip", "tiled.hip", "tiled2.hip", "tiled16.hip", "silu_quant.hip", "prescale.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "repack.hip", "stream.hip", "stream_nt1.hip", "gemv.hip", "fp4gemv.hip",
+           "decode.hip", "tiled.hip", "tiled2.hip", "tiled16.hip", "silu_quant.hip", "prescale.hip"]
+# LLVM instruction-scheduling strategy per translation unit, where another
+# than the default measured faster on MI355X: the W4A16 tiled kernel with
+# max-ilp (forward at 256 / 4096 tokens, hidden 5120: 208 -> 198 us, 1948 ->
+# 1895 us), the one-token-group weight-streaming kernels with iterative-ilp
+# (W4A16 forward at 16 tokens 60.5 -> 55.4 us; W4A4 at 4 / 16 tokens 37.8 /
+# 42.9 -> 37.3 / 42.3 us). The same strategies made other kernels slower
+# (max-ilp: the W4A4 tiled kernel 3.2 -> 5.5 ms; iterative-ilp: the 4-group
+# streaming kernel at 64 tokens 77.5 -> 84.2 us), so they stay per file.
+SCHED = {"tiled16.hip": "max-ilp", "stream_nt1.hip": "iterative-ilp"}
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-Wall",
@@ -22,7 +32,8 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-Wall",
 
 def _compile(src: str, verbose: bool) -> str:
     out = os.path.join(OBJ, src + ".o")
-    cmd = [HIPCC] + COMMON + ["-c", os.path.join(CSRC, src), "-o", out]
+    sched = ["-mllvm", "-amdgpu-sched-strategy=" + SCHED[src]] if src in SCHED else []
+    cmd = [HIPCC] + COMMON + sched + ["-c", os.path.join(CSRC, src), "-o", out]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     if verbose:
