@@ -272,14 +272,20 @@ static hipError_t launch_nt_nw(const GemmArgs& a, hipStream_t s) {
 // sets (95 VGPRs with one gate/up pair, 155 with two) leave room for 5 or 3
 // waves per SIMD, so 8-wave workgroups ran their 1088 or 544 workgroups in
 // over two rounds; 4-wave ones fit one round (gate_up at 2 / 4 / 16 tokens,
-// hidden 5120: 24.8 / 25.7 / 36.0 -> 24.3 / 25.0 / 33.9 us). 4 waves for
-// more token groups (their register sets leave room for fewer waves per
-// SIMD). Row groups per workgroup: stream_groups.
+// hidden 5120: 24.8 / 25.7 / 36.0 -> 24.3 / 25.0 / 33.9 us). The W4A4
+// SwiGLU kernel also runs 4-wave workgroups above 8 tokens (gate_up at 16
+// tokens 24.1 -> 22.9 us, hidden 5120; 30.7 -> 30.2 us, hidden 7168; at 4
+// tokens they were slower, 20.4 -> 20.9 us). 4 waves for more token groups
+// (their register sets leave room for fewer waves per SIMD). Row groups per
+// workgroup: stream_groups.
 template <int MODE, int EPI, int NT>
 static hipError_t launch_nt(const GemmArgs& a, hipStream_t s) {
   constexpr bool sw = EpiTraits<EPI>::swiglu;
   if constexpr (NT == 1) {
     constexpr int kNW = MODE == kW4A16 && sw ? 4 : 8;
+    if constexpr (MODE == kW4A4 && sw) {
+      if (a.M > 8 && stream_groups(MODE, sw, a.M, a.N) == 2) return launch_nt_nw<MODE, EPI, NT, 4, 2>(a, s);
+    }
     switch (stream_groups(MODE, sw, a.M, a.N)) {
       case 1:
         if constexpr (!sw) return launch_nt_nw<MODE, EPI, NT, 8, 1>(a, s);
