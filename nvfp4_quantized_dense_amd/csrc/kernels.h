@@ -114,7 +114,8 @@ inline int splitk_ways(int64_t units, int64_t T, int64_t target, int64_t min_til
 
 // epi: Epi enum of device_common.h; mode: Mode enum.
 hipError_t launch_stream_gemm(int mode, int epi, const GemmArgs& a, hipStream_t s);
-// Its one-token-group launches (M <= 16), stream_nt1.hip.
+// Its one-token-group launches (W4A4 up to 16 tokens, W4A16 at any count),
+// stream_nt1.hip.
 hipError_t launch_stream_nt1(int mode, int epi, const GemmArgs& a, hipStream_t s);
 // LDS the W4A16 GEMV may stage token rows in (one row of K bf16 at least).
 constexpr int64_t kValuGemvLdsBytes = 65536;

@@ -1,7 +1,8 @@
-// stream_nt1.hip -- the one-token-group (up to 16 tokens) instantiations of
-// the weight-streaming kernel (stream_kernel.h). A translation unit of its
-// own so that it can be scheduled differently from the 2-4 token-group
-// kernels (build.py).
+// stream_nt1.hip -- the one-token-group instantiations of the
+// weight-streaming kernel (stream_kernel.h): W4A4 up to 16 tokens, W4A16 at
+// any count (token groups along the grid's y dimension). A translation unit
+// of its own so that it can be scheduled differently from the 2-4
+// token-group kernels (build.py).
 #include "stream_kernel.h"
 
 namespace nvfp4 {
