@@ -76,7 +76,7 @@ extern "C" {
 #define NVFP4_PATH_AUTO 0    /* choose by M */
 #define NVFP4_PATH_GEMV 1    /* decode GEMV sized for M <= 2: W4A4 on the FP4 matrix core with the
                                 blocks kept apart, W4A16 on the vector ALU (any M) */
-#define NVFP4_PATH_STREAM 2  /* weight-streaming MFMA kernel (any M, sized for M <= 64) */
+#define NVFP4_PATH_STREAM 2  /* weight-streaming MFMA kernel (any M; chosen for W4A4 M <= 128, W4A16 M <= 48) */
 #define NVFP4_PATH_TILED 3   /* LDS-tiled MFMA GEMM (any M) */
 
 /* Message of the last failed call on this thread ("" if none). */
@@ -278,7 +278,8 @@ int silu_mul_nvfp4_quant(const void* gate_up, int64_t E, int64_t M, int64_t I, c
  *   nvfp4_packed_bytes(NVFP4_REPACK_PLAIN, N, K) bytes.
  * masked_m: device int32 [E] (NULL: every row valid); alpha: device fp32 [E].
  * out: [E, M, N] of out_dtype; rows past masked_m[e] are not written.
- * One launch per expert (weight-streaming kernel for M <= 64, tiled above),
+ * One launch per expert (weight-streaming kernel for M <= 128 under W4A4 and
+ * M <= 48 under W4A16, tiled above),
  * each reading its row count on the device. Errors as nvfp4_gemm;
  * NVFP4_ERR_UNSUPPORTED when one expert's operands reach 2^31 bytes.
  */

@@ -99,14 +99,23 @@ bool stream_capturing(hipStream_t s) {
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
+// Largest token count the weight-streaming kernel takes under the
+// automatic path, from the forward measured on both paths (hidden 5120 and
+// 7168): W4A4 streaming beats the 256-token tiled kernel up to 128 tokens
+// (80: 233 against 274 us, hidden 7168; 128: 206 against 228 us, hidden
+// 5120, a tie at 7168) and loses from 144 (349 against 279 us); W4A16
+// streaming wins up to 48 (117 against 122 us) and loses at 56 (148 against
+// 124 us) to the 128-token tiled kernel.
+int64_t stream_max_m(int mode) { return mode == NVFP4_MODE_W4A4 ? 128 : 48; }
+
 // Kernel class for a GEMM of M tokens: the decode GEMV up to M = 2 (W4A4,
 // whose FP4 GEMV carries two tokens per workgroup) or M = 1 (W4A16), the
-// weight-streaming MFMA kernel up to M = 64, the LDS-tiled kernel above.
+// weight-streaming MFMA kernel up to stream_max_m, the LDS-tiled kernel above.
 int choose_path(int mode, int64_t M) {
   int p = g_path.load();
   if (p != NVFP4_PATH_AUTO) return p;
   if (M <= (mode == NVFP4_MODE_W4A4 ? 2 : 1)) return NVFP4_PATH_GEMV;
-  if (M <= 64) return NVFP4_PATH_STREAM;
+  if (M <= stream_max_m(mode)) return NVFP4_PATH_STREAM;
   return NVFP4_PATH_TILED;
 }
 
@@ -704,9 +713,10 @@ int nvfp4_grouped_gemm(int mode, const void* a, const uint8_t* a_scales, const v
     return fail(NVFP4_ERR_UNSUPPORTED, "grouped GEMM needs each expert's operands below 2^31 bytes");
   st = check_device();
   if (st) return st;
-  // One launch per expert on the weight-streaming kernel (M <= 64) or the
-  // tiled kernel, each reading its valid row count from masked_m[e].
-  const Kernel k = M <= 64 ? kStream : (mode == NVFP4_MODE_W4A4 ? kTiled2 : kTiled16);
+  // One launch per expert on the weight-streaming kernel (M <=
+  // stream_max_m) or the tiled kernel, each reading its valid row count from
+  // masked_m[e].
+  const Kernel k = M <= stream_max_m(mode) ? kStream : (mode == NVFP4_MODE_W4A4 ? kTiled2 : kTiled16);
   const int epi = out_dtype == NVFP4_DTYPE_F32 ? nvfp4::kOutF32 : nvfp4::kOutBF16;
   const size_t out_row = (size_t)N * (out_dtype == NVFP4_DTYPE_F32 ? 4 : 2);
   const size_t a_row = mode == NVFP4_MODE_W4A4 ? (size_t)K / 2 : (size_t)K * 2;

@@ -1,5 +1,5 @@
 """GPU parity of the grouped (expert) NVFP4 GEMM with masked_m against the
-CPU oracle, W4A4 and W4A16, on the weight-streaming (M <= 64) and tiled
+CPU oracle, W4A4 and W4A16, on the weight-streaming (small M) and tiled
 kernels: rows past masked_m keep the sentinel the output held, valid rows
 meet the fp32 tolerance, and each expert matches the plain GEMM entry."""
 import numpy as np
