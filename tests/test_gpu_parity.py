@@ -267,8 +267,10 @@ def test_mlp_tiny_workload(path, mode):
     _check_mlp(mode, 4, 256, 512)
 
 
-@pytest.mark.parametrize("M", [1, 7, 64, 200])
+@pytest.mark.parametrize("M", [1, 7, 48, 56, 64, 100, 128, 144, 200])
 def test_mlp_auto_dispatch(M):
+    """Token counts on both sides of each automatic switch: W4A16 streams up
+    to 48 tokens, W4A4 up to 128; the tiled kernels take over above."""
     nv.set_path(nv.PATH_AUTO)
     _check_mlp("w4a4", M, 512, 768, seed=M)
     _check_mlp("w4a16", M, 512, 768, seed=M)
@@ -281,7 +283,7 @@ def test_mlp_decode_full_size():
         _check_mlp("w4a4", 1, 5120, 17408, seed=seed, outliers=True)
 
 
-@pytest.mark.parametrize("M", [1, 4, 16, 64])
+@pytest.mark.parametrize("M", [1, 4, 16, 64, 128])
 def test_mlp_small_batch_full_size(M):
     """Fused W4A4 MLP, hidden 7168, intermediate 18432."""
     nv.set_path(nv.PATH_AUTO)
