@@ -171,7 +171,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default="decode_w4a4", choices=list(WORKLOADS) + ["silu_quant"])
+    ap.add_argument("--workload", default="decode_w4a4",
+                    choices=list(WORKLOADS) + ["silu_quant", "grouped_w4a4", "grouped_w4a16"])
+    ap.add_argument("--experts", type=int, default=8, help="experts of the grouped workloads")
     ap.add_argument("--M", type=int, default=None, help="override the token count")
     ap.add_argument("--copies", type=int, default=None, help="weight copies rotated (default >= 1 GB)")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
@@ -204,6 +206,9 @@ def main():
 
     if args.workload == "silu_quant":
         print(json.dumps(run_silu_quant(args)), flush=True)
+        return
+    if args.workload.startswith("grouped"):
+        print(json.dumps(run_grouped(args)), flush=True)
         return
     M0, H, I, mode, outliers, n_seeds0, d_steps, d_warm = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
@@ -443,6 +448,119 @@ def run_silu_quant(args):
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "k_silu_mul_quant",
                      "kernel_us": k_us, "launches_timed": steps, "algorithmic_bytes": per_bytes},
+        "cpu_baseline": cpu,
+    }
+
+
+def run_grouped(args):
+    """The grouped (expert) GEMM with masked_m: E experts' GEMMs of hidden
+    7168 -> 4096 (the gate_up of a 2048-wide expert), a capacity of M tokens
+    per expert (default 64) of which masked_m[e], drawn once from a seeded
+    generator in [1, M], are valid; W4A4 (NVFP4 activations) or W4A16 (bf16).
+    A step is one nvfp4_grouped_gemm call on bf16 output. The experts'
+    weights rotate over copies of >= 1 GB in all; algorithmic bytes are the
+    weights plus the valid rows' activations and outputs."""
+    dev = torch.device("cuda:0")
+    mode = 0 if args.workload == "grouped_w4a4" else 1
+    E, N, K = args.experts, 4096, 7168
+    M = args.M if args.M is not None else 64
+    steps = args.steps if args.steps is not None else 300
+    warmup = args.warmup if args.warmup is not None else 20
+    mm_h = np.random.default_rng(11).integers(1, M + 1, E).astype(np.int32)
+    packed, g_w = [], []
+    for e in range(E):
+        w = torch.from_numpy(synth.weights(e, N, K, synth.TENSOR_W_GATE_UP)).to(dev)
+        g, gi = nv.nvfp4_calibrate(w)
+        c, sc = nv.nvfp4_quantize(w, gi)
+        packed.append(nv.nvfp4_repack_weight(nv.REPACK_PLAIN, c, sc).reshape(-1))
+        g_w.append(g)
+        del w, c, sc
+    w0 = torch.cat(packed)
+    del packed
+    copies = args.copies or max(2, int(np.ceil(1.0e9 / w0.numel())))
+    ws = [w0] + [w0.clone() for _ in range(copies - 1)]
+    x = np.stack([synth.activations(100 + e, M, K) for e in range(E)])  # bf16 bits [E, M, K]
+    xd = bf16_tensor(x.reshape(E * M, K), dev)
+    gw = torch.cat(g_w)
+    if mode == 0:
+        g_a, gi_a = nv.nvfp4_calibrate(xd)
+        ac, asc = nv.nvfp4_quantize(xd, gi_a)
+        a, a_s = ac.reshape(E, M, K // 2), asc.reshape(E, M, K // 16)
+        alpha = (gw * g_a).contiguous()  # fp32 product per expert
+        a_row = K * NVFP4_BYTES
+    else:
+        a, a_s = xd.reshape(E, M, K), None
+        alpha = gw.contiguous()
+        a_row = K * 2
+    mm = torch.from_numpy(mm_h).to(dev)
+    out = torch.empty((E, M, N), dtype=torch.bfloat16, device=dev)
+    rows = int(mm_h.sum())
+    per_bytes = E * N * K * NVFP4_BYTES + rows * (a_row + N * 2)
+    per_flops = 2.0 * rows * N * K
+    stream = torch.cuda.current_stream()
+    log(f"[bench] workload {args.workload} E={E} M={M} N={N} K={K} valid rows {rows} copies={copies} "
+        f"steps={steps} warmup={warmup}")
+
+    def step(i):
+        nv.nvfp4_grouped_gemm(mode, a, a_s, ws[i % copies], N, K, alpha, masked_m=mm, out=out, stream=stream)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    k_us = e0.elapsed_time(e1) * 1e3 / steps
+    ms_per_step = dt * 1e3 / steps
+    achieved = per_bytes / (k_us * 1e-6) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        n_e = 2  # the oracle on the first two experts, scaled by their share of the bytes
+        wc, wsc = [], []
+        for e in range(n_e):
+            wf = synth.weights(e, N, K, synth.TENSOR_W_GATE_UP)
+            _, gi = oracle.global_scale(wf)
+            c, sc = oracle.quantize(wf, gi)
+            wc.append(c)
+            wsc.append(sc)
+        wc, wsc = np.stack(wc), np.stack(wsc)
+        if mode == 0:
+            _, gia = oracle.global_scale(x.reshape(E * M, K))
+            c, sc = oracle.quantize(x[:n_e].reshape(n_e * M, K), gia)
+            oa, oas = c.reshape(n_e, M, K // 2), sc.reshape(n_e, M, K // 16)
+        else:
+            oa, oas = x[:n_e], None
+        al = np.ones(n_e, np.float32)
+        sub_bytes = n_e * N * K * NVFP4_BYTES + int(mm_h[:n_e].sum()) * (a_row + N * 2)
+        n, t1 = 0, time.perf_counter()
+        while time.perf_counter() - t1 < args.cpu_budget:
+            oracle.grouped_gemm(mode, oa, oas, wc, wsc, mm_h[:n_e], al)
+            n += 1
+        cdt = time.perf_counter() - t1
+        cpu = {"value": sub_bytes * n / cdt / 1e9, "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+               "sample": f"{n} calls on {n_e} of {E} experts ({int(mm_h[:n_e].sum())} valid rows), {cdt:.1f} s, "
+                         f"algorithmic bytes of those experts"}
+    return {
+        "metric": "NVFP4 MLP TFLOPS + GB/s (% roofline), decode M=1..16 and prefill M=8192",
+        "value": per_bytes / (ms_per_step * 1e-3) / 1e9, "unit": "GB/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16" if mode == 0 else "bf16", "data": "synthetic",
+        "config": {"workload": f"{args.workload} E={E} M={M} N={N} K={K}", "experts": E, "M": M, "N": N, "K": K,
+                   "masked_m": mm_h.tolist(), "weight_copies": copies,
+                   "tflops": per_flops / (ms_per_step * 1e-3) / 1e12},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": f"nvfp4_grouped_gemm ({E} launches)", "kernel_us": k_us, "launches_timed": steps,
+                     "algorithmic_bytes": per_bytes, "algorithmic_flops": per_flops},
         "cpu_baseline": cpu,
     }
 

@@ -108,6 +108,10 @@ size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 // 124 us) to the 128-token tiled kernel.
 int64_t stream_max_m(int mode) { return mode == NVFP4_MODE_W4A4 ? 128 : 48; }
 
+// Largest tokens per expert a grouped GEMM runs as one streaming launch
+// over all experts under the automatic path.
+constexpr int64_t kGroupedStreamMaxM = 256;
+
 // Kernel class for a GEMM of M tokens: the decode GEMV up to M = 2 (W4A4,
 // whose FP4 GEMV carries two tokens per workgroup) or M = 1 (W4A16), the
 // weight-streaming MFMA kernel up to stream_max_m, the LDS-tiled kernel above.
@@ -713,14 +717,35 @@ int nvfp4_grouped_gemm(int mode, const void* a, const uint8_t* a_scales, const v
     return fail(NVFP4_ERR_UNSUPPORTED, "grouped GEMM needs each expert's operands below 2^31 bytes");
   st = check_device();
   if (st) return st;
-  // One launch per expert on the weight-streaming kernel (M <=
-  // stream_max_m) or the tiled kernel, each reading its valid row count from
-  // masked_m[e].
-  const Kernel k = M <= stream_max_m(mode) ? kStream : (mode == NVFP4_MODE_W4A4 ? kTiled2 : kTiled16);
   const int epi = out_dtype == NVFP4_DTYPE_F32 ? nvfp4::kOutF32 : nvfp4::kOutBF16;
   const size_t out_row = (size_t)N * (out_dtype == NVFP4_DTYPE_F32 ? 4 : 2);
   const size_t a_row = mode == NVFP4_MODE_W4A4 ? (size_t)K / 2 : (size_t)K * 2;
   hipStream_t sm = as_stream(stream);
+  // Up to kGroupedStreamMaxM tokens per expert (the path override aside):
+  // every expert in one launch of the weight-streaming kernel, grid z over
+  // the experts, each workgroup reading its expert's valid row count from
+  // masked_m. An expert's GEMM alone is too narrow to fill the CUs (4096
+  // rows: 128 workgroups streaming, 16 tiled).
+  const int p = g_path.load();
+  const bool one_launch = p == NVFP4_PATH_AUTO ? M <= kGroupedStreamMaxM : p != NVFP4_PATH_TILED;
+  if (one_launch && E > 1 && E <= 65535) {
+    nvfp4::GemmArgs g{a, a_scales, static_cast<const uint8_t*>(w_packed), M, N, K, alpha, nullptr, out, nullptr};
+    g.m_dev = masked_m;
+    g.experts = (int)E;
+    g.e_a = (int64_t)(M * a_row);
+    g.e_as = a_scales ? M * (K / 16) : 0;
+    g.e_w = (int64_t)wbytes;
+    g.e_out = (int64_t)(M * out_row);
+    hipError_t err = nvfp4::launch_stream_gemm(mode, epi, g, sm);
+    if (err != hipSuccess) return hip_status(err, "grouped_gemm launch");
+    g_err[0] = '\0';
+    return NVFP4_OK;
+  }
+  // Otherwise one launch per expert on the weight-streaming kernel (M <=
+  // stream_max_m) or the tiled kernel (always under NVFP4_PATH_TILED), each
+  // reading its valid row count from masked_m[e].
+  const Kernel tiled = mode == NVFP4_MODE_W4A4 ? kTiled2 : kTiled16;
+  const Kernel k = p == NVFP4_PATH_TILED ? tiled : (one_launch || M <= stream_max_m(mode) ? kStream : tiled);
   for (int64_t e = 0; e < E; ++e) {
     nvfp4::GemmArgs g{static_cast<const uint8_t*>(a) + (size_t)e * M * a_row,
                       a_scales ? a_scales + (size_t)e * M * (K / 16) : nullptr,

@@ -74,6 +74,12 @@ struct GemmArgs {
   // workgroup with no valid row exits at once. Weight-streaming and tiled
   // kernels, ksplit = 1.
   const int32_t* m_dev = nullptr;
+  // Grouped (expert) GEMMs in one launch of the weight-streaming kernel:
+  // when experts > 1, blockIdx.z is the expert e, and a, a_scales, w and
+  // out advance by e times these byte strides, alpha and m_dev by e
+  // elements (unsplit: ksplit = 1).
+  int experts = 0;
+  int64_t e_a = 0, e_as = 0, e_w = 0, e_out = 0;
   // W4A16 SwiGLU epilogue with bf16 h: when set, h is multiplied by the
   // next layer's AWQ pre-quant scale (bf16 [I]) and rounded again to bf16.
   const uint16_t* h_prescale = nullptr;

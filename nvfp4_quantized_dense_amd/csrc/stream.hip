@@ -32,6 +32,7 @@ static hipError_t launch_mode_epi(const GemmArgs& a, hipStream_t s) {
 hipError_t launch_stream_gemm(int mode, int epi, const GemmArgs& a, hipStream_t s) {
   if (a.M == 0) return hipSuccess;
   if (!splitk_valid(a, epi)) return hipErrorInvalidValue;
+  if (a.experts > 1 && (a.ksplit != 1 || a.experts > 65535)) return hipErrorInvalidValue;
   if (stream_one_group(mode, a.M)) return launch_stream_nt1(mode, epi, a, s);
   if (mode != kW4A4) return hipErrorInvalidValue;  // W4A16 runs one token group at every M
   switch (epi) {

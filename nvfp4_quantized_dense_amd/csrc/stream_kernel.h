@@ -145,8 +145,21 @@ __device__ __forceinline__ void stream_compute(f32x4 (&acc)[NG][NT], const Strea
 #endif  // __HIP_DEVICE_COMPILE__
 
 template <int MODE, int EPI, int NT, int NW, int G>
-__global__ __launch_bounds__(NW * 64) void k_stream(GemmArgs args) {
+__global__ __launch_bounds__(NW * 64) void k_stream(GemmArgs args_in) {
 #if defined(__HIP_DEVICE_COMPILE__)
+  GemmArgs args = args_in;
+  int kz = (int)blockIdx.z;  // K split of this workgroup
+  if (args.experts > 1) {
+    // Grouped GEMM: grid z walks the experts (each unsplit).
+    const int64_t e = blockIdx.z;
+    args.a = static_cast<const uint8_t*>(args.a) + e * args.e_a;
+    if (args.a_scales != nullptr) args.a_scales += e * args.e_as;
+    args.w += e * args.e_w;
+    args.out = static_cast<uint8_t*>(args.out) + e * args.e_out;
+    args.alpha += e;
+    if (args.m_dev != nullptr) args.m_dev += e;
+    kz = 0;
+  }
   constexpr int NG = G;
   static_assert(!EpiTraits<EPI>::swiglu || G % 2 == 0, "SwiGLU takes gate/up group pairs");
   const int lane = threadIdx.x & 63;
@@ -196,7 +209,7 @@ __global__ __launch_bounds__(NW * 64) void k_stream(GemmArgs args) {
   const int nt = (int)T;
   const int ks = args.ksplit;
   const int tper = (nt + ks - 1) / ks;
-  const int t0 = (int)blockIdx.z * tper;
+  const int t0 = kz * tper;
   const int t1 = t0 + tper < nt ? t0 + tper : nt;
   int t = t0 + wave;
   StreamTile<MODE, NG, NT> ta;
@@ -236,7 +249,7 @@ __global__ __launch_bounds__(NW * 64) void k_stream(GemmArgs args) {
     if (ks > 1) {
       const int64_t unit = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
       if (!splitk_last<NG * NT>(reinterpret_cast<f32x4(&)[NG * NT]>(acc), args.part, args.counters, ks, unit,
-                                (int)blockIdx.z, lane))
+                                kz, lane))
         return;
     }
   }
@@ -262,7 +275,8 @@ __global__ __launch_bounds__(NW * 64) void k_stream(GemmArgs args) {
 
 template <int MODE, int EPI, int NT, int NW, int G>
 static hipError_t launch_nt_nw(const GemmArgs& a, hipStream_t s) {
-  dim3 grid((unsigned)(a.N / kTileRows / G), (unsigned)((a.M + 16 * NT - 1) / (16 * NT)), (unsigned)a.ksplit);
+  dim3 grid((unsigned)(a.N / kTileRows / G), (unsigned)((a.M + 16 * NT - 1) / (16 * NT)),
+            (unsigned)(a.experts > 1 ? a.experts : a.ksplit));
   k_stream<MODE, EPI, NT, NW, G><<<grid, NW * 64, 0, s>>>(a);
   return hipGetLastError();
 }

@@ -1,6 +1,7 @@
 """GPU parity of the grouped (expert) NVFP4 GEMM with masked_m against the
-CPU oracle, W4A4 and W4A16, on the weight-streaming (small M) and tiled
-kernels: rows past masked_m keep the sentinel the output held, valid rows
+CPU oracle, W4A4 and W4A16, on the weight-streaming kernel (every expert in
+one launch) and the tiled kernels (one launch per expert): rows past
+masked_m keep the sentinel the output held, valid rows
 meet the fp32 tolerance, and each expert matches the plain GEMM entry."""
 import numpy as np
 import pytest
@@ -44,8 +45,22 @@ def _packed(wc, ws):
 @pytest.mark.parametrize("mode", [0, 1])
 @pytest.mark.parametrize("E,M,N,K,mm", [
     (3, 1, 272, 768, [1, 0, 1]), (4, 5, 272, 768, [5, 2, 0, 9]), (2, 40, 512, 1024, [40, 17]),
-    (3, 300, 288, 512, [300, 1, 129]), (2, 64, 256, 256, None)])
-def test_grouped_gemm_matches_oracle(mode, E, M, N, K, mm):
+    (3, 300, 288, 512, [300, 1, 129]), (2, 64, 256, 256, None),
+    (20, 16, 256, 512, [16, 0, 3, 16, 9, 0, 1, 12, 16, 5, 7, 0, 16, 2, 11, 16, 4, 8, 0, 15]),
+    (4, 200, 256, 512, [200, 77, 0, 130])])
+@pytest.mark.parametrize("kpath", ["auto", "tiled"])
+def test_grouped_gemm_matches_oracle(kpath, mode, E, M, N, K, mm):
+    """Under the automatic path every expert runs in one streaming launch
+    up to 256 tokens per expert (one launch per expert above); the tiled
+    override runs one tiled launch per expert."""
+    prev = nv.set_path(nv.PATH_TILED if kpath == "tiled" else nv.PATH_AUTO)
+    try:
+        _grouped_vs_oracle(mode, E, M, N, K, mm)
+    finally:
+        nv.set_path(prev)
+
+
+def _grouped_vs_oracle(mode, E, M, N, K, mm):
     ac, asc, xb, wc, ws, al = _case(E * 100 + M, E, M, N, K)
     a, sc = (ac, asc) if mode == 0 else (xb, None)
     mmv = None if mm is None else np.array(mm, np.int32)
