@@ -278,9 +278,10 @@ int silu_mul_nvfp4_quant(const void* gate_up, int64_t E, int64_t M, int64_t I, c
  *   nvfp4_packed_bytes(NVFP4_REPACK_PLAIN, N, K) bytes.
  * masked_m: device int32 [E] (NULL: every row valid); alpha: device fp32 [E].
  * out: [E, M, N] of out_dtype; rows past masked_m[e] are not written.
- * One launch per expert (weight-streaming kernel for M <= 128 under W4A4 and
- * M <= 48 under W4A16, tiled above),
- * each reading its row count on the device. Errors as nvfp4_gemm;
+ * Up to 256 tokens per expert (under NVFP4_PATH_AUTO) every expert runs in
+ * one launch of the weight-streaming kernel; above that, or under
+ * NVFP4_PATH_TILED, one tiled launch per expert. Every workgroup reads its
+ * expert's row count on the device. Errors as nvfp4_gemm;
  * NVFP4_ERR_UNSUPPORTED when one expert's operands reach 2^31 bytes.
  */
 int nvfp4_grouped_gemm(int mode, const void* a, const uint8_t* a_scales, const void* w_packed, int64_t E,
