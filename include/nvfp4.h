@@ -278,9 +278,9 @@ int silu_mul_nvfp4_quant(const void* gate_up, int64_t E, int64_t M, int64_t I, c
  *   nvfp4_packed_bytes(NVFP4_REPACK_PLAIN, N, K) bytes.
  * masked_m: device int32 [E] (NULL: every row valid); alpha: device fp32 [E].
  * out: [E, M, N] of out_dtype; rows past masked_m[e] are not written.
- * Up to 256 tokens per expert (under NVFP4_PATH_AUTO) every expert runs in
- * one launch of the weight-streaming kernel; above that, or under
- * NVFP4_PATH_TILED, one tiled launch per expert. Every workgroup reads its
+ * All experts run in one launch (0 <= E <= 65535): of the weight-streaming
+ * kernel up to 256 tokens per expert under NVFP4_PATH_AUTO, of the tiled
+ * kernel above (or under NVFP4_PATH_TILED). Every workgroup reads its
  * expert's row count on the device. Errors as nvfp4_gemm;
  * NVFP4_ERR_UNSUPPORTED when one expert's operands reach 2^31 bytes.
  */

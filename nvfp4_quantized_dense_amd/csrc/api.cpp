@@ -701,7 +701,7 @@ int mlp_forward_w4a16_awq(const uint16_t* x, int64_t M, int64_t H, int64_t I, co
 int nvfp4_grouped_gemm(int mode, const void* a, const uint8_t* a_scales, const void* w_packed, int64_t E,
                        int64_t M, int64_t N, int64_t K, const int32_t* masked_m, const float* alpha, void* out,
                        int out_dtype, void* stream) {
-  if (E < 0 || !dim_ok(E)) return fail(NVFP4_ERR_INVALID_ARG, "bad expert count %lld", (long long)E);
+  if (E < 0 || E > 65535) return fail(NVFP4_ERR_INVALID_ARG, "expert count %lld not in [0, 65535]", (long long)E);
   int st = check_gemm(mode, a, a_scales, w_packed, E == 0 ? 0 : M, N, K, alpha, out);
   if (st) return st;
   if (out_dtype != NVFP4_DTYPE_F32 && out_dtype != NVFP4_DTYPE_BF16)
@@ -721,42 +721,28 @@ int nvfp4_grouped_gemm(int mode, const void* a, const uint8_t* a_scales, const v
   const size_t out_row = (size_t)N * (out_dtype == NVFP4_DTYPE_F32 ? 4 : 2);
   const size_t a_row = mode == NVFP4_MODE_W4A4 ? (size_t)K / 2 : (size_t)K * 2;
   hipStream_t sm = as_stream(stream);
-  // Up to kGroupedStreamMaxM tokens per expert (the path override aside):
-  // every expert in one launch of the weight-streaming kernel, grid z over
-  // the experts, each workgroup reading its expert's valid row count from
-  // masked_m. An expert's GEMM alone is too narrow to fill the CUs (4096
-  // rows: 128 workgroups streaming, 16 tiled).
+  // Every expert in one launch (grid z of the weight-streaming kernel, grid
+  // y of the tiled ones), each workgroup reading its expert's valid row
+  // count from masked_m: an expert's GEMM alone is too narrow to fill the
+  // CUs (4096 rows: 128 streaming workgroups, 16 x (M / 256) tiled ones).
+  // The weight-streaming kernel up to kGroupedStreamMaxM tokens per expert
+  // (under the automatic path; always under the stream or GEMV override),
+  // the tiled kernel above (always under the tiled override).
   const int p = g_path.load();
-  const bool one_launch = p == NVFP4_PATH_AUTO ? M <= kGroupedStreamMaxM : p != NVFP4_PATH_TILED;
-  if (one_launch && E > 1 && E <= 65535) {
-    nvfp4::GemmArgs g{a, a_scales, static_cast<const uint8_t*>(w_packed), M, N, K, alpha, nullptr, out, nullptr};
-    g.m_dev = masked_m;
+  const bool streaming = p == NVFP4_PATH_AUTO ? M <= kGroupedStreamMaxM : p != NVFP4_PATH_TILED;
+  nvfp4::GemmArgs g{a, a_scales, static_cast<const uint8_t*>(w_packed), M, N, K, alpha, nullptr, out, nullptr};
+  g.m_dev = masked_m;
+  if (E > 1) {
     g.experts = (int)E;
     g.e_a = (int64_t)(M * a_row);
     g.e_as = a_scales ? M * (K / 16) : 0;
     g.e_w = (int64_t)wbytes;
     g.e_out = (int64_t)(M * out_row);
-    hipError_t err = nvfp4::launch_stream_gemm(mode, epi, g, sm);
-    if (err != hipSuccess) return hip_status(err, "grouped_gemm launch");
-    g_err[0] = '\0';
-    return NVFP4_OK;
   }
-  // Otherwise one launch per expert on the weight-streaming kernel (M <=
-  // stream_max_m) or the tiled kernel (always under NVFP4_PATH_TILED), each
-  // reading its valid row count from masked_m[e].
-  const Kernel tiled = mode == NVFP4_MODE_W4A4 ? kTiled2 : kTiled16;
-  const Kernel k = p == NVFP4_PATH_TILED ? tiled : (one_launch || M <= stream_max_m(mode) ? kStream : tiled);
-  for (int64_t e = 0; e < E; ++e) {
-    nvfp4::GemmArgs g{static_cast<const uint8_t*>(a) + (size_t)e * M * a_row,
-                      a_scales ? a_scales + (size_t)e * M * (K / 16) : nullptr,
-                      static_cast<const uint8_t*>(w_packed) + (size_t)e * wbytes,
-                      M, N, K, alpha + e, nullptr, static_cast<uint8_t*>(out) + (size_t)e * M * out_row, nullptr};
-    g.m_dev = masked_m ? masked_m + e : nullptr;
-    hipError_t err = k == kStream ? nvfp4::launch_stream_gemm(mode, epi, g, sm)
-                     : k == kTiled2 ? nvfp4::launch_tiled2_gemm(epi, g, sm)
-                                    : nvfp4::launch_tiled16_gemm(epi, g, sm);
-    if (err != hipSuccess) return hip_status(err, "grouped_gemm launch");
-  }
+  hipError_t err = streaming ? nvfp4::launch_stream_gemm(mode, epi, g, sm)
+                   : mode == NVFP4_MODE_W4A4 ? nvfp4::launch_tiled2_gemm(epi, g, sm)
+                                             : nvfp4::launch_tiled16_gemm(epi, g, sm);
+  if (err != hipSuccess) return hip_status(err, "grouped_gemm launch");
   g_err[0] = '\0';
   return NVFP4_OK;
 }

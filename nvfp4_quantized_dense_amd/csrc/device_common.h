@@ -279,6 +279,17 @@ __device__ __forceinline__ float uniform_now(const float* p) {
   return __int_as_float(v);
 }
 
+// A grouped GEMM launched once for all experts (GemmArgs.experts > 1):
+// the operands of expert e.
+__device__ __forceinline__ void expert_slice(GemmArgs& a, int64_t e) {
+  a.a = static_cast<const uint8_t*>(a.a) + e * a.e_a;
+  if (a.a_scales != nullptr) a.a_scales += e * a.e_as;
+  a.w += e * a.e_w;
+  a.out = static_cast<uint8_t*>(a.out) + e * a.e_out;
+  a.alpha += e;
+  if (a.m_dev != nullptr) a.m_dev += e;
+}
+
 // Valid token rows of a GEMM (the device-side masked row count of a grouped
 // GEMM, else M).
 __device__ __forceinline__ int64_t valid_rows(const GemmArgs& a) {

@@ -150,14 +150,7 @@ __global__ __launch_bounds__(NW * 64) void k_stream(GemmArgs args_in) {
   GemmArgs args = args_in;
   int kz = (int)blockIdx.z;  // K split of this workgroup
   if (args.experts > 1) {
-    // Grouped GEMM: grid z walks the experts (each unsplit).
-    const int64_t e = blockIdx.z;
-    args.a = static_cast<const uint8_t*>(args.a) + e * args.e_a;
-    if (args.a_scales != nullptr) args.a_scales += e * args.e_as;
-    args.w += e * args.e_w;
-    args.out = static_cast<uint8_t*>(args.out) + e * args.e_out;
-    args.alpha += e;
-    if (args.m_dev != nullptr) args.m_dev += e;
+    expert_slice(args, blockIdx.z);  // grouped GEMM: grid z walks the experts (each unsplit)
     kz = 0;
   }
   constexpr int NG = G;

@@ -151,9 +151,11 @@ __device__ __forceinline__ void compute_stage16(f32x4 (&acc)[2][8], const uint8_
 // tokens, hidden 5120). This launch covers output tiles [tile0, tile0 +
 // count); with SPLIT each of them as args.ksplit K splits.
 template <int EPI, bool SPLIT>
-__global__ __launch_bounds__(kNW16 * 64, 1) void k_tiled16(GemmArgs args, int64_t n_tiles, int64_t per_xcd,
+__global__ __launch_bounds__(kNW16 * 64, 1) void k_tiled16(GemmArgs args_in, int64_t n_tiles, int64_t per_xcd,
                                                            int64_t tile0, int64_t count) {
 #if defined(__HIP_DEVICE_COMPILE__)
+  GemmArgs args = args_in;
+  if (args.experts > 1) expert_slice(args, blockIdx.y);  // grouped GEMM: grid y walks the experts
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kStage16];
   __shared__ uint32_t arrived;
   clear_words(args.zero_ptr, args.zero_n);
@@ -240,7 +242,8 @@ template <int EPI, bool SPLIT>
 static hipError_t launch16_range(const GemmArgs& a, int64_t n_tiles, int64_t tile0, int64_t count, int ks,
                                  hipStream_t s) {
   const int64_t per_xcd = (count * ks + 7) / 8;
-  k_tiled16<EPI, SPLIT><<<(unsigned)(8 * per_xcd), kNW16 * 64, 0, s>>>(a, n_tiles, per_xcd, tile0, count);
+  const dim3 grid((unsigned)(8 * per_xcd), (unsigned)(a.experts > 1 ? a.experts : 1));
+  k_tiled16<EPI, SPLIT><<<grid, kNW16 * 64, 0, s>>>(a, n_tiles, per_xcd, tile0, count);
   return hipGetLastError();
 }
 
@@ -272,6 +275,7 @@ static hipError_t launch16_e(const GemmArgs& a, hipStream_t s) {
 // offsets); the caller checks.
 hipError_t launch_tiled16_gemm(int epi, const GemmArgs& a, hipStream_t s) {
   if (a.M == 0) return hipSuccess;
+  if (a.experts > 1 && (a.ksplit != 1 || a.experts > 65535)) return hipErrorInvalidValue;
   if (!splitk_valid(a, epi, true)) return hipErrorInvalidValue;
   switch (epi) {
     case kOutF32: return launch16_e<kOutF32>(a, s);

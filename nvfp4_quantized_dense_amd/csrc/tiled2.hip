@@ -180,9 +180,11 @@ __device__ __forceinline__ void compute_chunk(f32x4 (&acc)[GR][TG], const uint8_
 // This launch covers output tiles [tile0, tile0 + count); with SPLIT (dense
 // epilogues, args.ksplit > 1) each of them as args.ksplit K splits.
 template <int EPI, int NWR, int NWT, bool SPLIT>
-__global__ __launch_bounds__(NWR * NWT * 64, 1) void k_tiled2(GemmArgs args, int64_t m_tiles, int64_t per_xcd,
+__global__ __launch_bounds__(NWR * NWT * 64, 1) void k_tiled2(GemmArgs args_in, int64_t m_tiles, int64_t per_xcd,
                                                               int64_t tile0, int64_t count) {
 #if defined(__HIP_DEVICE_COMPILE__)
+  GemmArgs args = args_in;
+  if (args.experts > 1) expert_slice(args, blockIdx.y);  // grouped GEMM: grid y walks the experts
   constexpr int NW = NWR * NWT;
   constexpr int GR = kG / NWR;
   constexpr int TG = kTG / NWT;
@@ -282,7 +284,8 @@ static hipError_t launch_range(const GemmArgs& a, int64_t m_tiles, int64_t tile0
                                hipStream_t s) {
   constexpr int NWR = 2, NWT = 4;
   const int64_t per_xcd = (count * ks + 7) / 8;
-  k_tiled2<EPI, NWR, NWT, SPLIT><<<(unsigned)(8 * per_xcd), NWR * NWT * 64, 0, s>>>(a, m_tiles, per_xcd, tile0, count);
+  const dim3 grid((unsigned)(8 * per_xcd), (unsigned)(a.experts > 1 ? a.experts : 1));
+  k_tiled2<EPI, NWR, NWT, SPLIT><<<grid, NWR * NWT * 64, 0, s>>>(a, m_tiles, per_xcd, tile0, count);
   return hipGetLastError();
 }
 
@@ -319,6 +322,7 @@ TileShape tiled2_shape(int64_t M, int64_t N) {
 // (32-bit buffer offsets); the caller checks.
 hipError_t launch_tiled2_gemm(int epi, const GemmArgs& a, hipStream_t s) {
   if (a.M == 0) return hipSuccess;
+  if (a.experts > 1 && (a.ksplit != 1 || a.experts > 65535)) return hipErrorInvalidValue;
   if (!splitk_valid(a, epi, true)) return hipErrorInvalidValue;
   switch (epi) {
     case kOutF32: return launch_e<kOutF32>(a, s);

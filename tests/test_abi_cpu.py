@@ -122,6 +122,7 @@ def test_invalid_arguments_are_rejected_on_the_host():
     assert lib.nvfp4_grouped_gemm(0, P, N, P, 2, 4, 32, 256, N, P, P, 1, N) == INV   # W4A4 needs scales
     assert lib.nvfp4_grouped_gemm(1, P, N, P, 2, 4, 32, 256, U, P, P, 1, N) == INV   # misaligned masked_m
     assert lib.nvfp4_grouped_gemm(0, P, P, P, -1, 4, 32, 256, N, P, P, 1, N) == INV  # E < 0
+    assert lib.nvfp4_grouped_gemm(0, P, P, P, 65536, 4, 32, 256, N, P, P, 1, N) == INV  # E > 65535 (grid limit)
     assert lib.nvfp4_grouped_gemm(0, N, N, N, 0, 4, 32, 256, N, N, N, 1, N) == nv.NVFP4_OK  # no experts
     assert lib.nvfp4_set_path(9) == INV
 
