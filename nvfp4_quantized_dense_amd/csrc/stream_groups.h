@@ -15,12 +15,14 @@
 namespace nvfp4 {
 
 // W4A16 (bf16 activations: at 16 tokens a slice is 3.6 times the bytes of
-// the weight tile it multiplies): dense 2; SwiGLU 2 pairs above 8 tokens
-// (gate_up at 16 tokens, hidden 5120: 39.8 -> 35.5 us), one pair below (at
-// 2 and 4 tokens two pairs took 28.7 against 24.2 us; dense 4 was slower
-// at 2 and 4 tokens and even at 16).
+// the weight tile it multiplies): SwiGLU 2 pairs above 8 tokens (gate_up at
+// 16 tokens, hidden 5120: 39.8 -> 35.5 us), one pair below (at 2 and 4
+// tokens two pairs took 28.7 against 24.2 us); dense 4 above 16 tokens,
+// where the grid has several token-group rows (down projection at 32
+// tokens, intermediate 17408: 42.9 -> 29.7 us), 2 up to 16 (4 took 28.7
+// against 23.1 us at 16 tokens and was slower at 2 and 4).
 inline int stream_groups(int mode, bool swiglu, int64_t M, int64_t N) {
-  int g = mode == kW4A16 && swiglu && M > 8 ? 4 : 2;
+  int g = mode == kW4A16 && (swiglu ? M > 8 : M > 16) ? 4 : 2;
   while (g > (swiglu ? 2 : 1) && (N / 16) % g != 0) g /= 2;
   return g;
 }
