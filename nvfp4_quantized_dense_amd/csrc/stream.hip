@@ -15,7 +15,7 @@ static bool stream_one_group(int mode, int64_t M) { return M <= 16 || mode == kW
 TileShape stream_shape(int mode, int64_t M, int64_t N) {
   int64_t groups = (M + 15) / 16;
   const int64_t nt = stream_one_group(mode, M) ? 1 : (groups < 4 ? groups : 4);
-  const int64_t g = nt == 1 ? stream_groups(mode, false, M, N) : 1;
+  const int64_t g = nt == 1 ? stream_groups(mode, false, M, N) : ((N / kTileRows) % 2 == 0 ? 2 : 1);
   return TileShape{N / kTileRows / g * ((M + 16 * nt - 1) / (16 * nt)), 256 * nt * g, nt == 1 ? 8 : 4};
 }
 

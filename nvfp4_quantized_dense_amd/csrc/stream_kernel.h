@@ -302,7 +302,14 @@ static hipError_t launch_nt(const GemmArgs& a, hipStream_t s) {
     }
     return hipErrorInvalidValue;
   }
-  return launch_nt_nw<MODE, EPI, NT, 4, sw ? 2 : 1>(a, s);
+  // 2-4 token groups: 2 row groups per workgroup for either epilogue (the
+  // dense W4A4 down projection at 64 / 128 tokens, hidden 7168: 71.2 / 138.2
+  // -> 41.9 / 79.5 us against 1 row group); 1 when N / 16 is odd (dense only:
+  // SwiGLU row groups come in gate/up pairs).
+  if constexpr (!sw) {
+    if ((a.N / kTileRows) % 2 != 0) return launch_nt_nw<MODE, EPI, NT, 4, 1>(a, s);
+  }
+  return launch_nt_nw<MODE, EPI, NT, 4, 2>(a, s);
 }
 
 }  // namespace nvfp4
