@@ -306,8 +306,13 @@ static hipError_t launch_nt(const GemmArgs& a, hipStream_t s) {
   // dense W4A4 down projection at 64 / 128 tokens, hidden 7168: 71.2 / 138.2
   // -> 41.9 / 79.5 us against 1 row group); 1 when N / 16 is odd (dense only:
   // SwiGLU row groups come in gate/up pairs).
+  // At 2 token groups the W4A4 SwiGLU kernel takes two gate/up pairs
+  // (forward at 32 tokens 83.6 -> 79.9 us, hidden 7168; 69.7 -> 65.8 us,
+  // hidden 5120; mixed at 4 groups).
   if constexpr (!sw) {
     if ((a.N / kTileRows) % 2 != 0) return launch_nt_nw<MODE, EPI, NT, 4, 1>(a, s);
+  } else if constexpr (MODE == kW4A4 && NT == 2) {
+    if ((a.N / kTileRows) % 4 == 0) return launch_nt_nw<MODE, EPI, NT, 4, 4>(a, s);
   }
   return launch_nt_nw<MODE, EPI, NT, 4, 2>(a, s);
 }

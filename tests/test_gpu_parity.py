@@ -209,7 +209,7 @@ def test_w4a16_prefill_tiles(M):
 
 # -- fused gate_up + SwiGLU (+ NVFP4) ------------------------------------------
 
-@pytest.mark.parametrize("M", [1, 3, 16, 40, 129])
+@pytest.mark.parametrize("M", [1, 3, 16, 24, 40, 129])
 def test_swiglu_fused_requant(path, M):
     H, I = 512, 256
     w = mlp_weights(H, I, 1)
@@ -267,7 +267,7 @@ def test_mlp_tiny_workload(path, mode):
     _check_mlp(mode, 4, 256, 512)
 
 
-@pytest.mark.parametrize("M", [1, 7, 48, 56, 64, 100, 128, 144, 200])
+@pytest.mark.parametrize("M", [1, 7, 24, 48, 56, 64, 100, 128, 144, 200])
 def test_mlp_auto_dispatch(M):
     """Token counts on both sides of each automatic switch: W4A16 streams up
     to 48 tokens, W4A4 up to 128; the tiled kernels take over above."""
