@@ -48,12 +48,12 @@ def _packed(wc, ws):
     (3, 300, 288, 512, [300, 1, 129]), (2, 64, 256, 256, None),
     (20, 16, 256, 512, [16, 0, 3, 16, 9, 0, 1, 12, 16, 5, 7, 0, 16, 2, 11, 16, 4, 8, 0, 15]),
     (4, 200, 256, 512, [200, 77, 0, 130])])
-@pytest.mark.parametrize("kpath", ["auto", "tiled"])
+@pytest.mark.parametrize("kpath", ["auto", "tiled", "stream"])
 def test_grouped_gemm_matches_oracle(kpath, mode, E, M, N, K, mm):
-    """Under the automatic path every expert runs in one streaming launch
-    up to 256 tokens per expert (one launch per expert above); the tiled
-    override runs one tiled launch per expert."""
-    prev = nv.set_path(nv.PATH_TILED if kpath == "tiled" else nv.PATH_AUTO)
+    """Every expert runs in one launch: under the automatic path on the
+    weight-streaming kernel up to 256 tokens per expert and on the tiled
+    kernel above; the overrides force either kernel at any size."""
+    prev = nv.set_path({"tiled": nv.PATH_TILED, "stream": nv.PATH_STREAM}.get(kpath, nv.PATH_AUTO))
     try:
         _grouped_vs_oracle(mode, E, M, N, K, mm)
     finally:
@@ -90,3 +90,20 @@ def test_grouped_gemm_equals_plain_gemm_per_expert():
             assert np.array_equal(y[e], ye), e
     finally:
         nv.set_path(prev)
+
+
+@pytest.mark.parametrize("M", [16, 300])
+def test_grouped_gemm_bf16_output(M):
+    """bf16 output is the f32 output rounded to nearest even, on the
+    streaming (16 tokens) and tiled (300) launches, masked rows untouched."""
+    E, N, K = 3, 256, 512
+    ac, asc, xb, wc, ws, al = _case(11 + M, E, M, N, K)
+    mmv = to_dev(np.array([M, M // 3, 0], np.int32))
+    args = (0, to_dev(ac), to_dev(asc), _packed(wc, ws), N, K, to_dev(al))
+    y32 = to_host(nv.nvfp4_grouped_gemm(*args, masked_m=mmv))
+    sentinel = torch.full((E, M, N), 0x7FC1, dtype=torch.int16, device=dev()).view(torch.bfloat16)
+    y16 = nv.nvfp4_grouped_gemm(*args, masked_m=mmv, out=sentinel)
+    b = to_host(y16.view(torch.int16)).view(np.uint16)
+    for e, rows in enumerate([M, M // 3, 0]):
+        assert np.array_equal(b[e, :rows], synth.f32_to_bf16_bits(y32[e, :rows])), e
+        assert np.all(b[e, rows:] == 0x7FC1), f"expert {e}: rows past masked_m written"
