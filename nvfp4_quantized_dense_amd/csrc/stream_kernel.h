@@ -144,8 +144,14 @@ __device__ __forceinline__ void stream_compute(f32x4 (&acc)[NG][NT], const Strea
 }  // namespace
 #endif  // __HIP_DEVICE_COMPILE__
 
+// The SwiGLU kernels of 2-3 token groups are held to 3 waves per SIMD
+// (105-159 VGPRs, none spilled): the forward at 32 tokens 78.9 -> 77.5 us
+// (hidden 7168), 66.5 -> 65.1 us (hidden 5120). At 4 groups the same cap
+// spills 2-6 registers and is not applied.
 template <int MODE, int EPI, int NT, int NW, int G>
-__global__ __launch_bounds__(NW * 64) void k_stream(GemmArgs args_in) {
+__global__ __launch_bounds__(NW * 64)
+__attribute__((amdgpu_waves_per_eu((NT == 2 || NT == 3) && EpiTraits<EPI>::swiglu ? 3 : 1)))
+void k_stream(GemmArgs args_in) {
 #if defined(__HIP_DEVICE_COMPILE__)
   GemmArgs args = args_in;
   int kz = (int)blockIdx.z;  // K split of this workgroup
