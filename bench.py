@@ -10,9 +10,12 @@ Prints one JSON line. `value` is algorithmic bytes (decode workloads, GB/s)
 or algorithmic flops (prefill, TFLOP/s) per second of wall clock over the
 timed steps (no events inside them: an event record between kernels costs a
 few microseconds of idle GPU); `roofline` reports the dominant kernel (the
-fused gate_up kernel), timed with one HIP event pair around a back-to-back
-run of that kernel on the stream it runs on; `cpu_baseline` is the CPU
-oracle timed on a bounded sample of the same workload.
+single-launch decode kernel, i.e. the whole forward, at W4A4 with one token;
+otherwise the fused gate_up kernel; for the grouped and SiLU-quantize
+workloads the one call they time), measured with one HIP event pair around a
+back-to-back run of it on the stream it runs on; `cpu_baseline` is the CPU
+oracle timed on a bounded sample of the same workload. Other workloads:
+`--workload silu_quant`, `grouped_w4a4`, `grouped_w4a16`.
 """
 import argparse
 import glob
