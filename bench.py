@@ -14,7 +14,9 @@ single-launch decode kernel, i.e. the whole forward, at W4A4 with one token;
 otherwise the fused gate_up kernel; for the grouped and SiLU-quantize
 workloads the one call they time), measured with one HIP event pair around a
 back-to-back run of it on the stream it runs on; `cpu_baseline` is the CPU
-oracle timed on a bounded sample of the same workload. Other workloads:
+oracle timed on a bounded sample of the same workload; `step_us` is the
+median, p10 and p90 of per-step GPU time from an event pair around each
+step, in a second pass after the timed one. Other workloads:
 `--workload silu_quant`, `grouped_w4a4`, `grouped_w4a16`.
 """
 import argparse
@@ -118,6 +120,31 @@ def prepare_weights(H, I, dev, copies):
     return out[0], out[1], gs[0], gs[1]
 
 
+def step_percentiles(step, n, stream):
+    """Per-step GPU time in us (median, p10, p90): one HIP event pair around
+    each of n steps on the launch stream, run after the timed region."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i, (a, b) in enumerate(ev):
+        a.record(stream)
+        step(i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+    return {"median": float(np.median(t)), "p10": float(np.percentile(t, 10)),
+            "p90": float(np.percentile(t, 90)), "n": n}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(M, H, I, mode, outliers, per_step_bytes, per_step_flops, budget_s, use_flops, dyn=False,
                  awq=False):
     """The CPU oracle on a bounded sample of the workload's steps."""
@@ -166,7 +193,7 @@ def cpu_baseline(M, H, I, mode, outliers, per_step_bytes, per_step_flops, budget
         value, unit = per_step_bytes / step_s / 1e9, "GB/s"
     return {"value": value, "unit": unit, "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"{n} steps of {rows} of {M} token rows each, full MLP forward, "
-                      f"{dt:.1f} s, scaled to whole steps"}
+                      f"{dt:.1f} s, scaled to whole steps", "cpu_model": cpu_model()}
 
 
 def main():
@@ -354,6 +381,7 @@ def run_one(args, dev, M, H, I, mode, outliers, n_seeds, steps, warmup, copies, 
     roof["launches_timed"] = n_k
     roof["algorithmic_bytes"] = leg_bytes
     roof["algorithmic_flops"] = leg_flops
+    step_us = step_percentiles(step, steps, stream)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -380,6 +408,7 @@ def run_one(args, dev, M, H, I, mode, outliers, n_seeds, steps, warmup, copies, 
                    "out_dtype": "bf16", "tflops": alg["flops"] / (ms_per_step * 1e-3) / 1e12,
                    "gbs": alg["total"] / (ms_per_step * 1e-3) / 1e9},
         "roofline": roof,
+        "step_us": step_us,
         "cpu_baseline": cpu,
     }
     return res
