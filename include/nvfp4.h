@@ -37,6 +37,10 @@
  * the environment. Device pointers must be 16-byte aligned. Calls that share
  * no output buffer may run concurrently on different streams.
  *
+ * Sizes: unless an entry point below states its own limit, every row count
+ * and GEMM dimension (M, N, K, H, I, R, C) is at most 2^24 = 16,777,216; a
+ * larger size is NVFP4_ERR_INVALID_ARG.
+ *
  * Errors: every entry point returns NVFP4_OK or a negative code and leaves a
  * thread-local message for nvfp4_last_error(). Argument checks come before
  * any HIP call, so a rejected call has no effect on the device. There is no
@@ -101,7 +105,8 @@ int nvfp4_calibrate(const void* x, int x_dtype, int64_t n, float* g, float* g_in
  *   s = E4M3(sv) rounded to nearest, ties to even, saturating at 448;
  *   r = fl(g_inv / s) (0 if s == 0);  code_k = E2M1(fl(x_k * r)) rounded to
  *   nearest, ties to the even code, saturating at 6, sign kept (-0 -> 0x8).
- * x: [M, K] of x_dtype (bf16 activations, or f32 e.g. for weights); K % 16 == 0.
+ * x: [M, K] of x_dtype (bf16 activations, or f32 e.g. for weights); K % 16 == 0,
+ * M <= 2^24, K <= 2^30.
  * codes: [M, K/2] out; scales: [M, K/16] out. Bit-exact with the oracle.
  */
 int nvfp4_quantize(const void* x, int x_dtype, int64_t M, int64_t K, const float* g_inv,
@@ -114,7 +119,7 @@ int nvfp4_quantize(const void* x, int x_dtype, int64_t M, int64_t K, const float
  * t of x is calibrated on its own amax, g_t = fl(amax_t / 2688),
  * g_inv_t = fl(1 / g_t) (0 for an all-zero row, which quantizes to zeros),
  * and quantized with g_inv_t exactly as nvfp4_quantize does.
- * x [M, K] of x_dtype (finite), K % 16 == 0; codes [M, K/2], scales
+ * x [M, K] of x_dtype (finite), K % 16 == 0, M <= 2^24, K <= 2^30; codes [M, K/2], scales
  * [M, K/16] and row_g [M] (fp32 g_t, the GEMM's per-token factor) out.
  */
 int nvfp4_quantize_per_token(const void* x, int x_dtype, int64_t M, int64_t K, uint8_t* codes,
@@ -294,7 +299,8 @@ int nvfp4_grouped_gemm(int mode, const void* a, const uint8_t* a_scales, const v
  * channel `pre_quant_scale` before the W4A16 GEMM (PR #35120 report,
  * implementation breakdown item 2):
  *   out[m, k] = bf16(x[m, k] * s[k])   (exact fp32 product, rounded to nearest even)
- * x, out: bf16 [M, K] (out may be x); s: bf16 [K]; K % 8 == 0; all 16-byte
+ * x, out: bf16 [M, K] (out may be x); s: bf16 [K]; K % 8 == 0, M <= 2^24,
+ * K <= 2^30; all 16-byte
  * aligned. Feed out to nvfp4_gemm(NVFP4_MODE_W4A16, ...).
  */
 int nvfp4_prescale_bf16(const void* x, const void* s, int64_t M, int64_t K, void* out, void* stream);

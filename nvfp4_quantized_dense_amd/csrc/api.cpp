@@ -322,7 +322,7 @@ int nvfp4_quantize(const void* x, int x_dtype, int64_t M, int64_t K, const float
   if (x_dtype != NVFP4_DTYPE_BF16 && x_dtype != NVFP4_DTYPE_F32)
     return fail(NVFP4_ERR_INVALID_ARG, "x_dtype must be BF16 or F32");
   if (!dim_ok(M) || K < 0 || K > (int64_t(1) << 30) || K % 16 != 0)
-    return fail(NVFP4_ERR_INVALID_ARG, "need 0 <= M and K a multiple of 16 (M=%lld K=%lld)",
+    return fail(NVFP4_ERR_INVALID_ARG, "need 0 <= M <= 2^24 and 0 <= K <= 2^30 a multiple of 16 (M=%lld K=%lld)",
                 (long long)M, (long long)K);
   if (M * K == 0) { g_err[0] = '\0'; return NVFP4_OK; }
   if (!x || !g_inv || !codes || !scales) return fail(NVFP4_ERR_INVALID_ARG, "null pointer argument");
@@ -340,7 +340,7 @@ int nvfp4_quantize_per_token(const void* x, int x_dtype, int64_t M, int64_t K, u
   if (x_dtype != NVFP4_DTYPE_BF16 && x_dtype != NVFP4_DTYPE_F32)
     return fail(NVFP4_ERR_INVALID_ARG, "x_dtype must be BF16 or F32");
   if (!dim_ok(M) || K < 0 || K > (int64_t(1) << 30) || K % 16 != 0)
-    return fail(NVFP4_ERR_INVALID_ARG, "need 0 <= M and K a multiple of 16 (M=%lld K=%lld)",
+    return fail(NVFP4_ERR_INVALID_ARG, "need 0 <= M <= 2^24 and 0 <= K <= 2^30 a multiple of 16 (M=%lld K=%lld)",
                 (long long)M, (long long)K);
   if (M * K == 0) { g_err[0] = '\0'; return NVFP4_OK; }
   if (!x || !codes || !scales || !row_g) return fail(NVFP4_ERR_INVALID_ARG, "null pointer argument");
@@ -749,7 +749,7 @@ int nvfp4_grouped_gemm(int mode, const void* a, const uint8_t* a_scales, const v
 
 int nvfp4_prescale_bf16(const void* x, const void* s, int64_t M, int64_t K, void* out, void* stream) {
   if (!dim_ok(M) || K < 0 || K > (int64_t(1) << 30) || K % 8 != 0)
-    return fail(NVFP4_ERR_INVALID_ARG, "need 0 <= M and K a multiple of 8 (M=%lld K=%lld)", (long long)M,
+    return fail(NVFP4_ERR_INVALID_ARG, "need 0 <= M <= 2^24 and 0 <= K <= 2^30 a multiple of 8 (M=%lld K=%lld)", (long long)M,
                 (long long)K);
   if (M * K == 0) { g_err[0] = '\0'; return NVFP4_OK; }
   if (!x || !s || !out) return fail(NVFP4_ERR_INVALID_ARG, "null pointer argument");

@@ -67,6 +67,9 @@ def test_invalid_arguments_are_rejected_on_the_host():
     assert lib.nvfp4_quantize(U, 0, 4, 256, P, P, P, N) == INV                 # misaligned
     assert b"aligned" in lib.nvfp4_last_error()
     assert lib.nvfp4_quantize(N, 0, 0, 256, N, N, N, N) == nv.NVFP4_OK         # empty: no-op
+    assert lib.nvfp4_quantize(P, 0, (1 << 24) + 1, 16, P, P, P, N) == INV      # M > 2^24
+    assert b"2^24" in lib.nvfp4_last_error()
+    assert lib.nvfp4_quantize(P, 0, 1, (1 << 30) + 16, P, P, P, N) == INV     # K > 2^30
     assert lib.nvfp4_gemm(3, P, P, P, 4, 16, 256, P, P, 1, N) == INV           # mode
     assert b"mode" in lib.nvfp4_last_error()
     assert lib.nvfp4_gemm(0, P, P, P, 4, 16, 200, P, P, 1, N) == INV           # K % 256

@@ -92,6 +92,46 @@ def test_quantize_exhaustive_bf16_slot():
     assert np.array_equal(to_host(c), oc) and np.array_equal(to_host(s), os_)
 
 
+def _e4m3_grid():
+    """The 127 finite non-negative E4M3 values (bytes 0x00..0x7E), from the
+    format's definition: subnormals m/8 * 2^-6, normals (1 + m/8) * 2^(e-7)."""
+    b = np.arange(0x7F)
+    e, m = b >> 3, b & 7
+    return np.where(e == 0, m / 8 * 2.0 ** -6, (1 + m / 8) * 2.0 ** (e - 7))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_quantize_e4m3_scale_sweep(dtype):
+    """The block-scale encoder at every E4M3 value, every midpoint between
+    neighbours (ties to the even mantissa), one fp32 ulp either side of each,
+    the saturation edge above 448, the underflow range below the smallest
+    subnormal, and 200k log-uniform scales: with g_inv = 1 a block whose max
+    is fl(6 sv) gives exactly sv before rounding. The other 15 elements are
+    uniform below the max, so the element encoder runs under every scale."""
+    rng = np.random.default_rng(23)
+    v = _e4m3_grid()
+    mid = (v[:-1] + v[1:]) / 2
+    sat = np.array([448.0, 456.0, 464.0, 472.0, 480.0, 1e4])
+    base = np.concatenate([v, mid, sat]).astype(np.float32)
+    sv = np.concatenate([base, np.nextafter(base, np.float32(np.inf)),
+                         np.nextafter(base, np.float32(0)),
+                         np.exp2(rng.uniform(-13, 10, 200_000)).astype(np.float32)])
+    sv = sv[sv > 0]
+    amax = sv * np.float32(6)
+    n = amax.size
+    x = (rng.uniform(-1, 1, (n, 16)) * amax[:, None].astype(np.float64)).astype(np.float32)
+    x[np.arange(n), rng.integers(0, 16, n)] = amax * rng.choice(np.float32([-1, 1]), n)
+    if dtype == "bf16":
+        xo = synth.f32_to_bf16_bits(x)
+    else:
+        xo = x
+    for gi in [np.float32(1.0), np.float32(0.37), np.float32(2.0e3)]:
+        c, s = nv.nvfp4_quantize(to_dev(xo), scalar(gi))
+        oc, os_ = oracle.quantize(xo, gi)
+        assert np.array_equal(to_host(s), os_), f"scale bytes differ (g_inv={gi})"
+        assert np.array_equal(to_host(c), oc), f"codes differ (g_inv={gi})"
+
+
 @pytest.mark.parametrize("n,dtype", [(1, "bf16"), (4097, "bf16"), (1 << 20, "f32")])
 def test_calibrate_bit_exact(n, dtype):
     rng = np.random.default_rng(n)
