@@ -231,7 +231,7 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
-              "(this build has no multi-GPU path; see the sharding notes in DESIGN.md)")
+              "(the library has no multi-GPU path; its figure is one GPU's throughput)")
         sys.exit(2)
 
     if args.workload == "silu_quant":
