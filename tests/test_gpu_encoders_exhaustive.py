@@ -164,3 +164,25 @@ def test_e4m3_encoder_random_sample_direct():
         oc, os_ = oracle.quantize(x, gi)
         assert np.array_equal(to_host(s), os_), f"scale bytes differ (g_inv={gi})"
         assert np.array_equal(to_host(c), oc), f"codes differ (g_inv={gi})"
+
+
+def test_bf16_every_block_max_under_many_global_scales():
+    """The activation path (bf16 input): every positive finite bf16 value as a
+    block maximum, with a random sign and slot, the other 15 elements random
+    below it, under 48 global scales from 2^-40 to 2^40 (including ones whose
+    amax * g_inv overflows fp32: the scale saturates at 448)."""
+    import nvfp4_synth as synth
+    rng = np.random.default_rng(9)
+    amax = synth.bf16_bits_to_f32(np.arange(1, 0x7F80, dtype=np.uint16))
+    n = amax.size
+    x = (rng.uniform(-1, 1, (n, 16)) * amax[:, None].astype(np.float64)).astype(np.float32)
+    x[np.arange(n), rng.integers(0, 16, n)] = amax * rng.choice(np.float32([-1, 1]), n)
+    xb = synth.f32_to_bf16_bits(x)
+    xd = to_dev(xb)
+    g_invs = np.concatenate([np.float32([1.0, 0.5, 3.0, 2688.0, 1.0 / 2688.0]),
+                             np.exp2(rng.uniform(-40, 40, 43)).astype(np.float32)])
+    for gi in g_invs:
+        c, s = nv.nvfp4_quantize(xd, scalar(gi))
+        oc, os_ = oracle.quantize(xb, gi)
+        assert np.array_equal(to_host(s), os_), f"scale bytes differ (g_inv={gi!r})"
+        assert np.array_equal(to_host(c), oc), f"codes differ (g_inv={gi!r})"
