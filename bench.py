@@ -590,12 +590,16 @@ def run_grouped(args):
             oracle.grouped_gemm(mode, oa, oas, wc, wsc, mm_h[:n_e], al)
             n += 1
         cdt = time.perf_counter() - t1
-        cpu = {"value": sub_bytes * n / cdt / 1e9, "unit": "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
+        sub_flops = 2.0 * int(mm_h[:n_e].sum()) * N * K
+        cpu = {"value": (sub_flops * n / cdt / 1e12 if M >= 256 else sub_bytes * n / cdt / 1e9),
+               "unit": "TFLOP/s" if M >= 256 else "GB/s", "cores": oracle.num_threads(), "kind": "oracle",
                "sample": f"{n} calls on {n_e} of {E} experts ({int(mm_h[:n_e].sum())} valid rows), {cdt:.1f} s, "
-                         f"algorithmic bytes of those experts"}
+                         f"algorithmic {'flops' if M >= 256 else 'bytes'} of those experts"}
     return {
         "metric": "NVFP4 MLP TFLOPS + GB/s (% roofline), decode M=1..16 and prefill M=8192",
-        "value": per_bytes / (ms_per_step * 1e-3) / 1e9, "unit": "GB/s", "n_gpus": 1, "steps": steps,
+        "value": (per_flops / (ms_per_step * 1e-3) / 1e12 if M >= 256 else
+                  per_bytes / (ms_per_step * 1e-3) / 1e9),
+        "unit": "TFLOP/s" if M >= 256 else "GB/s", "n_gpus": 1, "steps": steps,
         "warmup": warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f16" if mode == 0 else "bf16", "data": "synthetic",
         "config": {"workload": f"{args.workload} E={E} M={M} N={N} K={K}", "experts": E, "M": M, "N": N, "K": K,
