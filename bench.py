@@ -18,6 +18,13 @@ oracle timed on a bounded sample of the same workload; `step_us` is the
 median, p10 and p90 of per-step GPU time from an event pair around each
 step, in a second pass after the timed one. Other workloads:
 `--workload silu_quant`, `grouped_w4a4`, `grouped_w4a16`.
+
+With no --workload, --M or --sweep the line is the one-token decode (hidden
+5120, intermediate 17408) and carries the metric's other halves as extra
+keys, each a whole result of its own (value, roofline, cpu_baseline):
+`decode_m16`, the fused small-batch MLP at 16 tokens (hidden 7168,
+intermediate 18432), and `prefill`, the 8192-token W4A4 prefill on the same
+weights.
 """
 import argparse
 import glob
@@ -145,18 +152,30 @@ def cpu_model() -> str:
     return "unknown"
 
 
+_ORACLE_WEIGHTS = {}
+
+
+def oracle_weights(H, I):
+    """The seed-0 weights quantized by the oracle (cached per shape)."""
+    import oracle
+    if (H, I) not in _ORACLE_WEIGHTS:
+        _ORACLE_WEIGHTS.clear()
+        wgu = synth.weights(0, 2 * I, H, synth.TENSOR_W_GATE_UP)
+        g_gu, gi_gu = oracle.global_scale(wgu)
+        c_gu, s_gu = oracle.quantize(wgu, gi_gu)
+        del wgu
+        wd = synth.weights(0, H, I, synth.TENSOR_W_DOWN)
+        g_d, gi_d = oracle.global_scale(wd)
+        c_d, s_d = oracle.quantize(wd, gi_d)
+        _ORACLE_WEIGHTS[(H, I)] = (g_gu, c_gu, s_gu, g_d, c_d, s_d)
+    return _ORACLE_WEIGHTS[(H, I)]
+
+
 def cpu_baseline(M, H, I, mode, outliers, per_step_bytes, per_step_flops, budget_s, use_flops, dyn=False,
                  awq=False):
     """The CPU oracle on a bounded sample of the workload's steps."""
     import oracle
-    wgu = synth.weights(0, 2 * I, H, synth.TENSOR_W_GATE_UP)
-    g_gu, gi_gu = oracle.global_scale(wgu)
-    c_gu, s_gu = oracle.quantize(wgu, gi_gu)
-    del wgu
-    wd = synth.weights(0, H, I, synth.TENSOR_W_DOWN)
-    g_d, gi_d = oracle.global_scale(wd)
-    c_d, s_d = oracle.quantize(wd, gi_d)
-    del wd
+    g_gu, c_gu, s_gu, g_d, c_d, s_d = oracle_weights(H, I)
     rows = min(M, 8)
     x0 = synth.activations(0, M, H, outliers=outliers)[:rows]
     if awq:
@@ -201,8 +220,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--workload", default="decode_w4a4",
-                    choices=list(WORKLOADS) + ["silu_quant", "grouped_w4a4", "grouped_w4a16"])
+    ap.add_argument("--workload", default=None,
+                    choices=list(WORKLOADS) + ["silu_quant", "grouped_w4a4", "grouped_w4a16"],
+                    help="default: decode_w4a4, with the decode_m16 and prefill legs in the same line")
     ap.add_argument("--experts", type=int, default=8, help="experts of the grouped workloads")
     ap.add_argument("--M", type=int, default=None, help="override the token count")
     ap.add_argument("--copies", type=int, default=None, help="weight copies rotated (default >= 1 GB)")
@@ -234,35 +254,75 @@ def main():
               "(the library has no multi-GPU path; its figure is one GPU's throughput)")
         sys.exit(2)
 
+    default_line = args.workload is None and args.M is None and args.sweep is None
+    if args.workload is None:
+        args.workload = "decode_w4a4"
     if args.workload == "silu_quant":
         print(json.dumps(run_silu_quant(args)), flush=True)
         return
     if args.workload.startswith("grouped"):
         print(json.dumps(run_grouped(args)), flush=True)
         return
-    M0, H, I, mode, outliers, n_seeds0, d_steps, d_warm = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     nv.set_path(args.path)
+    if not default_line:
+        M0 = WORKLOADS[args.workload][0]
+        Ms = [int(v) for v in args.sweep.split(",")] if args.sweep else [args.M if args.M is not None else M0]
+        for res in run_workload(args, dev, args.workload, Ms):
+            print(json.dumps(res), flush=True)
+        return
+    # The metric's three figures in one line: one-token decode (the headline
+    # fields), then 16 tokens and 8192 tokens of the hidden-7168 MLP on one
+    # set of weights.
+    res = run_workload(args, dev, "decode_w4a4", [1])[0]
+    res["decode_m16"], res["prefill"] = run_workload(args, dev, "smallbatch_w4a4", [16, 8192],
+                                                     names=["smallbatch_w4a4", "prefill_w4a4"])
+    print(json.dumps(res), flush=True)
+
+
+def run_workload(args, dev, workload, Ms, names=None):
+    """Results of the workload's MLP at each token count in Ms, on one set of
+    packed weights (names: the workload name each M is reported under)."""
+    _, H, I, mode, outliers, _, _, _ = WORKLOADS[workload]
     weight_bytes = 3 * H * I * NVFP4_BYTES
     copies = args.copies or max(1, int(np.ceil(1.0e9 / weight_bytes)))
     t = time.perf_counter()
     p_gu, p_d, g_gu, g_d = prepare_weights(H, I, dev, copies)
     log(f"[bench] weights ready in {time.perf_counter() - t:.1f}s ({copies} copies)")
-    Ms = [int(v) for v in args.sweep.split(",")] if args.sweep else [args.M if args.M is not None else M0]
-    for M in Ms:
+    out = []
+    for k, M in enumerate(Ms):
+        name = names[k] if names else workload
+        M0, _, _, _, outliers, n_seeds0, d_steps, d_warm = WORKLOADS[name]
         n_seeds = n_seeds0 if M == M0 else max(2, min(n_seeds0, (1 << 22) // max(1, M * H)))
         steps = args.steps if args.steps is not None else (d_steps if M == M0 else max(10, min(500, int(2e5 / M))))
         warmup = args.warmup if args.warmup is not None else min(d_warm, steps)
-        res = run_one(args, dev, M, H, I, mode, outliers, n_seeds, steps, warmup, copies,
-                      p_gu, p_d, g_gu, g_d)
-        print(json.dumps(res), flush=True)
+        out.append(run_one(args, name, dev, M, H, I, mode, outliers, n_seeds, steps, warmup, copies,
+                           p_gu, p_d, g_gu, g_d))
+    del p_gu, p_d
+    torch.cuda.empty_cache()
+    return out
 
 
-def run_one(args, dev, M, H, I, mode, outliers, n_seeds, steps, warmup, copies, p_gu, p_d, g_gu, g_d):
+def compute_dtype(mode, M, path):
+    """The arithmetic the dominant kernel computes in: the one-token (and
+    two-token) W4A4 decode GEMVs multiply E2M1 codes on the FP4 matrix core
+    (exact products, E4M3 scales and sums in f32); the other W4A4 kernels
+    run f16 MFMA on dequantized operands, W4A16 bf16 MFMA (or, at one token,
+    bf16 dot products on the vector ALU)."""
+    if mode == "w4a4":
+        if (path == 0 and M <= 2) or path == 1:
+            return "fp4", "E2M1 x E2M1 on the FP4 MFMA (unit E8M0 scales); E4M3 block scales and sums in f32"
+        return "f16", "f16 MFMA on dequantized q*s (exact in f16), f32 accumulation"
+    if (path == 0 and M <= 1) or path == 1:
+        return "bf16", "bf16 dot products on the vector ALU against q*s, f32 accumulation"
+    return "bf16", "bf16 MFMA on dequantized q*s (exact in bf16), f32 accumulation"
+
+
+def run_one(args, workload, dev, M, H, I, mode, outliers, n_seeds, steps, warmup, copies, p_gu, p_d, g_gu, g_d):
     out_dtype = torch.bfloat16
     alg = algorithmic(M, H, I, mode, 2)
     prefill = M >= 256
-    log(f"[bench] workload {args.workload} M={M} H={H} I={I} mode={mode} copies={copies} "
+    log(f"[bench] workload {workload} M={M} H={H} I={I} mode={mode} copies={copies} "
         f"steps={steps} warmup={warmup}")
     xs = [bf16_tensor(synth.activations(s, M, H, outliers=outliers), dev) for s in range(n_seeds)]
 
@@ -371,7 +431,7 @@ def run_one(args, dev, M, H, I, mode, outliers, n_seeds, steps, warmup, copies, 
         achieved = leg_bytes / (fused_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "traffic": None}
-    roof["traffic"] = None if dyn else recorded_traffic(args.workload, M)
+    roof["traffic"] = None if dyn else recorded_traffic(workload, M)
     if single:
         roof["kernel"] = "mlp_forward single-launch decode (k_decode_mlp)"
     else:
@@ -400,14 +460,20 @@ def run_one(args, dev, M, H, I, mode, outliers, n_seeds, steps, warmup, copies, 
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16" if mode == "w4a4" else "bf16",
+        "dtype": compute_dtype(mode, M, args.path)[0],
+        "compute": compute_dtype(mode, M, args.path)[1],
         "data": "synthetic",
-        "config": {"workload": f"{args.workload}{' per-token' if dyn else ''}{' awq' if awq else ''} M={M} H={H} I={I}",
+        "config": {"workload": f"{workload}{' per-token' if dyn else ''}{' awq' if awq else ''} M={M} H={H} I={I}",
                    "M": M, "hidden": H, "intermediate": I,
                    "mode": "w4a4_per_token" if dyn else ("w4a16_awq" if awq else mode), "seeds": n_seeds, "weight_copies": copies,
                    "out_dtype": "bf16", "tflops": alg["flops"] / (ms_per_step * 1e-3) / 1e12,
                    "gbs": alg["total"] / (ms_per_step * 1e-3) / 1e9},
         "roofline": roof,
+        "forward": {"us": ms_per_step * 1e3,
+                    "frac": (alg["total"] / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS if not prefill else
+                             alg["flops"] / (ms_per_step * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS),
+                    "of": "the whole forward's algorithmic " + ("flops" if prefill else "bytes") +
+                          " per wall-clock step against the same peak"},
         "step_us": step_us,
         "cpu_baseline": cpu,
     }

@@ -30,7 +30,7 @@
  * synchronizes with the host.
  *
  * Ownership and execution: the caller allocates every buffer (inputs,
- * outputs, packed weights sized by nvfp4_packed_bytes, workspace sized by
+ * outputs, packed weights sized by nvfp4_repack_bytes, workspace sized by
  * mlp_workspace_bytes) and keeps it alive until the work on `stream` has
  * finished. Calls are asynchronous on `stream` (a hipStream_t; NULL is the
  * default stream). The library never allocates, frees, synchronizes or reads
@@ -76,12 +76,15 @@ extern "C" {
 #define NVFP4_REPACK_PLAIN 0  /* any [R, C] weight, e.g. down_proj */
 #define NVFP4_REPACK_SWIGLU 1 /* merged gate_up [2I, C], rows [gate; up] */
 
-/* Kernel-class override for tests and benchmarks (process-wide). */
+/* Kernel-class override for tests and benchmarks (per calling thread). */
 #define NVFP4_PATH_AUTO 0    /* choose by M */
 #define NVFP4_PATH_GEMV 1    /* decode GEMV sized for M <= 2: W4A4 on the FP4 matrix core with the
                                 blocks kept apart, W4A16 on the vector ALU (any M) */
 #define NVFP4_PATH_STREAM 2  /* weight-streaming MFMA kernel (any M; chosen for W4A4 M <= 128, W4A16 M <= 48) */
 #define NVFP4_PATH_TILED 3   /* LDS-tiled MFMA GEMM (any M) */
+#define NVFP4_PATH_TILED64 4 /* the tiled GEMM with 64-bit addressing, which AUTO and the other
+                                paths run only for operands of 2^31 bytes or more (any M; no
+                                split-K; the grouped GEMM treats it as NVFP4_PATH_TILED) */
 
 /* Message of the last failed call on this thread ("" if none). */
 const char* nvfp4_last_error(void);
@@ -129,7 +132,9 @@ int nvfp4_quantize_per_token(const void* x, int x_dtype, int64_t M, int64_t K, u
  * Bytes of the packed weight for an [R, C] NVFP4 matrix: R * C * 9 / 16
  * (the codes and scales, permuted). R % 16 == 0 and C % 256 == 0; kind
  * SWIGLU also needs (R / 2) % 16 == 0. Returns 0 for invalid arguments.
+ * nvfp4_packed_bytes is the same function under an older name.
  */
+size_t nvfp4_repack_bytes(int kind, int64_t R, int64_t C);
 size_t nvfp4_packed_bytes(int kind, int64_t R, int64_t C);
 
 /*
@@ -145,7 +150,7 @@ size_t nvfp4_packed_bytes(int kind, int64_t R, int64_t C);
  *   kind SWIGLU takes rows [gate (I rows); up (I rows)] and orders row groups
  *   gate 0, up 0, gate 1, up 1, ... (groups of 16), so a pair of adjacent
  *   groups holds the gate and up rows of 16 consecutive outputs.
- * codes [R, C/2], scales [R, C/16] in; packed out (nvfp4_packed_bytes bytes).
+ * codes [R, C/2], scales [R, C/16] in; packed out (nvfp4_repack_bytes bytes).
  * Deterministic; the inputs may be freed afterwards.
  */
 int nvfp4_repack_weight(int kind, const uint8_t* codes, const uint8_t* scales, int64_t R,
@@ -219,10 +224,26 @@ int gemm_swiglu(int mode, const void* a, const uint8_t* a_scales, const void* w_
  * x's per-token scales); W4A16 holds h in bf16 (W4A16_AWQ also x', the
  * pre-scaled x). Then the split-K partial tiles and two sets of arrival
  * counters (down projection, gate_up), sized for the largest plan over the
- * kernel paths. Each region starts 256-byte aligned. At W4A4 M = 1 the
- * split region holds the single-launch decode kernel's records instead (see
+ * kernel paths. Each region starts 256-byte aligned. Last, in every mode and
+ * for every shape, a tail of 4 MiB counted back from the END of the
+ * workspace as passed (ws + ws_bytes): the status word (its last 4 bytes,
+ * mlp_workspace_status) and the single-launch decode kernel's records (see
  * mlp_forward). Returns 0 for an unknown mode or bad sizes. */
 size_t mlp_workspace_bytes(int mode, int64_t M, int64_t H, int64_t I);
+
+/* Status bits of a workspace's status word. */
+#define NVFP4_STATUS_DECODE_WAIT_EXPIRED 1u /* a single-launch decode gave up a bounded wait:
+                                               its rows of out are NaN */
+
+/*
+ * The status word of an mlp_forward workspace: the device address of its
+ * last 4 bytes (4-byte aligned), computed from the arguments alone (no HIP
+ * call); NULL if ws is NULL or ws_bytes < 512. Kernels OR status bits into
+ * it; the library never clears it. It starts as the workspace's first
+ * contents (0 in a zero-filled one); the caller reads it (after the stream
+ * has finished) and clears it when it likes.
+ */
+uint32_t* mlp_workspace_status(void* ws, size_t ws_bytes);
 
 /*
  * Dense MLP forward, the pages' fused path (PR #26626, DeepseekV2MLP.forward):
@@ -237,14 +258,19 @@ size_t mlp_workspace_bytes(int mode, int64_t M, int64_t H, int64_t I);
  * [H, I]; H % 256 == 0, I % 256 == 0. out [M, H] of out_dtype.
  * W4A4 at M = 1 under NVFP4_PATH_AUTO (and outside stream capture) runs as
  * one launch: its workgroups pass h and the down projection's partial sums
- * to each other through 64-bit records in the workspace, each tagged with a
- * 32-bit number new to the call. The workspace must therefore hold zeros the
- * first time it is used this way (every call leaves it ready for the next;
- * memory with other contents could hold a current tag by chance). Calls that
- * share a workspace must not overlap (the same holds on every path). On the
- * other paths the workspace may hold anything: the split-K counters are
- * cleared by the gate_up GEMM's first launch. NVFP4_MODE_W4A16_AWQ is not
- * accepted here (mlp_forward_w4a16_awq takes its scales).
+ * to each other through 64-bit records in the workspace's tail, each tagged
+ * with a 32-bit number new to the call. The tail must therefore hold zeros
+ * the first time it is used this way (memory with other contents could hold
+ * a current tag by chance). No other call writes the tail, so a workspace
+ * stays ready for the next decode whatever calls (of any mode, M, H and I)
+ * run in between, as long as every call on the buffer passes the same
+ * ws_bytes (the tail is placed from ws + ws_bytes). A wait of that kernel is bounded: if one ever gives up,
+ * that unit's rows of out are NaN and NVFP4_STATUS_DECODE_WAIT_EXPIRED is set
+ * in the status word. Calls that share a workspace must not overlap (the
+ * same holds on every path). Outside the tail the workspace may hold
+ * anything: the split-K counters are cleared by the gate_up GEMM's first
+ * launch. NVFP4_MODE_W4A16_AWQ is not accepted here (mlp_forward_w4a16_awq
+ * takes its scales).
  */
 int mlp_forward(int mode, const uint16_t* x, int64_t M, int64_t H, int64_t I,
                 const void* w_gu_packed, const float* alpha_gu, const void* w_d_packed,
@@ -280,7 +306,7 @@ int silu_mul_nvfp4_quant(const void* gate_up, int64_t E, int64_t M, int64_t I, c
  * a: W4A4 codes [E, M, K/2] with a_scales [E, M, K/16]; W4A16 bf16 [E, M, K]
  *   (a_scales NULL).
  * w_packed: E packed PLAIN weights [N, K] back to back, each
- *   nvfp4_packed_bytes(NVFP4_REPACK_PLAIN, N, K) bytes.
+ *   nvfp4_repack_bytes(NVFP4_REPACK_PLAIN, N, K) bytes.
  * masked_m: device int32 [E] (NULL: every row valid); alpha: device fp32 [E].
  * out: [E, M, N] of out_dtype; rows past masked_m[e] are not written.
  * All experts run in one launch (0 <= E <= 65535): of the weight-streaming
@@ -320,9 +346,19 @@ int mlp_forward_w4a16_awq(const uint16_t* x, int64_t M, int64_t H, int64_t I, co
                           const float* g_gu, const uint16_t* s_gu, const void* w_d_packed, const float* g_d,
                           const uint16_t* s_d, void* ws, size_t ws_bytes, void* out, int out_dtype, void* stream);
 
-/* Select the kernel class used by the GEMM entry points (NVFP4_PATH_*).
- * Process-wide; meant for tests and benchmarks. Returns the previous value,
- * or NVFP4_ERR_INVALID_ARG. */
+/* Test hook for the bounded waits of the single-launch decode (mlp_forward,
+ * W4A4, M = 1), for calls from the calling thread: with withhold != 0 its
+ * workgroups tag their records with a number the waiting workgroups never
+ * look for, and each wait gives up after spin_limit polls, so every wait
+ * expires, sets NVFP4_STATUS_DECODE_WAIT_EXPIRED and writes NaN, and every
+ * workgroup still exits. withhold = 0 restores normal operation. Returns
+ * NVFP4_OK, or NVFP4_ERR_INVALID_ARG for spin_limit < 1 with withhold set. */
+int nvfp4_set_decode_wait_test(int withhold, int spin_limit);
+
+/* Select the kernel class used by the GEMM entry points (NVFP4_PATH_*) for
+ * calls made from the calling thread (each thread starts at
+ * NVFP4_PATH_AUTO); meant for tests and benchmarks. Returns the previous
+ * value, or NVFP4_ERR_INVALID_ARG. */
 int nvfp4_set_path(int path);
 
 #ifdef __cplusplus

@@ -21,7 +21,7 @@ NVFP4_ERR_HIP = -3
 DTYPE_BF16, DTYPE_F32 = 0, 1
 MODE_W4A4, MODE_W4A16, MODE_W4A4_DYN, MODE_W4A16_AWQ = 0, 1, 2, 3
 REPACK_PLAIN, REPACK_SWIGLU = 0, 1
-PATH_AUTO, PATH_GEMV, PATH_STREAM, PATH_TILED = 0, 1, 2, 3
+PATH_AUTO, PATH_GEMV, PATH_STREAM, PATH_TILED, PATH_TILED64 = 0, 1, 2, 3, 4
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -35,6 +35,7 @@ SIGNATURES = {
     "nvfp4_calibrate": (_int, [_vp, _int, _i64, _vp, _vp, _vp]),
     "nvfp4_quantize": (_int, [_vp, _int, _i64, _i64, _vp, _vp, _vp, _vp]),
     "nvfp4_quantize_per_token": (_int, [_vp, _int, _i64, _i64, _vp, _vp, _vp, _vp]),
+    "nvfp4_repack_bytes": (_sz, [_int, _i64, _i64]),
     "nvfp4_packed_bytes": (_sz, [_int, _i64, _i64]),
     "nvfp4_repack_weight": (_int, [_int, _vp, _vp, _i64, _i64, _vp, _vp]),
     "nvfp4_unpack_weight": (_int, [_int, _vp, _i64, _i64, _vp, _vp, _vp]),
@@ -50,6 +51,8 @@ SIGNATURES = {
                                      _vp]),
     "nvfp4_grouped_gemm": (_int, [_int, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _int, _vp]),
     "mlp_workspace_bytes": (_sz, [_int, _i64, _i64, _i64]),
+    "mlp_workspace_status": (_vp, [_vp, _sz]),
+    "nvfp4_set_decode_wait_test": (_int, [_int, _int]),
     "mlp_forward": (_int, [_int, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                            _vp, _int, _vp]),
 }
@@ -160,15 +163,18 @@ def nvfp4_quantize_per_token(x, codes=None, scales=None, row_g=None, stream=None
     return codes, scales, row_g
 
 
-def nvfp4_packed_bytes(kind, R, C) -> int:
-    return int(lib().nvfp4_packed_bytes(int(kind), int(R), int(C)))
+def nvfp4_repack_bytes(kind, R, C) -> int:
+    return int(lib().nvfp4_repack_bytes(int(kind), int(R), int(C)))
+
+
+nvfp4_packed_bytes = nvfp4_repack_bytes
 
 
 def nvfp4_repack_weight(kind, codes, scales, packed=None, stream=None):
     """Canonical NVFP4 weight (codes [R, C/2], scales [R, C/16]) -> packed uint8."""
     _dense(codes, "codes"); _dense(scales, "scales")
     R, C = codes.shape[0], codes.shape[1] * 2
-    nbytes = nvfp4_packed_bytes(kind, R, C)
+    nbytes = nvfp4_repack_bytes(kind, R, C)
     if packed is None:
         packed = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=codes.device)
     _check("nvfp4_repack_weight", lib().nvfp4_repack_weight(int(kind), _ptr(codes), _ptr(scales), R, C,
@@ -274,6 +280,26 @@ def silu_mul_nvfp4_quant(gate_up, g_inv, masked_m=None, codes=None, scales=None,
 
 def mlp_workspace_bytes(mode, M, H, I) -> int:
     return int(lib().mlp_workspace_bytes(int(mode), int(M), int(H), int(I)))
+
+
+STATUS_DECODE_WAIT_EXPIRED = 1
+
+
+def mlp_workspace_status(ws):
+    """The workspace's status word as a 1-element int32 view of ws (its last
+    4 bytes, the address the library computes)."""
+    n = ws.numel() * ws.element_size()
+    addr = lib().mlp_workspace_status(_ptr(ws), n)
+    if not addr:
+        raise ValueError("workspace too small for a status word")
+    off = addr - ws.data_ptr()
+    return ws.view(torch.uint8)[off:off + 4].view(torch.int32)
+
+
+def set_decode_wait_test(withhold: bool, spin_limit: int = 0):
+    """Test hook: the calling thread's single-launch decodes withhold their
+    records, so every bounded wait gives up after spin_limit polls."""
+    _check("nvfp4_set_decode_wait_test", lib().nvfp4_set_decode_wait_test(int(bool(withhold)), int(spin_limit)))
 
 
 def mlp_forward(mode, x, w_gu_packed, alpha_gu, w_d_packed, alpha_d, I, g1_inv=None, g2_inv=None,

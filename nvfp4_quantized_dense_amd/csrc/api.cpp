@@ -18,7 +18,10 @@
 namespace {
 
 thread_local char g_err[512] = "";
-std::atomic<int> g_path{NVFP4_PATH_AUTO};
+thread_local int g_path = NVFP4_PATH_AUTO;  // nvfp4_set_path, per calling thread
+// nvfp4_set_decode_wait_test, per calling thread: withhold the single-launch
+// decode's records and bound its waits by this many polls (0: off).
+thread_local int g_decode_test_spins = 0;
 
 int fail(int code, const char* fmt, ...) {
   va_list ap;
@@ -116,7 +119,7 @@ constexpr int64_t kGroupedStreamMaxM = 256;
 // whose FP4 GEMV carries two tokens per workgroup) or M = 1 (W4A16), the
 // weight-streaming MFMA kernel up to stream_max_m, the LDS-tiled kernel above.
 int choose_path(int mode, int64_t M) {
-  int p = g_path.load();
+  int p = g_path;
   if (p != NVFP4_PATH_AUTO) return p;
   if (M <= (mode == NVFP4_MODE_W4A4 ? 2 : 1)) return NVFP4_PATH_GEMV;
   if (M <= stream_max_m(mode)) return NVFP4_PATH_STREAM;
@@ -136,7 +139,7 @@ bool fits_buffers(const nvfp4::GemmArgs& a, int mode) {
 enum Kernel { kFp4Gemv, kValuGemv, kStream, kTiled2, kTiled16, kTiled };
 
 Kernel select_kernel(int path, int mode, const nvfp4::GemmArgs& a) {
-  if (fits_buffers(a, mode)) {
+  if (path != NVFP4_PATH_TILED64 && fits_buffers(a, mode)) {
     if (path == NVFP4_PATH_GEMV) {
       if (mode == NVFP4_MODE_W4A4 && nvfp4::fp4_gemv_supported(a.M, a.K)) return kFp4Gemv;
       if (mode == NVFP4_MODE_W4A16 && a.K * 2 + 16 <= nvfp4::kValuGemvLdsBytes) return kValuGemv;
@@ -145,7 +148,8 @@ Kernel select_kernel(int path, int mode, const nvfp4::GemmArgs& a) {
     if (path == NVFP4_PATH_STREAM) return kStream;
     return mode == NVFP4_MODE_W4A4 ? kTiled2 : kTiled16;
   }
-  // Beyond 2^31-byte operands only the 64-bit-addressed tiled kernel runs.
+  // Beyond 2^31-byte operands only the 64-bit-addressed tiled kernel runs
+  // (and under the override that forces it at any size).
   return kTiled;
 }
 
@@ -298,9 +302,11 @@ extern "C" {
 const char* nvfp4_last_error(void) { return g_err; }
 
 int nvfp4_set_path(int path) {
-  if (path < NVFP4_PATH_AUTO || path > NVFP4_PATH_TILED)
+  if (path < NVFP4_PATH_AUTO || path > NVFP4_PATH_TILED64)
     return fail(NVFP4_ERR_INVALID_ARG, "unknown path %d", path);
-  return g_path.exchange(path);
+  const int prev = g_path;
+  g_path = path;
+  return prev;
 }
 
 int nvfp4_calibrate(const void* x, int x_dtype, int64_t n, float* g, float* g_inv, void* stream) {
@@ -370,16 +376,18 @@ int silu_mul_nvfp4_quant(const void* gate_up, int64_t E, int64_t M, int64_t I, c
                     "silu_mul_nvfp4_quant launch");
 }
 
-size_t nvfp4_packed_bytes(int kind, int64_t R, int64_t C) {
+size_t nvfp4_repack_bytes(int kind, int64_t R, int64_t C) {
   if (kind != NVFP4_REPACK_PLAIN && kind != NVFP4_REPACK_SWIGLU) return 0;
   if (R <= 0 || C <= 0 || R % 16 != 0 || C % 256 != 0 || R > kMaxDim || C > kMaxDim) return 0;
   if (kind == NVFP4_REPACK_SWIGLU && (R / 2) % 16 != 0) return 0;
   return static_cast<size_t>(R) * static_cast<size_t>(C) / 16 * 9;
 }
 
+size_t nvfp4_packed_bytes(int kind, int64_t R, int64_t C) { return nvfp4_repack_bytes(kind, R, C); }
+
 static int repack_common(int kind, const uint8_t* codes, const uint8_t* scales, int64_t R, int64_t C,
                          const void* packed, bool unpack, uint8_t* oc, uint8_t* os, void* stream) {
-  if (nvfp4_packed_bytes(kind, R, C) == 0)
+  if (nvfp4_repack_bytes(kind, R, C) == 0)
     return fail(NVFP4_ERR_INVALID_ARG,
                 "repack needs kind PLAIN/SWIGLU, R %% 16 == 0 (SWIGLU: R/2 %% 16 == 0), C %% 256 == 0 "
                 "(kind=%d R=%lld C=%lld)", kind, (long long)R, (long long)C);
@@ -500,26 +508,47 @@ static size_t mlp_act_bytes(int mode, size_t m, int64_t H, int64_t I) {
   return align256(m * I * 2);
 }
 
-// Records of the single-launch W4A4 decode kernel.
+// Records of the single-launch W4A4 decode kernel (0 where it cannot run).
 static size_t decode_bytes(int64_t H, int64_t I) {
+  if (!nvfp4::decode_supported(H, I)) return 0;
   return align256((size_t)nvfp4::decode_record_words(H, I) * sizeof(uint64_t));
 }
 
-// Split-K part: sized for the largest plan over the kernels of every path
-// (and, at W4A4 M = 1, for the single-launch decode kernel's records), so
-// the size does not depend on the process-wide path override.
-// Split-K partials and counters of the largest plan over the paths, or the
-// single-launch decode records where that kernel may run.
-static size_t mlp_split_bytes(int mode, int64_t M, int64_t H, int64_t I, bool decode) {
+// The tail of every mlp_forward workspace, counted from the END of the
+// buffer as the caller passes it (ws + ws_bytes): the status word in its
+// last 4 bytes and, 256 bytes before it, the single-launch decode kernel's
+// records. Its size is the same for every mode, token count and shape, so no
+// other call on a buffer shared with the same ws_bytes writes there, and the
+// records stay as the decode launches leave them. 4 MiB holds the records of
+// every shape the decode kernel takes (its LDS bounds H and I by 61440 and
+// its 31-bit offsets H * I by 1.9e9: at most 3.98 MB) plus the status word
+// and the records' alignment; decode_in_tail checks it per shape.
+constexpr size_t kTailBytes = size_t(4) << 20;
+static size_t tail_bytes(int64_t, int64_t) { return kTailBytes; }
+static bool decode_in_tail(int64_t H, int64_t I) {
+  return nvfp4::decode_supported(H, I) && decode_bytes(H, I) + 512 <= kTailBytes;
+}
+
+static uint32_t* tail_status(void* ws, size_t ws_bytes) {
+  return reinterpret_cast<uint32_t*>((reinterpret_cast<uintptr_t>(ws) + ws_bytes - 4) & ~uintptr_t(3));
+}
+
+static uint64_t* tail_records(void* ws, size_t ws_bytes, int64_t H, int64_t I) {
+  const uintptr_t end = reinterpret_cast<uintptr_t>(ws) + ws_bytes;
+  return reinterpret_cast<uint64_t*>((end - 256 - decode_bytes(H, I)) & ~uintptr_t(255));
+}
+
+// Split-K partials and counters of the largest plan over the kernels of
+// every path, so the size does not depend on the path override.
+static size_t mlp_split_bytes(int mode, int64_t M, int64_t H, int64_t I) {
   size_t most = 0;
-  for (int path : {NVFP4_PATH_GEMV, NVFP4_PATH_STREAM, NVFP4_PATH_TILED}) {
+  for (int path : {NVFP4_PATH_GEMV, NVFP4_PATH_STREAM, NVFP4_PATH_TILED, NVFP4_PATH_TILED64}) {
     // The two GEMMs share the partials region (they run one after the
     // other) and have counters of their own.
     const SplitPlan d = split_plan(mlp_kernel(path, mode, M, H, I), mode, M, H, I, false);
     const SplitPlan g = split_plan(mlp_kernel(path, mode, M, 2 * I, H), mode, M, 2 * I, H, true);
     most = std::max(most, std::max(d.part_bytes, g.part_bytes) + d.counter_bytes + g.counter_bytes);
   }
-  if (decode && M == 1 && nvfp4::decode_supported(H, I)) most = std::max(most, decode_bytes(H, I));
   return most;
 }
 
@@ -531,8 +560,19 @@ size_t mlp_workspace_bytes(int mode, int64_t M, int64_t H, int64_t I) {
   // W4A4_DYN runs the W4A4 GEMM kernels, never the single-launch decode
   // one; W4A16_AWQ the W4A16 ones.
   const int kmode = (mode == NVFP4_MODE_W4A16 || mode == NVFP4_MODE_W4A16_AWQ) ? NVFP4_MODE_W4A16 : NVFP4_MODE_W4A4;
-  return mlp_act_bytes(mode, static_cast<size_t>(M), H, I) +
-         mlp_split_bytes(kmode, M, H, I, mode == NVFP4_MODE_W4A4);
+  return mlp_act_bytes(mode, static_cast<size_t>(M), H, I) + mlp_split_bytes(kmode, M, H, I) + tail_bytes(H, I);
+}
+
+uint32_t* mlp_workspace_status(void* ws, size_t ws_bytes) {
+  if (!ws || ws_bytes < 512) return nullptr;
+  return tail_status(ws, ws_bytes);
+}
+
+int nvfp4_set_decode_wait_test(int withhold, int spin_limit) {
+  if (withhold && spin_limit < 1) return fail(NVFP4_ERR_INVALID_ARG, "spin_limit must be positive");
+  g_decode_test_spins = withhold ? spin_limit : 0;
+  g_err[0] = '\0';
+  return NVFP4_OK;
 }
 
 }  // extern "C"
@@ -632,10 +672,17 @@ static int mlp_forward_impl(int mode, const uint16_t* x, int64_t M, int64_t H, i
     // One token under the automatic path: the whole forward in one launch
     // (x quantized as it is staged, h handed from the gate_up workgroups to
     // the down workgroups as epoch-tagged records in the workspace).
-    if (M == 1 && g_path.load() == NVFP4_PATH_AUTO && nvfp4::decode_supported(H, I) && !stream_capturing(s)) {
+    if (M == 1 && g_path == NVFP4_PATH_AUTO && decode_in_tail(H, I) && !stream_capturing(s)) {
       nvfp4::DecodeArgs d{x, g1_inv, static_cast<const uint8_t*>(w_gu_packed), static_cast<const uint8_t*>(w_d_packed),
-                          alpha_gu, alpha_d, g2_inv, hq, hs, out, reinterpret_cast<uint64_t*>(split_base),
-                          H, I, nvfp4::decode_splits(H, I), next_epoch()};
+                          alpha_gu, alpha_d, g2_inv, hq, hs, out, tail_records(ws, ws_bytes, H, I),
+                          H, I, nvfp4::decode_splits(H, I), next_epoch(), tail_status(ws, ws_bytes),
+                          nvfp4::kDecodeSpinLimit, 0u};
+      if (g_decode_test_spins > 0) {
+        // Test hook: producers tag with the epoch's top bit flipped, a tag
+        // the epoch counter reaches only 2^31 launches later.
+        d.spin_limit = g_decode_test_spins;
+        d.tag_skew = 0x80000000u;
+      }
       return hip_status(nvfp4::launch_decode_mlp(epi_out, d, s), "mlp_forward decode");
     }
     // At M = 1 the decode GEMV quantizes x itself as it stages it (no
@@ -708,7 +755,7 @@ int nvfp4_grouped_gemm(int mode, const void* a, const uint8_t* a_scales, const v
     return fail(NVFP4_ERR_INVALID_ARG, "out_dtype must be F32 or BF16");
   if (reinterpret_cast<uintptr_t>(masked_m) % 4) return fail(NVFP4_ERR_INVALID_ARG, "masked_m must be 4-byte aligned");
   if (M == 0 || E == 0) { g_err[0] = '\0'; return NVFP4_OK; }
-  const size_t wbytes = nvfp4_packed_bytes(NVFP4_REPACK_PLAIN, N, K);
+  const size_t wbytes = nvfp4_repack_bytes(NVFP4_REPACK_PLAIN, N, K);
   nvfp4::GemmArgs probe{};
   probe.M = M;
   probe.N = N;
@@ -728,8 +775,9 @@ int nvfp4_grouped_gemm(int mode, const void* a, const uint8_t* a_scales, const v
   // The weight-streaming kernel up to kGroupedStreamMaxM tokens per expert
   // (under the automatic path; always under the stream or GEMV override),
   // the tiled kernel above (always under the tiled override).
-  const int p = g_path.load();
-  const bool streaming = p == NVFP4_PATH_AUTO ? M <= kGroupedStreamMaxM : p != NVFP4_PATH_TILED;
+  const int p = g_path;
+  const bool streaming =
+      p == NVFP4_PATH_AUTO ? M <= kGroupedStreamMaxM : (p != NVFP4_PATH_TILED && p != NVFP4_PATH_TILED64);
   nvfp4::GemmArgs g{a, a_scales, static_cast<const uint8_t*>(w_packed), M, N, K, alpha, nullptr, out, nullptr};
   g.m_dev = masked_m;
   if (E > 1) {

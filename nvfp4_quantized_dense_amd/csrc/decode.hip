@@ -1,10 +1,10 @@
 // decode.hip -- the W4A4 MLP forward of one token in a single launch:
 // NVFP4 quantization of x, gate_up GEMV + SiLU(gate) * up + NVFP4
-// re-quantization of h, and the down projection GEMV (DeepseekV2MLP.forward
-// on the quantized path, PR #26626; NVFP4 arithmetic as in the NVFP4 format
-// description, "How NVFP4 works"), with no kernel boundary between the two
-// GEMVs: the down projection's weight loads start while the gate_up GEMV is
-// still streaming its own.
+// re-quantization of h, and the down projection GEMV (the quantized
+// DeepseekV2MLP.forward of the sglang PR #26626 digest, key source
+// snippets; the NVFP4 encoding is the one nvfp4_quantize documents), with no
+// kernel boundary between the two GEMVs: the down projection's weight loads
+// start while the gate_up GEMV is still streaming its own.
 //
 // Two kinds of workgroup, by index:
 //   * gate_up units, workgroups [0, I / 16): unit i is the FP4 GEMV of gate
@@ -34,7 +34,7 @@
 // workgroups are running or done whatever the number of resident ones. The
 // waits are bounded all the same: one that runs out (which no schedule of
 // the hardware produces) writes NaN for the rows of that unit instead of
-// hanging.
+// hanging, and sets kDecodeWaitExpired in the status word for the host.
 #include <algorithm>
 
 #include "fp4_tile.h"
@@ -45,7 +45,6 @@ namespace {
 constexpr int kDecodeWaves = 4;
 constexpr int kDownSets = 4;         // weight tiles per wave in flight in a down unit
 constexpr int kPollWords = 8;        // record words per thread a down unit can poll
-constexpr int kSpinLimit = 1 << 20;  // polls of a wait (each at least a memory round trip)
 // K tiles per down split aimed at: all of a split's weight tiles in the
 // wave's registers (kDownSets per wave) before the wait for h.
 constexpr int kSplitTiles = kDownSets * kDecodeWaves;
@@ -57,6 +56,9 @@ __device__ __forceinline__ void put_record(uint64_t* p, uint32_t data, uint32_t 
 }
 __device__ __forceinline__ uint64_t get_record(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void report_expired(uint32_t* status) {
+  __hip_atomic_fetch_or(status, kDecodeWaitExpired, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 }  // namespace
 
@@ -72,7 +74,8 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void k_decode_mlp(DecodeArgs d) 
   __shared__ float red[NW * 2 * 16];
   const int64_t nA = d.I / kTileRows;
   const bool lvalid = (lane & 15) == 0;  // lanes holding token 0
-  const uint32_t tag = (uint32_t)d.epoch;
+  const uint32_t tag = (uint32_t)d.epoch;  // the tag every wait looks for
+  const uint32_t ptag = tag ^ d.tag_skew;  // the tag records are written with
   // Records: h codes as 32-bit words (unit u: words 2 u, 2 u + 1 = code
   // bytes 0..3 and 4..7 of its block), then h scales (word u: the scale
   // byte), then the down units' partial sums (unit j, row k: word j * 16 + k).
@@ -97,9 +100,9 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void k_decode_mlp(DecodeArgs d) 
     if (lane == 0) {
       const uint32_t lo = (b.codes & 0xFFFFu) | (c16 << 16), hi = (c32 & 0xFFFFu) | (c48 << 16);
       const int64_t i = blockIdx.x;
-      put_record(rec_codes + 2 * i, lo, tag);
-      put_record(rec_codes + 2 * i + 1, hi, tag);
-      put_record(rec_scales + i, b.scale, tag);
+      put_record(rec_codes + 2 * i, lo, ptag);
+      put_record(rec_codes + 2 * i + 1, hi, ptag);
+      put_record(rec_scales + i, b.scale, ptag);
       reinterpret_cast<uint32_t*>(d.h_codes)[2 * i] = lo;
       reinterpret_cast<uint32_t*>(d.h_codes)[2 * i + 1] = hi;
       d.h_scales[i] = (uint8_t)b.scale;
@@ -155,7 +158,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void k_decode_mlp(DecodeArgs d) 
         }
       }
       if (!__syncthreads_or(pending != 0)) break;
-      if (spin >= kSpinLimit) {
+      if (spin >= d.spin_limit) {
         timed_out = true;
         break;
       }
@@ -182,12 +185,15 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void k_decode_mlp(DecodeArgs d) 
   f32x4 res[1];
   if (!f4_reduce<1, 1, NW>(acc, red, wave, lane, lvalid, res)) return;
   // timed_out is uniform (every thread took the same exit of the poll).
-  if (timed_out) res[0] = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+  if (timed_out) {
+    res[0] = f32x4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+    if (tid == 0) report_expired(d.status);
+  }
   const int64_t row0 = r * kTileRows + 4 * q;
   if (s < d.ksplit - 1) {
     if (lvalid) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) put_record(rec_part + j * 16 + 4 * q + k, __float_as_uint(res[0][k]), tag);
+      for (int k = 0; k < 4; ++k) put_record(rec_part + j * 16 + 4 * q + k, __float_as_uint(res[0][k]), ptag);
     }
     return;
   }
@@ -207,8 +213,9 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void k_decode_mlp(DecodeArgs d) 
           }
         }
         if (__all(ok)) break;
-        if (spin >= kSpinLimit) {
+        if (spin >= d.spin_limit) {
           v[0] = v[1] = v[2] = v[3] = __float_as_uint(__builtin_nanf(""));
+          if (lane == 0) report_expired(d.status);
           break;
         }
         __builtin_amdgcn_s_sleep(1);
@@ -254,7 +261,8 @@ bool decode_supported(int64_t H, int64_t I) {
 int64_t decode_record_words(int64_t H, int64_t I) { return 3 * (I / kTileRows) + H * kDecodeMaxSplits; }
 
 hipError_t launch_decode_mlp(int epi, const DecodeArgs& d, hipStream_t s) {
-  if (!decode_supported(d.H, d.I) || !split_ok(d.I, d.ksplit) || (uint32_t)d.epoch == 0u)
+  if (!decode_supported(d.H, d.I) || !split_ok(d.I, d.ksplit) || (uint32_t)d.epoch == 0u || !d.records ||
+      !d.status || d.spin_limit < 1)
     return hipErrorInvalidValue;
   const int T = (int)(d.I / kTileK), per = (T + d.ksplit - 1) / d.ksplit;
   const int64_t grid = d.I / kTileRows + d.H / kTileRows * d.ksplit;

@@ -171,7 +171,13 @@ struct DecodeArgs {
   int64_t H, I;
   int ksplit;             // decode_splits(H, I), or another count the launcher accepts
   uint64_t epoch;         // low 32 bits nonzero, differing from the last 2^32 - 1 launches' on records
+  uint32_t* status;       // OR-ed with kDecodeWaitExpired by a unit whose bounded wait gave up
+  int spin_limit;         // polls of one wait before it gives up (kDecodeSpinLimit)
+  uint32_t tag_skew;      // 0; nonzero only to test the expired wait: producers then tag their
+                          // records (epoch ^ tag_skew), which no consumer waits for
 };
+constexpr uint32_t kDecodeWaitExpired = 1;
+constexpr int kDecodeSpinLimit = 1 << 20;
 bool decode_supported(int64_t H, int64_t I);
 int decode_splits(int64_t H, int64_t I);
 int64_t decode_record_words(int64_t H, int64_t I);

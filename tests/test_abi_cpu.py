@@ -15,14 +15,15 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def declared_functions():
     src = open(os.path.join(ROOT, "include", "nvfp4.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:int|size_t|char\s*\*|const char\s*\*)\s*\**\s*"
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:int|size_t|uint32_t|char\s*\*|const char\s*\*)\s*\**\s*"
                                  r"([a-z_0-9]+)\s*\(", src, flags=re.M)))
 
 
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["nvfp4_quantize", "nvfp4_gemm", "gemm_swiglu_nvfp4_quant", "mlp_forward",
-              "nvfp4_repack_weight", "nvfp4_packed_bytes", "nvfp4_last_error"]:
+              "nvfp4_repack_weight", "nvfp4_repack_bytes", "nvfp4_packed_bytes", "nvfp4_last_error",
+              "mlp_workspace_bytes", "mlp_workspace_status"]:
         assert n in names, names
 
 
@@ -40,15 +41,61 @@ def test_packed_and_workspace_sizes():
     assert nv.nvfp4_packed_bytes(nv.REPACK_PLAIN, 16, 128) == 0       # cols % 256
     assert nv.nvfp4_packed_bytes(nv.REPACK_SWIGLU, 48, 256) == 0      # half not % 16
     assert nv.nvfp4_packed_bytes(7, 16, 256) == 0
+    assert nv.nvfp4_repack_bytes(nv.REPACK_PLAIN, 5120, 17408) == 5120 * 17408 * 9 // 16
+
+    def tail(H, I):
+        # the same 4 MiB for every shape: the status word and the
+        # single-launch decode's records (3 words per 16 elements of h, 8
+        # splits x 16-row partials: 354 KB at hidden 5120)
+        words = 3 * I // 16 + 8 * H
+        assert 512 + words * 8 <= 4 << 20
+        return 4 << 20
+
     w = nv.mlp_workspace_bytes(nv.MODE_W4A4, 1, 5120, 17408)
-    assert w >= 2560 + 320 + 8704 + 1088 and w % 256 == 0
-    assert nv.mlp_workspace_bytes(nv.MODE_W4A16, 4, 256, 512) == 4 * 512 * 2
+    # x 2560 + 320 -> 512, h 8704 -> 8960, 1088 -> 1280, then the largest
+    # split-K plan over the paths, then the tail
+    assert w >= 2560 + 512 + 8960 + 1280 + tail(5120, 17408) and w % 256 == 0
+    assert nv.mlp_workspace_bytes(nv.MODE_W4A16, 4, 256, 512) == 4 * 512 * 2 + tail(256, 512)
     assert nv.mlp_workspace_bytes(9, 1, 256, 512) == 0
     # W4A4_DYN: the W4A4 activations, then one fp32 g per token
     # x codes 512, x scales 64 -> 256, h codes 1024, h scales 128 -> 256, g 16 -> 256
-    assert nv.mlp_workspace_bytes(nv.MODE_W4A4_DYN, 4, 256, 512) == 512 + 256 + 1024 + 256 + 256
+    assert nv.mlp_workspace_bytes(nv.MODE_W4A4_DYN, 4, 256, 512) == 512 + 256 + 1024 + 256 + 256 + tail(256, 512)
     assert nv.mlp_workspace_bytes(nv.MODE_W4A4_DYN, 1000, 256, 512) >= \
         nv.mlp_workspace_bytes(nv.MODE_W4A4, 1000, 256, 512) + 4000
+    # the tail comes after everything a call of any token count writes, so a
+    # buffer sized for many tokens holds the same tail at its end
+    for M in (1, 16, 256, 4096):
+        for mode in (nv.MODE_W4A4, nv.MODE_W4A16, nv.MODE_W4A4_DYN, nv.MODE_W4A16_AWQ):
+            assert nv.mlp_workspace_bytes(mode, M, 7168, 18432) >= tail(7168, 18432) + M * 7168 // 2
+
+
+def test_workspace_status_address():
+    lib = nv.lib()
+    base = 0x7F0000000000
+    for n in (512, 4096, 4099, 1 << 20):
+        a = lib.mlp_workspace_status(ctypes.c_void_p(base), n)
+        assert a == (base + n - 4) & ~3
+    assert lib.mlp_workspace_status(ctypes.c_void_p(base), 511) is None
+    assert lib.mlp_workspace_status(None, 4096) is None
+
+
+def test_decode_wait_test_hook_arguments():
+    lib = nv.lib()
+    assert lib.nvfp4_set_decode_wait_test(1, 0) == nv.NVFP4_ERR_INVALID_ARG
+    assert lib.nvfp4_set_decode_wait_test(1, 16) == nv.NVFP4_OK
+    assert lib.nvfp4_set_decode_wait_test(0, 0) == nv.NVFP4_OK
+
+
+def test_path_override_is_per_thread():
+    import threading
+    assert nv.set_path(nv.PATH_TILED64) == nv.PATH_AUTO
+    seen = []
+    t = threading.Thread(target=lambda: seen.append(nv.set_path(nv.PATH_AUTO)))
+    t.start()
+    t.join()
+    assert seen == [nv.PATH_AUTO]           # another thread starts at AUTO
+    assert nv.set_path(nv.PATH_AUTO) == nv.PATH_TILED64
+    assert nv.lib().nvfp4_set_path(5) == nv.NVFP4_ERR_INVALID_ARG
 
 
 def _code(fn, *args):
@@ -119,7 +166,8 @@ def test_invalid_arguments_are_rejected_on_the_host():
     assert lib.mlp_forward_w4a16_awq(P, 4, 256, 512, P, P, N, P, P, P, P, ws, P, 1, N) == INV  # null s_gu
     assert lib.mlp_forward_w4a16_awq(P, 4, 256, 512, P, P, P, P, P, U, P, ws, P, 1, N) == INV  # misaligned s_d
     assert lib.mlp_forward(3, P, 4, 256, 512, P, P, P, P, N, N, P, ws, P, 1, N) == INV  # AWQ through mlp_forward
-    assert nv.mlp_workspace_bytes(nv.MODE_W4A16_AWQ, 4, 256, 512) == 4 * 512 * 2 + 4 * 256 * 2
+    assert nv.mlp_workspace_bytes(nv.MODE_W4A16_AWQ, 4, 256, 512) == \
+        nv.mlp_workspace_bytes(nv.MODE_W4A16, 4, 256, 512) + 4 * 256 * 2
     # grouped GEMM
     assert lib.nvfp4_grouped_gemm(0, P, P, P, 2, 4, 24, 256, N, P, P, 1, N) == INV   # N % 16
     assert lib.nvfp4_grouped_gemm(0, P, N, P, 2, 4, 32, 256, N, P, P, 1, N) == INV   # W4A4 needs scales

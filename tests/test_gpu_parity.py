@@ -30,7 +30,9 @@ def _lib():
     nv.set_path(nv.PATH_AUTO)
 
 
-PATHS = {"gemv": 1, "stream": 2, "tiled": 3}
+# "tiled64" forces the 64-bit-addressed tiled kernel, which the other paths
+# run only for operands of 2^31 bytes or more.
+PATHS = {"gemv": 1, "stream": 2, "tiled": 3, "tiled64": 4}
 
 
 @pytest.fixture(params=list(PATHS))
@@ -142,6 +144,16 @@ def test_calibrate_bit_exact(n, dtype):
     assert to_host(g)[0] == og and to_host(gi)[0] == ogi
 
 
+def test_calibrate_golden_non_power_of_two():
+    """g and g_inv at the hand-worked amax values (tests/golden), on the GPU."""
+    from golden_fixtures import global_scale_examples
+    for amax, g_ref, gi_ref, _ in global_scale_examples():
+        x = np.array([0.25, -amax, 1.0, 2.0], np.float32)
+        for xo in (x, synth.f32_to_bf16_bits(x)):
+            g, gi = nv.nvfp4_calibrate(to_dev(xo))
+            assert to_host(g)[0] == g_ref and to_host(gi)[0] == gi_ref, amax
+
+
 @pytest.mark.parametrize("kind,R,C", [(0, 16, 256), (0, 5120, 512), (1, 32, 256), (1, 1024, 768)])
 def test_repack_round_trip(kind, R, C):
     rng = np.random.default_rng(R + C)
@@ -177,6 +189,45 @@ def test_gemm_matches_oracle(path, M, mode):
                        to_dev(as_) if mode == "w4a4" else None, p, N, K, scalar(alpha),
                        out_dtype=torch.bfloat16)
     assert np.array_equal(to_host(yb), synth.f32_to_bf16_bits(to_host(y)))
+
+
+def _full_range_scales(rng, R, K, which):
+    """Scale bytes over the finite E4M3 range: 'all' draws 0x00..0x7E
+    uniformly (zero, the subnormals 0x01..0x07 and the saturated 0x7E among
+    them); 'low' keeps to 0x00..0x0F (zero, subnormals, the smallest
+    normals); 'high' to 0x70..0x7E. Each kind also holds its edge bytes."""
+    lo, hi, edge = {"all": (0, 0x7F, [0x00, 0x01, 0x07, 0x08, 0x7E]),
+                    "low": (0, 0x10, [0x00, 0x01, 0x07, 0x0F]),
+                    "high": (0x70, 0x7F, [0x70, 0x7E])}[which]
+    s = rng.integers(lo, hi, (R, K // 16), dtype=np.uint8)
+    s.flat[:len(edge)] = edge
+    return s
+
+
+@pytest.mark.parametrize("M", [1, 2, 5, 17, 130])
+@pytest.mark.parametrize("mode", ["w4a4", "w4a16"])
+def test_gemm_full_scale_byte_range(path, M, mode):
+    """Scale bytes over 0x00..0x7E on both operands: uniform over the range,
+    and low weight scales (subnormal) against high activation scales and the
+    reverse, so that blocks with subnormal scales carry as much of the sum as
+    any other."""
+    rng = np.random.default_rng(900 + M)
+    N, K = 272, 768
+    for wk, ak in [("all", "all"), ("low", "high"), ("high", "low")]:
+        wc = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+        ws = _full_range_scales(rng, N, K, wk)
+        p = nv.nvfp4_repack_weight(0, to_dev(wc), to_dev(ws))
+        alpha = np.float32(0.0173)
+        if mode == "w4a4":
+            ac = rng.integers(0, 256, (M, K // 2), dtype=np.uint8)
+            as_ = _full_range_scales(rng, M, K, ak)
+            ref = oracle.gemm_w4a4(ac, as_, wc, ws, alpha)
+            y = nv.nvfp4_gemm(0, to_dev(ac), to_dev(as_), p, N, K, scalar(alpha))
+        else:
+            x = synth.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+            ref = oracle.gemm_w4a16(x, wc, ws, alpha)
+            y = nv.nvfp4_gemm(1, to_dev(x), None, p, N, K, scalar(alpha))
+        gemm_close(to_host(y), ref, f"{path} {mode} M={M} scales w={wk} a={ak}")
 
 
 @pytest.mark.parametrize("M", [1, 4, 33])
@@ -325,12 +376,22 @@ def test_mlp_decode_full_size():
     w = mlp_weights(H, I, 0)
     p_gu, p_d = packed_weights(H, I, 0)
     sc = calibrate_activation_scales(synth.activations(0, 1, H, outliers=True), w)
+    ws = torch.zeros(nv.mlp_workspace_bytes(0, 1, H, I), dtype=torch.uint8, device=dev())
+    n_diff = 0
     for seed in list(range(0, 1000, 50)) + [1, 999]:
         x = synth.activations(seed, 1, H, outliers=True)
-        y = to_host(_run_mlp("w4a4", x, w, sc, p_gu, p_d))
+        y = to_host(nv.mlp_forward(0, to_dev(x), p_gu, scalar(sc["a_gu"]), p_d, scalar(sc["a_d"]), I,
+                                   g1_inv=scalar(sc["g1_inv"]), g2_inv=scalar(sc["g2_inv"]), ws=ws))
+        torch.cuda.synchronize()
         r = oracle.mlp_w4a4(x, w["c_gu"], w["s_gu"], sc["a_gu"], w["c_d"], w["s_d"], sc["a_d"],
                             sc["g1_inv"], sc["g2_inv"])
         gemm_close(y, r["out"], f"decode W4A4 seed {seed}")
+        # the single launch's NVFP4 h (left in the workspace) against the
+        # pure oracle's pre-quant h, under the tie rule
+        hc, hs = _ws_h(ws, H, I)
+        n_diff += requant_check(hc.reshape(1, I // 2), hs.reshape(1, I // 16), r["h"], sc["g2_inv"])[0]
+    print(f"decode h: {n_diff} re-quantized elements differ over 22 inputs")
+    assert to_host(nv.mlp_workspace_status(ws))[0] == 0
 
 
 @pytest.mark.parametrize("M", [1, 4, 16, 64, 128])
@@ -443,6 +504,85 @@ def test_mlp_decode_single_launch(H, I):
     assert np.array_equal(h1[0], h3[0]) and np.array_equal(h1[1], h3[1]), "h differs from the two-launch path"
 
 
+def test_mlp_workspace_shared_across_token_counts():
+    """One workspace sized for 16 tokens serves W4A4 at 16 tokens, W4A16 at
+    16, per-token W4A4 at 16 and the single-launch W4A4 decode at 1 token,
+    in turns. The decode's records lie in the workspace's tail, which no
+    other call writes: the tail bytes the decode leaves are still there
+    after the other calls, and every output equals a fresh workspace's."""
+    nv.set_path(nv.PATH_AUTO)
+    H, I = 512, 4352
+    w = mlp_weights(H, I, 0)
+    p_gu, p_d = packed_weights(H, I, 0)
+    nws = max(nv.mlp_workspace_bytes(m, 16, H, I) for m in (0, 1, 2))
+    ws = torch.zeros(nws, dtype=torch.uint8, device=dev())
+    tail = 4 << 20  # the workspace tail: status word and decode records
+    x16 = synth.activations(5, 16, H)
+    x1 = synth.activations(6, 1, H)
+    sc = calibrate_activation_scales(x16, w)
+    a_gu, a_d, g1i, g2i = scalar(sc["a_gu"]), scalar(sc["a_d"]), scalar(sc["g1_inv"]), scalar(sc["g2_inv"])
+    calls = {
+        "w4a4 M=16": lambda ws_: nv.mlp_forward(0, to_dev(x16), p_gu, a_gu, p_d, a_d, I, g1_inv=g1i, g2_inv=g2i,
+                                                ws=ws_),
+        "w4a16 M=16": lambda ws_: nv.mlp_forward(1, to_dev(x16), p_gu, scalar(w["g_gu"]), p_d, scalar(w["g_d"]), I,
+                                                 ws=ws_),
+        "dyn M=16": lambda ws_: nv.mlp_forward(2, to_dev(x16), p_gu, scalar(w["g_gu"]), p_d, a_d, I, g2_inv=g2i,
+                                               ws=ws_),
+        "w4a4 M=1": lambda ws_: nv.mlp_forward(0, to_dev(x1), p_gu, a_gu, p_d, a_d, I, g1_inv=g1i, g2_inv=g2i,
+                                               ws=ws_),
+    }
+    fresh = {k: to_host(f(torch.zeros(nws, dtype=torch.uint8, device=dev()))) for k, f in calls.items()}
+    after_decode = None
+    for rnd in range(3):
+        for k, f in calls.items():
+            y = to_host(f(ws))
+            torch.cuda.synchronize()
+            assert np.array_equal(y, fresh[k]), f"{k} in round {rnd} differs from a fresh workspace"
+            t = to_host(ws)[-tail:].copy()
+            if k == "w4a4 M=1":
+                after_decode = t
+            elif after_decode is not None:
+                assert np.array_equal(t, after_decode), f"{k} wrote the decode's tail"
+    r = oracle.mlp_w4a4(x1, w["c_gu"], w["s_gu"], sc["a_gu"], w["c_d"], w["s_d"], sc["a_d"], sc["g1_inv"],
+                        sc["g2_inv"])
+    gemm_close(fresh["w4a4 M=1"], r["out"], "decode through a shared workspace")
+    assert to_host(nv.mlp_workspace_status(ws))[0] == 0
+
+
+def test_mlp_decode_expired_wait_reports():
+    """The single-launch decode's bounded waits, made to give up from the
+    host: the test hook has its workgroups tag their records with a number
+    the waiting ones never look for and bounds each wait at 64 polls. Every
+    workgroup still exits; the output is NaN and the workspace's status word
+    says so. The next call without the hook is correct and leaves the status
+    alone."""
+    nv.set_path(nv.PATH_AUTO)
+    H, I = 512, 4352
+    w = mlp_weights(H, I, 0)
+    p_gu, p_d = packed_weights(H, I, 0)
+    x = synth.activations(9, 1, H)
+    sc = calibrate_activation_scales(x, w)
+    ws = torch.zeros(nv.mlp_workspace_bytes(0, 1, H, I), dtype=torch.uint8, device=dev())
+    status = nv.mlp_workspace_status(ws)
+    run = lambda: nv.mlp_forward(0, to_dev(x), p_gu, scalar(sc["a_gu"]), p_d, scalar(sc["a_d"]), I,
+                                 g1_inv=scalar(sc["g1_inv"]), g2_inv=scalar(sc["g2_inv"]), ws=ws)
+    nv.set_decode_wait_test(True, 64)
+    try:
+        y = to_host(run())
+    finally:
+        nv.set_decode_wait_test(False)
+    torch.cuda.synchronize()
+    assert to_host(status)[0] == nv.STATUS_DECODE_WAIT_EXPIRED
+    assert np.all(np.isnan(y))
+    status.zero_()
+    y = to_host(run())
+    torch.cuda.synchronize()
+    assert to_host(status)[0] == 0
+    r = oracle.mlp_w4a4(x, w["c_gu"], w["s_gu"], sc["a_gu"], w["c_d"], w["s_d"], sc["a_d"], sc["g1_inv"],
+                        sc["g2_inv"])
+    gemm_close(y, r["out"], "decode after an expired launch")
+
+
 def test_mlp_decode_graph_capture():
     """Under stream capture mlp_forward records the two-launch path (the
     single launch needs a new epoch per run); replays match eager results."""
@@ -480,6 +620,25 @@ def test_mlp_decode_graph_capture():
                             sc["g1_inv"], sc["g2_inv"])
         gemm_close(y_graph, r["out"], "graph replay")
         gemm_close(eager, r["out"], "eager")
+
+
+def test_swiglu_fused_requant_prefill_sampled_rows():
+    """The fused gate_up + SwiGLU + NVFP4 kernel at the prefill shape (8192
+    tokens, hidden 7168, intermediate 18432: the tiled kernel) against the
+    pure oracle's h on 16 seeded rows, under the tie rule."""
+    nv.set_path(nv.PATH_AUTO)
+    M, H, I = 8192, 7168, 18432
+    w = mlp_weights(H, I, 0)
+    p_gu, _ = packed_weights(H, I, 0)
+    x = synth.activations(0, M, H)
+    sc = calibrate_activation_scales(x[:64], w)
+    xq, xs = oracle.quantize(x, sc["g1_inv"])
+    hc, hs = nv.gemm_swiglu_nvfp4_quant(to_dev(xq), to_dev(xs), p_gu, I, H, scalar(sc["a_gu"]),
+                                        scalar(sc["g2_inv"]))
+    rows = np.sort(np.random.default_rng(18432).choice(M, 16, replace=False))
+    h_ref = oracle.swiglu(oracle.gemm_w4a4(xq[rows], xs[rows], w["c_gu"], w["s_gu"], sc["a_gu"]))
+    n, total = requant_check(to_host(hc)[rows], to_host(hs)[rows], h_ref, sc["g2_inv"])
+    print(f"prefill h: {n} of {total} re-quantized elements differ")
 
 
 def test_mlp_prefill_full_size_sampled_rows():

@@ -31,7 +31,7 @@ def _lib():
     nv.set_path(nv.PATH_AUTO)
 
 
-PATHS = {"gemv": 1, "stream": 2, "tiled": 3}
+PATHS = {"gemv": 1, "stream": 2, "tiled": 3, "tiled64": 4}
 
 
 @pytest.fixture(params=list(PATHS))

@@ -15,6 +15,7 @@ import pytest
 import torch
 
 import nvfp4_synth as synth
+from golden_fixtures import global_scale_examples
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 GRID = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
@@ -217,6 +218,19 @@ def test_quantize_single_slot_exhaustive_bf16(orc):
     best = np.where(tie_hi & (best % 2 == 1), best + 1, best)
     exp = best | np.where(np.signbit(f), 8, 0)
     assert np.array_equal(got, exp)
+
+
+def test_global_scale_golden_non_power_of_two(orc):
+    """g and g_inv at amax 3, 6, 11, 25 from the hand-worked fixture: g_inv is
+    the reciprocal of the rounded g, not fl(2688 / amax)."""
+    ex = global_scale_examples()
+    assert len(ex) == 4
+    for amax, g_ref, gi_ref, alt in ex:
+        x = np.array([[0.5, -amax, 1.0]], np.float32)
+        g, gi = orc.global_scale(x)
+        assert g == g_ref, (amax, g, g_ref)
+        assert gi == gi_ref, (amax, gi, gi_ref)
+        assert gi != alt
 
 
 def test_global_scale_and_alpha(orc):
