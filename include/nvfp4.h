@@ -278,6 +278,31 @@ int mlp_forward(int mode, const uint16_t* x, int64_t M, int64_t H, int64_t I,
                 size_t ws_bytes, void* out, int out_dtype, void* stream);
 
 /*
+ * mlp_forward without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). The workspace is the library's own scratch array:
+ * one static device array of NVFP4_NOALLOC_SCRATCH_BYTES per GPU, held from
+ * the library's first use on that GPU until the process ends, its address
+ * taken once per device (hipGetSymbolAddress). Nothing is allocated per call.
+ * Arguments and results as mlp_forward. Limit: the workspace the call's
+ * kernel path needs (activations, split-K partials and the 4 MiB tail, as
+ * mlp_workspace_bytes counts them for that path) must fit the scratch; a
+ * larger call is NVFP4_ERR_INVALID_ARG with nothing launched. At hidden 5120
+ * (intermediate 17408) and 7168 (18432) this covers every token count up to
+ * 256 in the W4A4 modes and up to 768 in W4A16.
+ * Every call on one GPU shares that GPU's scratch and leaves its contents
+ * there: calls that overlap in time on one GPU (on different streams, or
+ * from different threads) race and give wrong results; serialize them. The
+ * scratch's tail is cleared once, by a fill kernel on the stream of the
+ * first call on each device. Its status word is not exposed.
+ */
+#define NVFP4_NOALLOC_SCRATCH_BYTES (64u << 20)
+int mlp_forward_noalloc(int mode, const uint16_t* x, int64_t M, int64_t H, int64_t I,
+                        const void* w_gu_packed, const float* alpha_gu, const void* w_d_packed,
+                        const float* alpha_d, const float* g1_inv, const float* g2_inv, void* out,
+                        int out_dtype, void* stream);
+
+/*
  * Standalone SiLU(gate) * up + NVFP4 quantization of a bf16 gate_up output
  * batched by expert, `silu_and_mul_scaled_nvfp4_experts_quantize(gate_up,
  * masked_m, input_scale_inv)` as the PR #34859 digest calls it (key source

@@ -55,6 +55,7 @@ SIGNATURES = {
     "nvfp4_set_decode_wait_test": (_int, [_int, _int]),
     "mlp_forward": (_int, [_int, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
                            _vp, _int, _vp]),
+    "mlp_forward_noalloc": (_int, [_int, _vp, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _int, _vp]),
 }
 
 _LIB = None
@@ -316,6 +317,25 @@ def mlp_forward(mode, x, w_gu_packed, alpha_gu, w_d_packed, alpha_d, I, g1_inv=N
                                             _ptr(w_d_packed), _ptr(alpha_d), _ptr(g1_inv), _ptr(g2_inv),
                                             _ptr(ws), ws.numel() * ws.element_size(), _ptr(out),
                                             _dtype_code(out.dtype), _stream(stream)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def mlp_forward_noalloc(mode, x, w_gu_packed, alpha_gu, w_d_packed, alpha_d, I, g1_inv=None, g2_inv=None,
+                        out=None, out_dtype=torch.float32, stream=None):
+    """mlp_forward on the library's own per-GPU scratch (no workspace
+    argument; the library allocates nothing). Pass `out` to allocate nothing
+    here either. Calls that overlap on one GPU race."""
+    _dense(x, "x")
+    M, H = x.shape
+    if out is None:
+        out = torch.empty((M, H), dtype=out_dtype, device=x.device)
+    _check("mlp_forward_noalloc",
+           lib().mlp_forward_noalloc(int(mode), _ptr(x), M, H, I, _ptr(w_gu_packed), _ptr(alpha_gu), _ptr(w_d_packed),
+                                     _ptr(alpha_d), _ptr(g1_inv), _ptr(g2_inv), _ptr(out), _dtype_code(out.dtype),
+                                     _stream(stream)))
     return out
 
 

@@ -552,6 +552,16 @@ static size_t mlp_split_bytes(int mode, int64_t M, int64_t H, int64_t I) {
   return most;
 }
 
+// Workspace of an mlp_forward call on one path (the size of mlp_workspace_bytes
+// with the split-K plan of that path's kernels only).
+static size_t mlp_path_bytes(int mode, int64_t M, int64_t H, int64_t I, int path) {
+  const int kmode = (mode == NVFP4_MODE_W4A16 || mode == NVFP4_MODE_W4A16_AWQ) ? NVFP4_MODE_W4A16 : NVFP4_MODE_W4A4;
+  const SplitPlan d = split_plan(mlp_kernel(path, kmode, M, H, I), kmode, M, H, I, false);
+  const SplitPlan g = split_plan(mlp_kernel(path, kmode, M, 2 * I, H), kmode, M, 2 * I, H, true);
+  return mlp_act_bytes(mode, static_cast<size_t>(M), H, I) + std::max(d.part_bytes, g.part_bytes) + d.counter_bytes +
+         g.counter_bytes + tail_bytes(H, I);
+}
+
 size_t mlp_workspace_bytes(int mode, int64_t M, int64_t H, int64_t I) {
   if (M < 0 || H <= 0 || I <= 0 || !dim_ok(M) || !dim_ok(H) || !dim_ok(I)) return 0;
   if (mode != NVFP4_MODE_W4A4 && mode != NVFP4_MODE_W4A16 && mode != NVFP4_MODE_W4A4_DYN &&
@@ -577,12 +587,61 @@ int nvfp4_set_decode_wait_test(int withhold, int spin_limit) {
 
 }  // extern "C"
 
+// ---- the library's own workspace, for mlp_forward_noalloc -----------------
+//
+// One static device array per GPU (each device that loads the library holds
+// its own copy until the process ends). Host code never passes the array's
+// name to a kernel or copy: in host code it stands for no device address.
+// The address comes from hipGetSymbolAddress, once per device with that
+// device current, and is kept per device.
+static __device__ __align__(256) uint8_t scratch[NVFP4_NOALLOC_SCRATCH_BYTES];
+
+__global__ void k_clear_words(uint32_t* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+// The scratch address on the current device; on its first use there, the
+// tail (decode records and status word) is cleared on `s` by a fill kernel
+// (stream-ordered before the caller's work; no memset, so a capturing
+// caller records a kernel node). nullptr (with the message set) on failure.
+static uint8_t* scratch_on_current_device(hipStream_t s) {
+  static std::mutex mu;
+  static uint8_t* ptr[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    fail(NVFP4_ERR_HIP, "hipGetDevice failed or device index out of range");
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      fail(NVFP4_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+      return nullptr;
+    }
+    // The tail of the scratch (the same size for every shape).
+    uint32_t* t = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(p) + NVFP4_NOALLOC_SCRATCH_BYTES - kTailBytes);
+    k_clear_words<<<256, 256, 0, s>>>(t, (int64_t)(kTailBytes / 4));
+    const hipError_t le = hipGetLastError();
+    if (le != hipSuccess) {
+      fail(NVFP4_ERR_HIP, "scratch clear launch: %s", hipGetErrorString(le));
+      return nullptr;
+    }
+    ptr[dev] = static_cast<uint8_t*>(p);
+  }
+  return ptr[dev];
+}
+
 // The MLP forward of every mode; s_gu / s_d are the AWQ pre-quant scales of
-// NVFP4_MODE_W4A16_AWQ (null otherwise).
+// NVFP4_MODE_W4A16_AWQ (null otherwise). With use_scratch, ws and ws_bytes
+// are ignored and the library's scratch array serves as the workspace.
 static int mlp_forward_impl(int mode, const uint16_t* x, int64_t M, int64_t H, int64_t I, const void* w_gu_packed,
                             const float* alpha_gu, const void* w_d_packed, const float* alpha_d,
                             const float* g1_inv, const float* g2_inv, const uint16_t* s_gu, const uint16_t* s_d,
-                            void* ws, size_t ws_bytes, void* out, int out_dtype, void* stream) {
+                            void* ws, size_t ws_bytes, void* out, int out_dtype, void* stream,
+                            bool use_scratch = false) {
   if (mode != NVFP4_MODE_W4A4 && mode != NVFP4_MODE_W4A16 && mode != NVFP4_MODE_W4A4_DYN &&
       mode != NVFP4_MODE_W4A16_AWQ)
     return fail(NVFP4_ERR_INVALID_ARG, "unsupported quant mode %d", mode);
@@ -597,20 +656,36 @@ static int mlp_forward_impl(int mode, const uint16_t* x, int64_t M, int64_t H, i
   if (mode == NVFP4_MODE_W4A16_AWQ && M > 0 && (!s_gu || !s_d || !aligned16(s_gu) || !aligned16(s_d)))
     return fail(NVFP4_ERR_INVALID_ARG, "W4A16_AWQ needs 16-byte aligned pre-quant scales s_gu [H] and s_d [I]");
   if (M == 0) { g_err[0] = '\0'; return NVFP4_OK; }
-  if (!x || !w_gu_packed || !alpha_gu || !w_d_packed || !alpha_d || !out || !ws)
+  if (!x || !w_gu_packed || !alpha_gu || !w_d_packed || !alpha_d || !out || (!ws && !use_scratch))
     return fail(NVFP4_ERR_INVALID_ARG, "null pointer argument");
   if (mode == NVFP4_MODE_W4A4 && (!g1_inv || !g2_inv))
     return fail(NVFP4_ERR_INVALID_ARG, "W4A4 needs g1_inv and g2_inv");
   if (mode == NVFP4_MODE_W4A4_DYN && (g1_inv || !g2_inv))
     return fail(NVFP4_ERR_INVALID_ARG, "W4A4_DYN computes x's scales per token: g1_inv must be NULL, g2_inv set");
-  if (!aligned16(x) || !aligned16(w_gu_packed) || !aligned16(w_d_packed) || !aligned16(out) || !aligned16(ws))
+  if (!aligned16(x) || !aligned16(w_gu_packed) || !aligned16(w_d_packed) || !aligned16(out) ||
+      (!use_scratch && !aligned16(ws)))
     return fail(NVFP4_ERR_INVALID_ARG, "buffers must be 16-byte aligned");
-  const size_t need = mlp_workspace_bytes(mode, M, H, I);
-  if (ws_bytes < need)
-    return fail(NVFP4_ERR_INVALID_ARG, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  if (use_scratch) {
+    const int kmode = (mode == NVFP4_MODE_W4A16 || mode == NVFP4_MODE_W4A16_AWQ) ? NVFP4_MODE_W4A16 : NVFP4_MODE_W4A4;
+    const size_t need = mlp_path_bytes(mode, M, H, I, choose_path(kmode, M));
+    if (need > NVFP4_NOALLOC_SCRATCH_BYTES)
+      return fail(NVFP4_ERR_INVALID_ARG,
+                  "mlp_forward_noalloc: M=%lld H=%lld I=%lld needs %zu bytes of workspace, more than the %zu of the "
+                  "library's scratch (use mlp_forward with a workspace)",
+                  (long long)M, (long long)H, (long long)I, need, (size_t)NVFP4_NOALLOC_SCRATCH_BYTES);
+    ws_bytes = NVFP4_NOALLOC_SCRATCH_BYTES;
+  } else {
+    const size_t need = mlp_workspace_bytes(mode, M, H, I);
+    if (ws_bytes < need)
+      return fail(NVFP4_ERR_INVALID_ARG, "workspace %zu bytes < %zu needed", ws_bytes, need);
+  }
   int st = check_device();
   if (st) return st;
   hipStream_t s = as_stream(stream);
+  if (use_scratch) {
+    ws = scratch_on_current_device(s);
+    if (!ws) return NVFP4_ERR_HIP;
+  }
   const int ws_mode = mode;
   const bool dyn = mode == NVFP4_MODE_W4A4_DYN;
   if (dyn) mode = NVFP4_MODE_W4A4;  // the W4A4 kernels, x quantized per token
@@ -736,6 +811,15 @@ int mlp_forward(int mode, const uint16_t* x, int64_t M, int64_t H, int64_t I, co
     return fail(NVFP4_ERR_INVALID_ARG, "W4A16_AWQ takes its pre-quant scales: call mlp_forward_w4a16_awq");
   return mlp_forward_impl(mode, x, M, H, I, w_gu_packed, alpha_gu, w_d_packed, alpha_d, g1_inv, g2_inv, nullptr,
                           nullptr, ws, ws_bytes, out, out_dtype, stream);
+}
+
+int mlp_forward_noalloc(int mode, const uint16_t* x, int64_t M, int64_t H, int64_t I, const void* w_gu_packed,
+                        const float* alpha_gu, const void* w_d_packed, const float* alpha_d, const float* g1_inv,
+                        const float* g2_inv, void* out, int out_dtype, void* stream) {
+  if (mode == NVFP4_MODE_W4A16_AWQ)
+    return fail(NVFP4_ERR_INVALID_ARG, "W4A16_AWQ takes its pre-quant scales: call mlp_forward_w4a16_awq");
+  return mlp_forward_impl(mode, x, M, H, I, w_gu_packed, alpha_gu, w_d_packed, alpha_d, g1_inv, g2_inv, nullptr,
+                          nullptr, nullptr, 0, out, out_dtype, stream, true);
 }
 
 int mlp_forward_w4a16_awq(const uint16_t* x, int64_t M, int64_t H, int64_t I, const void* w_gu_packed,

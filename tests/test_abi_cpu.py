@@ -79,6 +79,23 @@ def test_workspace_status_address():
     assert lib.mlp_workspace_status(None, 4096) is None
 
 
+def test_noalloc_rejects_on_the_host():
+    """The allocation-free forward checks its arguments and its size limit
+    before any HIP call."""
+    lib = nv.lib()
+    P = ctypes.c_void_p(0x100000)
+    N = None
+    INV = nv.NVFP4_ERR_INVALID_ARG
+    # prefill at hidden 7168 needs far more than the 64 MiB scratch
+    assert lib.mlp_forward_noalloc(0, P, 8192, 7168, 18432, P, P, P, P, P, P, P, 1, N) == INV
+    assert b"scratch" in lib.nvfp4_last_error()
+    assert lib.mlp_forward_noalloc(1, P, 4096, 5120, 17408, P, P, P, P, N, N, P, 1, N) == INV
+    assert lib.mlp_forward_noalloc(0, N, 1, 256, 512, P, P, P, P, P, P, P, 1, N) == INV   # null x
+    assert lib.mlp_forward_noalloc(3, P, 1, 256, 512, P, P, P, P, N, N, P, 1, N) == INV   # AWQ
+    assert lib.mlp_forward_noalloc(0, P, 1, 250, 512, P, P, P, P, P, P, P, 1, N) == INV   # H % 256
+    assert lib.mlp_forward_noalloc(0, P, 0, 256, 512, N, N, N, N, N, N, N, 1, N) == nv.NVFP4_OK  # empty
+
+
 def test_decode_wait_test_hook_arguments():
     lib = nv.lib()
     assert lib.nvfp4_set_decode_wait_test(1, 0) == nv.NVFP4_ERR_INVALID_ARG
