@@ -256,10 +256,10 @@ uint32_t* mlp_workspace_status(void* ws, size_t ws_bytes);
  *          g1_inv must be NULL (h keeps its static g2_inv, as on the pages).
  * x bf16 [M, H]; w_gu_packed: SWIGLU packed [2I, H]; w_d_packed: PLAIN packed
  * [H, I]; H % 256 == 0, I % 256 == 0. out [M, H] of out_dtype.
- * W4A4 at M = 1 under NVFP4_PATH_AUTO (and outside stream capture) runs as
- * one launch: its workgroups pass h and the down projection's partial sums
- * to each other through 64-bit records in the workspace's tail, each tagged
- * with a 32-bit number new to the call. The tail must therefore hold zeros
+ * W4A4 and W4A16 at M = 1 under NVFP4_PATH_AUTO (and outside stream capture)
+ * run as one launch: its workgroups pass h and the down projection's partial
+ * sums to each other through 64-bit records in the workspace's tail, each
+ * tagged with a 32-bit number new to the call. The tail must therefore hold zeros
  * the first time it is used this way (memory with other contents could hold
  * a current tag by chance). No other call writes the tail, so a workspace
  * stays ready for the next decode whatever calls (of any mode, M, H and I)
@@ -371,8 +371,8 @@ int mlp_forward_w4a16_awq(const uint16_t* x, int64_t M, int64_t H, int64_t I, co
                           const float* g_gu, const uint16_t* s_gu, const void* w_d_packed, const float* g_d,
                           const uint16_t* s_d, void* ws, size_t ws_bytes, void* out, int out_dtype, void* stream);
 
-/* Test hook for the bounded waits of the single-launch decode (mlp_forward,
- * W4A4, M = 1), for calls from the calling thread: with withhold != 0 its
+/* Test hook for the bounded waits of the single-launch decodes (mlp_forward,
+ * W4A4 or W4A16, M = 1), for calls from the calling thread: with withhold != 0 its
  * workgroups tag their records with a number the waiting workgroups never
  * look for, and each wait gives up after spin_limit polls, so every wait
  * expires, sets NVFP4_STATUS_DECODE_WAIT_EXPIRED and writes NaN, and every

@@ -13,7 +13,7 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libnvfp4_mi355x.so")
 SOURCES = ["api.cpp", "quantize.hip", "repack.hip", "stream.hip", "stream_nt1.hip", "gemv.hip", "fp4gemv.hip",
-           "decode.hip", "tiled.hip", "tiled2.hip", "tiled16.hip", "silu_quant.hip", "prescale.hip"]
+           "decode.hip", "decode16.hip", "tiled.hip", "tiled2.hip", "tiled16.hip", "silu_quant.hip", "prescale.hip"]
 # LLVM instruction-scheduling strategy per translation unit, where another
 # than the default measured faster on MI355X: the W4A16 tiled kernel with
 # max-ilp (forward at 256 / 4096 tokens, hidden 5120: 208 -> 198 us, 1948 ->

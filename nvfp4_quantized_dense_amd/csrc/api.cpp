@@ -514,28 +514,39 @@ static size_t decode_bytes(int64_t H, int64_t I) {
   return align256((size_t)nvfp4::decode_record_words(H, I) * sizeof(uint64_t));
 }
 
+// Records of the single-launch W4A16 decode kernel (0 where it cannot run).
+static size_t decode16_bytes(int64_t H, int64_t I) {
+  if (!nvfp4::decode16_supported(H, I)) return 0;
+  return align256((size_t)nvfp4::decode16_record_words(H, I) * sizeof(uint64_t));
+}
+
 // The tail of every mlp_forward workspace, counted from the END of the
 // buffer as the caller passes it (ws + ws_bytes): the status word in its
 // last 4 bytes and, 256 bytes before it, the single-launch decode kernel's
 // records. Its size is the same for every mode, token count and shape, so no
 // other call on a buffer shared with the same ws_bytes writes there, and the
 // records stay as the decode launches leave them. 4 MiB holds the records of
-// every shape the decode kernel takes (its LDS bounds H and I by 61440 and
-// its 31-bit offsets H * I by 1.9e9: at most 3.98 MB) plus the status word
-// and the records' alignment; decode_in_tail checks it per shape.
+// every shape the decode kernels take (the W4A4 one's LDS bounds H and I by
+// 61440 and its 31-bit offsets H * I by 1.9e9: at most 3.98 MB; the W4A16
+// one's LDS bounds H by 32760 and its splits I by 32768: at most 2.3 MB)
+// plus the status word and the records' alignment; decode_in_tail checks
+// it per shape.
 constexpr size_t kTailBytes = size_t(4) << 20;
 static size_t tail_bytes(int64_t, int64_t) { return kTailBytes; }
 static bool decode_in_tail(int64_t H, int64_t I) {
   return nvfp4::decode_supported(H, I) && decode_bytes(H, I) + 512 <= kTailBytes;
+}
+static bool decode16_in_tail(int64_t H, int64_t I) {
+  return nvfp4::decode16_supported(H, I) && decode16_bytes(H, I) + 512 <= kTailBytes;
 }
 
 static uint32_t* tail_status(void* ws, size_t ws_bytes) {
   return reinterpret_cast<uint32_t*>((reinterpret_cast<uintptr_t>(ws) + ws_bytes - 4) & ~uintptr_t(3));
 }
 
-static uint64_t* tail_records(void* ws, size_t ws_bytes, int64_t H, int64_t I) {
+static uint64_t* tail_records(void* ws, size_t ws_bytes, size_t record_bytes) {
   const uintptr_t end = reinterpret_cast<uintptr_t>(ws) + ws_bytes;
-  return reinterpret_cast<uint64_t*>((end - 256 - decode_bytes(H, I)) & ~uintptr_t(255));
+  return reinterpret_cast<uint64_t*>((end - 256 - record_bytes) & ~uintptr_t(255));
 }
 
 // Split-K partials and counters of the largest plan over the kernels of
@@ -749,7 +760,7 @@ static int mlp_forward_impl(int mode, const uint16_t* x, int64_t M, int64_t H, i
     // the down workgroups as epoch-tagged records in the workspace).
     if (M == 1 && g_path == NVFP4_PATH_AUTO && decode_in_tail(H, I) && !stream_capturing(s)) {
       nvfp4::DecodeArgs d{x, g1_inv, static_cast<const uint8_t*>(w_gu_packed), static_cast<const uint8_t*>(w_d_packed),
-                          alpha_gu, alpha_d, g2_inv, hq, hs, out, tail_records(ws, ws_bytes, H, I),
+                          alpha_gu, alpha_d, g2_inv, hq, hs, out, tail_records(ws, ws_bytes, decode_bytes(H, I)),
                           H, I, nvfp4::decode_splits(H, I), next_epoch(), tail_status(ws, ws_bytes),
                           nvfp4::kDecodeSpinLimit, 0u};
       if (g_decode_test_spins > 0) {
@@ -783,6 +794,20 @@ static int mlp_forward_impl(int mode, const uint16_t* x, int64_t M, int64_t H, i
     return hip_status(e, "mlp_forward down");
   }
   uint8_t* hb = base;
+  // One token under the automatic path (plain W4A16, outside stream
+  // capture): the whole forward in one launch, the bf16 h handed from the
+  // gate_up workgroups to the down workgroups as tagged records.
+  if (M == 1 && !s_gu && g_path == NVFP4_PATH_AUTO && decode16_in_tail(H, I) && !stream_capturing(s)) {
+    nvfp4::Decode16Args d{x, static_cast<const uint8_t*>(w_gu_packed), static_cast<const uint8_t*>(w_d_packed),
+                          alpha_gu, alpha_d, reinterpret_cast<uint16_t*>(hb), out,
+                          tail_records(ws, ws_bytes, decode16_bytes(H, I)), H, I, nvfp4::decode16_splits(H, I),
+                          next_epoch(), tail_status(ws, ws_bytes), nvfp4::kDecodeSpinLimit, 0u};
+    if (g_decode_test_spins > 0) {
+      d.spin_limit = g_decode_test_spins;
+      d.tag_skew = 0x80000000u;
+    }
+    return hip_status(nvfp4::launch_decode_mlp16(epi_out, d, s), "mlp_forward decode (W4A16)");
+  }
   const void* xin = x;
   if (s_gu) {
     // AWQ: x' = bf16(x * s_gu) into the workspace; h gets s_d in the gate_up

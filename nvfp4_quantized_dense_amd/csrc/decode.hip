@@ -20,14 +20,10 @@
 //     store their 16 partial sums as tagged records; the unit of split S - 1
 //     polls those, adds the S partials in split order and writes the output.
 //
-// A tagged record is one 64-bit word written by one atomic store: 32 bits of
-// data and the low 32 bits of the launch's epoch (never 0: a zero-filled
-// workspace holds no valid record). Reading the word with a device-scope
-// atomic load gives the data and the proof that it belongs to this launch
-// in one access, so a producer never waits for its stores to complete and a
-// consumer needs no separate flag. The host gives every launch a new epoch,
-// so a record left by an earlier launch (whose tag differs, until 2^32
-// launches later) is never mistaken for a current one.
+// The records are the tagged 64-bit words of decode_records.h: 32 bits of
+// data and the low 32 bits of the launch's epoch, which the host makes new
+// for every launch, so a record left by an earlier launch (whose tag differs,
+// until 2^32 launches later) is never mistaken for a current one.
 //
 // Every wait is on workgroups of smaller index, or on gate_up units that
 // never wait: each XCD starts its workgroups in index order, so the awaited
@@ -37,6 +33,7 @@
 // hanging, and sets kDecodeWaitExpired in the status word for the host.
 #include <algorithm>
 
+#include "decode_records.h"
 #include "fp4_tile.h"
 
 namespace nvfp4 {
@@ -51,15 +48,6 @@ constexpr int kSplitTiles = kDownSets * kDecodeWaves;
 // Down units cover at most this many K tiles (48 record words per tile).
 constexpr int kMaxSplitTiles = kPollWords * kDecodeWaves * 64 / 48;
 
-__device__ __forceinline__ void put_record(uint64_t* p, uint32_t data, uint32_t tag) {
-  __hip_atomic_store(p, ((uint64_t)tag << 32) | data, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint64_t get_record(const uint64_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void report_expired(uint32_t* status) {
-  __hip_atomic_fetch_or(status, kDecodeWaitExpired, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 }  // namespace
 
 template <int EPI>

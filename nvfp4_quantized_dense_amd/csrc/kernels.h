@@ -183,4 +183,28 @@ int decode_splits(int64_t H, int64_t I);
 int64_t decode_record_words(int64_t H, int64_t I);
 hipError_t launch_decode_mlp(int epi, const DecodeArgs& d, hipStream_t s);
 
+// decode16.hip: the W4A16 MLP forward of one token in one launch (gate_up
+// units hand the bf16 h to the down units, and those their partial sums to
+// the last K split, as tagged records, as in decode.hip).
+struct Decode16Args {
+  const void* x;          // bf16 [1, H]
+  const uint8_t* w_gu;    // SWIGLU packed [2I, H]
+  const uint8_t* w_d;     // PLAIN packed [H, I]
+  const float* alpha_gu;  // g of the gate_up weight
+  const float* alpha_d;   // g of the down weight
+  uint16_t* h;            // bf16 [I], written (as by the two-launch path)
+  void* out;              // [1, H], f32 or bf16
+  uint64_t* records;      // decode16_record_words(H, I) words: zeros or left by earlier launches
+  int64_t H, I;
+  int ksplit;             // decode16_splits(H, I)
+  uint64_t epoch;         // as DecodeArgs::epoch
+  uint32_t* status;       // OR-ed with kDecodeWaitExpired by a unit whose bounded wait gave up
+  int spin_limit;         // polls of one wait before it gives up
+  uint32_t tag_skew;      // as DecodeArgs::tag_skew
+};
+bool decode16_supported(int64_t H, int64_t I);
+int decode16_splits(int64_t H, int64_t I);
+int64_t decode16_record_words(int64_t H, int64_t I);
+hipError_t launch_decode_mlp16(int epi, const Decode16Args& d, hipStream_t s);
+
 }  // namespace nvfp4

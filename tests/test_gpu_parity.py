@@ -462,46 +462,64 @@ def test_mlp_split_k(mode, kpath, M, I):
 # workspace) must equal the two-launch GEMV path's byte for byte: the same
 # arithmetic produces it.
 
-def _ws_h(ws, H, I):
-    """h codes and scale bytes inside an M = 1 W4A4 mlp_forward workspace."""
+def _ws_h(ws, H, I, mode=0):
+    """h inside an M = 1 mlp_forward workspace: W4A4 (codes, scale bytes)
+    after x's NVFP4; W4A16 bf16 h [I] at the start."""
+    b = to_host(ws)
+    if mode == 1:
+        return (b[:2 * I].copy(),)
     a256 = lambda v: (v + 255) // 256 * 256
     o = a256(H // 2) + a256(H // 16)
-    b = to_host(ws)
     return b[o:o + I // 2].copy(), b[o + a256(I // 2):o + a256(I // 2) + I // 16].copy()
+
+
+def _decode_call(mode, x, w, sc, p_gu, p_d, I):
+    if mode == 0:
+        return (0, to_dev(x), p_gu, scalar(sc["a_gu"]), p_d, scalar(sc["a_d"]), I), \
+            dict(g1_inv=scalar(sc["g1_inv"]), g2_inv=scalar(sc["g2_inv"]))
+    return (1, to_dev(x), p_gu, scalar(w["g_gu"]), p_d, scalar(w["g_d"]), I), {}
+
+
+def _decode_ref(mode, x, w, sc):
+    if mode == 0:
+        return oracle.mlp_w4a4(x, w["c_gu"], w["s_gu"], sc["a_gu"], w["c_d"], w["s_d"], sc["a_d"],
+                               sc["g1_inv"], sc["g2_inv"])
+    return oracle.mlp_w4a16(x, w["c_gu"], w["s_gu"], w["g_gu"], w["c_d"], w["s_d"], w["g_d"])
 
 
 @pytest.mark.parametrize("H,I", [(256, 256), (256, 4096), (512, 4352), (1024, 2304), (2048, 6912),
                                  (256, 18432)])
-def test_mlp_decode_single_launch(H, I):
+@pytest.mark.parametrize("mode", [0, 1])
+def test_mlp_decode_single_launch(mode, H, I):
     nv.set_path(nv.PATH_AUTO)
     w = mlp_weights(H, I, 0)
     p_gu, p_d = packed_weights(H, I, 0)
     x = synth.activations(H + I, 1, H)
-    sc = calibrate_activation_scales(x, w)
-    args = (0, to_dev(x), p_gu, scalar(sc["a_gu"]), p_d, scalar(sc["a_d"]), I)
-    gkw = dict(g1_inv=scalar(sc["g1_inv"]), g2_inv=scalar(sc["g2_inv"]))
-    nws = nv.mlp_workspace_bytes(0, 1, H, I)
+    sc = calibrate_activation_scales(x, w) if mode == 0 else None
+    args, gkw = _decode_call(mode, x, w, sc, p_gu, p_d, I)
+    nws = nv.mlp_workspace_bytes(mode, 1, H, I)
     ws = torch.zeros((nws,), dtype=torch.uint8, device=dev())
     y1 = to_host(nv.mlp_forward(*args, ws=ws, **gkw))
-    h1 = _ws_h(ws, H, I)
-    nv.mlp_forward(0, to_dev(synth.activations(H + I + 1, 1, H)), *args[2:], ws=ws, **gkw)
+    h1 = _ws_h(ws, H, I, mode)
+    nv.mlp_forward(mode, to_dev(synth.activations(H + I + 1, 1, H)), *args[2:], ws=ws, **gkw)
     y2 = to_host(nv.mlp_forward(*args, ws=ws, **gkw))
     yb = to_host(nv.mlp_forward(*args, ws=ws, out_dtype=torch.bfloat16, **gkw))
     prev = nv.set_path(PATHS["gemv"])
     try:
         ws2 = torch.full((nws,), 0xFF, dtype=torch.uint8, device=dev())
         y3 = to_host(nv.mlp_forward(*args, ws=ws2, **gkw))
-        h3 = _ws_h(ws2, H, I)
+        h3 = _ws_h(ws2, H, I, mode)
     finally:
         nv.set_path(prev)
     torch.cuda.synchronize()
-    r = oracle.mlp_w4a4(x, w["c_gu"], w["s_gu"], sc["a_gu"], w["c_d"], w["s_d"], sc["a_d"],
-                        sc["g1_inv"], sc["g2_inv"])
-    gemm_close(y1, r["out"], f"decode H={H} I={I}")
-    gemm_close(y3, r["out"], f"two-launch decode H={H} I={I}")
+    r = _decode_ref(mode, x, w, sc)
+    gemm_close(y1, r["out"], f"decode mode {mode} H={H} I={I}")
+    gemm_close(y3, r["out"], f"two-launch decode mode {mode} H={H} I={I}")
     assert np.array_equal(y1, y2), "the same input through a reused workspace differs"
     assert np.array_equal(yb, synth.f32_to_bf16_bits(y1)), "bf16 output is not the f32 output rounded"
-    assert np.array_equal(h1[0], h3[0]) and np.array_equal(h1[1], h3[1]), "h differs from the two-launch path"
+    for a, b in zip(h1, h3):
+        assert np.array_equal(a, b), "h differs from the two-launch path"
+    assert to_host(nv.mlp_workspace_status(ws))[0] == 0
 
 
 def test_mlp_workspace_shared_across_token_counts():
@@ -530,6 +548,8 @@ def test_mlp_workspace_shared_across_token_counts():
                                                ws=ws_),
         "w4a4 M=1": lambda ws_: nv.mlp_forward(0, to_dev(x1), p_gu, a_gu, p_d, a_d, I, g1_inv=g1i, g2_inv=g2i,
                                                ws=ws_),
+        "w4a16 M=1": lambda ws_: nv.mlp_forward(1, to_dev(x1), p_gu, scalar(w["g_gu"]), p_d, scalar(w["g_d"]), I,
+                                                ws=ws_),
     }
     fresh = {k: to_host(f(torch.zeros(nws, dtype=torch.uint8, device=dev()))) for k, f in calls.items()}
     after_decode = None
@@ -539,7 +559,7 @@ def test_mlp_workspace_shared_across_token_counts():
             torch.cuda.synchronize()
             assert np.array_equal(y, fresh[k]), f"{k} in round {rnd} differs from a fresh workspace"
             t = to_host(ws)[-tail:].copy()
-            if k == "w4a4 M=1":
+            if k.endswith("M=1"):
                 after_decode = t
             elif after_decode is not None:
                 assert np.array_equal(t, after_decode), f"{k} wrote the decode's tail"
@@ -549,7 +569,8 @@ def test_mlp_workspace_shared_across_token_counts():
     assert to_host(nv.mlp_workspace_status(ws))[0] == 0
 
 
-def test_mlp_decode_expired_wait_reports():
+@pytest.mark.parametrize("mode", [0, 1])
+def test_mlp_decode_expired_wait_reports(mode):
     """The single-launch decode's bounded waits, made to give up from the
     host: the test hook has its workgroups tag their records with a number
     the waiting ones never look for and bounds each wait at 64 polls. Every
@@ -561,11 +582,11 @@ def test_mlp_decode_expired_wait_reports():
     w = mlp_weights(H, I, 0)
     p_gu, p_d = packed_weights(H, I, 0)
     x = synth.activations(9, 1, H)
-    sc = calibrate_activation_scales(x, w)
-    ws = torch.zeros(nv.mlp_workspace_bytes(0, 1, H, I), dtype=torch.uint8, device=dev())
+    sc = calibrate_activation_scales(x, w) if mode == 0 else None
+    ws = torch.zeros(nv.mlp_workspace_bytes(mode, 1, H, I), dtype=torch.uint8, device=dev())
     status = nv.mlp_workspace_status(ws)
-    run = lambda: nv.mlp_forward(0, to_dev(x), p_gu, scalar(sc["a_gu"]), p_d, scalar(sc["a_d"]), I,
-                                 g1_inv=scalar(sc["g1_inv"]), g2_inv=scalar(sc["g2_inv"]), ws=ws)
+    args, gkw = _decode_call(mode, x, w, sc, p_gu, p_d, I)
+    run = lambda: nv.mlp_forward(*args, ws=ws, **gkw)
     nv.set_decode_wait_test(True, 64)
     try:
         y = to_host(run())
@@ -578,12 +599,11 @@ def test_mlp_decode_expired_wait_reports():
     y = to_host(run())
     torch.cuda.synchronize()
     assert to_host(status)[0] == 0
-    r = oracle.mlp_w4a4(x, w["c_gu"], w["s_gu"], sc["a_gu"], w["c_d"], w["s_d"], sc["a_d"], sc["g1_inv"],
-                        sc["g2_inv"])
-    gemm_close(y, r["out"], "decode after an expired launch")
+    gemm_close(y, _decode_ref(mode, x, w, sc)["out"], f"decode mode {mode} after an expired launch")
 
 
-def test_mlp_decode_graph_capture():
+@pytest.mark.parametrize("mode", [0, 1])
+def test_mlp_decode_graph_capture(mode):
     """Under stream capture mlp_forward records the two-launch path (the
     single launch needs a new epoch per run); replays match eager results."""
     nv.set_path(nv.PATH_AUTO)
@@ -591,14 +611,13 @@ def test_mlp_decode_graph_capture():
     w = mlp_weights(H, I, 0)
     p_gu, p_d = packed_weights(H, I, 0)
     xs = [synth.activations(7 + k, 1, H) for k in range(3)]
-    sc = calibrate_activation_scales(xs[0], w)
-    xd = to_dev(xs[0])
-    nws = nv.mlp_workspace_bytes(0, 1, H, I)
+    sc = calibrate_activation_scales(xs[0], w) if mode == 0 else None
+    args, gkw = _decode_call(mode, xs[0], w, sc, p_gu, p_d, I)
+    xd = args[1]
+    nws = nv.mlp_workspace_bytes(mode, 1, H, I)
     ws = torch.zeros((nws,), dtype=torch.uint8, device=dev())
     out = torch.empty((1, H), dtype=torch.float32, device=dev())
-    a_gu, a_d = scalar(sc["a_gu"]), scalar(sc["a_d"])
-    g1i, g2i = scalar(sc["g1_inv"]), scalar(sc["g2_inv"])
-    call = lambda: nv.mlp_forward(0, xd, p_gu, a_gu, p_d, a_d, I, g1_inv=g1i, g2_inv=g2i, ws=ws, out=out)
+    call = lambda: nv.mlp_forward(*args, ws=ws, out=out, **gkw)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -613,13 +632,11 @@ def test_mlp_decode_graph_capture():
         g.replay()
         torch.cuda.synchronize()
         y_graph = to_host(out)
-        eager = to_host(nv.mlp_forward(0, xd, p_gu, a_gu, p_d, a_d, I, g1_inv=g1i, g2_inv=g2i,
-                                       ws=torch.zeros_like(ws)))
+        eager = to_host(nv.mlp_forward(*args, ws=torch.zeros_like(ws), **gkw))
         torch.cuda.synchronize()
-        r = oracle.mlp_w4a4(x, w["c_gu"], w["s_gu"], sc["a_gu"], w["c_d"], w["s_d"], sc["a_d"],
-                            sc["g1_inv"], sc["g2_inv"])
-        gemm_close(y_graph, r["out"], "graph replay")
-        gemm_close(eager, r["out"], "eager")
+        r = _decode_ref(mode, x, w, sc)
+        gemm_close(y_graph, r["out"], f"graph replay mode {mode}")
+        gemm_close(eager, r["out"], f"eager mode {mode}")
 
 
 def test_swiglu_fused_requant_prefill_sampled_rows():
