@@ -10,8 +10,8 @@ Prints one JSON line. `value` is algorithmic bytes (decode workloads, GB/s)
 or algorithmic flops (prefill, TFLOP/s) per second of wall clock over the
 timed steps (no events inside them: an event record between kernels costs a
 few microseconds of idle GPU); `roofline` reports the dominant kernel (the
-single-launch decode kernel, i.e. the whole forward, at W4A4 with one token;
-otherwise the fused gate_up kernel; for the grouped and SiLU-quantize
+single-launch decode kernel, i.e. the whole forward, at one token in W4A4
+and W4A16; otherwise the fused gate_up kernel; for the grouped and SiLU-quantize
 workloads the one call they time), measured with one HIP event pair around a
 back-to-back run of it on the stream it runs on; `cpu_baseline` is the CPU
 oracle timed on a bounded sample of the same workload; `step_us` is the
@@ -401,11 +401,11 @@ def run_one(args, workload, dev, M, H, I, mode, outliers, n_seeds, steps, warmup
     log(f"[bench] timed {steps} steps in {dt:.3f}s")
 
     # Dominant kernel, back to back on the same stream (rotating weight
-    # copies), bracketed by one HIP event pair: at W4A4 M = 1 under the
-    # automatic path the whole forward is one launch (the single-launch
-    # decode kernel), so that launch, with the whole forward's bytes;
+    # copies), bracketed by one HIP event pair: at M = 1 under the automatic
+    # path the whole forward is one launch (the single-launch decode kernel
+    # of W4A4 or W4A16), so that launch, with the whole forward's bytes;
     # otherwise the fused gate_up launch alone.
-    single = mode == "w4a4" and not dyn and M == 1 and args.path == 0
+    single = not dyn and not awq and M == 1 and args.path == 0
     leg = step if single else fused
     leg_bytes = alg["total"] if single else alg["fused"]
     leg_flops = alg["flops"] if single else alg["flops_fused"]
@@ -431,9 +431,10 @@ def run_one(args, workload, dev, M, H, I, mode, outliers, n_seeds, steps, warmup
         achieved = leg_bytes / (fused_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBS, "traffic": None}
-    roof["traffic"] = None if dyn else recorded_traffic(workload, M)
+    roof["traffic"] = recorded_traffic(workload + ("_per_token" if dyn else "") + ("_awq" if awq else ""), M)
     if single:
-        roof["kernel"] = "mlp_forward single-launch decode (k_decode_mlp)"
+        roof["kernel"] = ("mlp_forward single-launch decode (k_decode_mlp)" if mode == "w4a4" else
+                          "mlp_forward single-launch decode (k_decode_mlp16)")
     else:
         roof["kernel"] = ("gemm_swiglu_nvfp4_quant_rowscale" if dyn else
                           "gemm_swiglu_nvfp4_quant" if mode == "w4a4" else "gemm_swiglu(w4a16, bf16 h)")
