@@ -21,7 +21,7 @@ NVFP4_ERR_HIP = -3
 DTYPE_BF16, DTYPE_F32 = 0, 1
 MODE_W4A4, MODE_W4A16, MODE_W4A4_DYN, MODE_W4A16_AWQ = 0, 1, 2, 3
 REPACK_PLAIN, REPACK_SWIGLU = 0, 1
-PATH_AUTO, PATH_GEMV, PATH_STREAM, PATH_TILED, PATH_TILED64 = 0, 1, 2, 3, 4
+PATH_AUTO, PATH_GEMV, PATH_STREAM, PATH_TILED, PATH_TILED64, PATH_MID = 0, 1, 2, 3, 4, 5
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64

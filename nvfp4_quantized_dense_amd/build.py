@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libnvfp4_mi355x.so")
-SOURCES = ["api.cpp", "quantize.hip", "repack.hip", "stream.hip", "stream_nt1.hip", "gemv.hip", "fp4gemv.hip",
+SOURCES = ["api.cpp", "quantize.hip", "repack.hip", "stream.hip", "stream_nt1.hip", "mid.hip", "gemv.hip", "fp4gemv.hip",
            "decode.hip", "decode16.hip", "tiled.hip", "tiled2.hip", "tiled16.hip", "silu_quant.hip", "prescale.hip"]
 # LLVM instruction-scheduling strategy per translation unit, where another
 # than the default measured faster on MI355X: the W4A16 tiled kernel with

@@ -115,13 +115,29 @@ int64_t stream_max_m(int mode) { return mode == NVFP4_MODE_W4A4 ? 128 : 48; }
 // over all experts under the automatic path.
 constexpr int64_t kGroupedStreamMaxM = 256;
 
+// Token counts at which a W4A4 GEMM with a SwiGLU epilogue (the gate_up of
+// the MLP) runs the mid-size kernel under the automatic path. Gate_up alone
+// (hidden 7168 / 5120): 64 tokens 78.9 / 61.0 us streaming against 68.8 /
+// 50.4; 128: 138.0 / 103.6 against 113.4 / 82.6; 192: 182.2 / 134.4 tiled
+// against 150.8 / 110.8; 256: 183.1 / 135.0 tiled against 192.5 / 138.6;
+// below 64 tokens streaming wins (48: 62.8 / 47.9 against 66.6 / 49.0).
+// Whole forward (hidden 7168): 256 tokens 287.9 -> 270.6 us, 144 tokens
+// 277.9 -> 224.1 us, 64 tokens 123.3 -> 108.3 us; at 512 tokens the tiled
+// gate_up with its K-split tail (mlp_forward) beats it: 439.7 against 468.0.
+// Dense GEMMs (the down projection, 5120 / 7168 rows: 40 / 56 mid-size
+// workgroups per 64 tokens) keep the streaming and tiled kernels, whose
+// split-K fills the CUs.
+constexpr int64_t kMidMinM = 64, kMidMaxM = 256;
+
 // Kernel class for a GEMM of M tokens: the decode GEMV up to M = 2 (W4A4,
 // whose FP4 GEMV carries two tokens per workgroup) or M = 1 (W4A16), the
+// mid-size kernel for W4A4 SwiGLU GEMMs of kMidMinM..kMidMaxM tokens, the
 // weight-streaming MFMA kernel up to stream_max_m, the LDS-tiled kernel above.
-int choose_path(int mode, int64_t M) {
+int choose_path(int mode, int64_t M, bool swiglu) {
   int p = g_path;
   if (p != NVFP4_PATH_AUTO) return p;
   if (M <= (mode == NVFP4_MODE_W4A4 ? 2 : 1)) return NVFP4_PATH_GEMV;
+  if (mode == NVFP4_MODE_W4A4 && swiglu && M >= kMidMinM && M <= kMidMaxM) return NVFP4_PATH_MID;
   if (M <= stream_max_m(mode)) return NVFP4_PATH_STREAM;
   return NVFP4_PATH_TILED;
 }
@@ -136,7 +152,7 @@ bool fits_buffers(const nvfp4::GemmArgs& a, int mode) {
 }
 
 // The kernel a GEMM runs on, from the path and what the operands allow.
-enum Kernel { kFp4Gemv, kValuGemv, kStream, kTiled2, kTiled16, kTiled };
+enum Kernel { kFp4Gemv, kValuGemv, kStream, kTiled2, kTiled16, kTiled, kMid };
 
 Kernel select_kernel(int path, int mode, const nvfp4::GemmArgs& a) {
   if (path != NVFP4_PATH_TILED64 && fits_buffers(a, mode)) {
@@ -146,6 +162,7 @@ Kernel select_kernel(int path, int mode, const nvfp4::GemmArgs& a) {
       return kStream;
     }
     if (path == NVFP4_PATH_STREAM) return kStream;
+    if (path == NVFP4_PATH_MID) return mode == NVFP4_MODE_W4A4 && nvfp4::mid_supported(a) ? kMid : kStream;
     return mode == NVFP4_MODE_W4A4 ? kTiled2 : kTiled16;
   }
   // Beyond 2^31-byte operands only the 64-bit-addressed tiled kernel runs
@@ -160,6 +177,7 @@ hipError_t run_gemm(int path, int mode, int epi, const nvfp4::GemmArgs& a, hipSt
     case kStream: return nvfp4::launch_stream_gemm(mode, epi, a, s);
     case kTiled2: return nvfp4::launch_tiled2_gemm(epi, a, s);
     case kTiled16: return nvfp4::launch_tiled16_gemm(epi, a, s);
+    case kMid: return nvfp4::launch_mid_gemm(epi, a, s);
     default: return nvfp4::launch_tiled_gemm(mode, epi, a, s);
   }
 }
@@ -270,7 +288,7 @@ Kernel mlp_kernel(int path, int mode, int64_t M, int64_t N, int64_t K) {
 
 // The kernels that clear the split-K counters of the GEMM after them.
 bool clears_counters(Kernel k) {
-  return k == kFp4Gemv || k == kValuGemv || k == kStream || k == kTiled2 || k == kTiled16;
+  return k == kFp4Gemv || k == kValuGemv || k == kStream || k == kTiled2 || k == kTiled16 || k == kMid;
 }
 
 // Shared checks of the GEMM entry points. N is the packed row count.
@@ -302,7 +320,7 @@ extern "C" {
 const char* nvfp4_last_error(void) { return g_err; }
 
 int nvfp4_set_path(int path) {
-  if (path < NVFP4_PATH_AUTO || path > NVFP4_PATH_TILED64)
+  if (path < NVFP4_PATH_AUTO || path > NVFP4_PATH_MID)
     return fail(NVFP4_ERR_INVALID_ARG, "unknown path %d", path);
   const int prev = g_path;
   g_path = path;
@@ -424,7 +442,7 @@ int nvfp4_gemm(int mode, const void* a, const uint8_t* a_scales, const void* w_p
   if (st) return st;
   nvfp4::GemmArgs ga{a, a_scales, static_cast<const uint8_t*>(w_packed), M, N, K, alpha, nullptr, out, nullptr};
   const int epi = out_dtype == NVFP4_DTYPE_F32 ? nvfp4::kOutF32 : nvfp4::kOutBF16;
-  return hip_status(run_gemm(choose_path(mode, M), mode, epi, ga, as_stream(stream)), "gemm launch");
+  return hip_status(run_gemm(choose_path(mode, M, false), mode, epi, ga, as_stream(stream)), "gemm launch");
 }
 
 int gemm_swiglu_nvfp4_quant(const uint8_t* a_codes, const uint8_t* a_scales, const void* w_gu_packed,
@@ -440,7 +458,7 @@ int gemm_swiglu_nvfp4_quant(const uint8_t* a_codes, const uint8_t* a_scales, con
   if (st) return st;
   nvfp4::GemmArgs ga{a_codes, a_scales, static_cast<const uint8_t*>(w_gu_packed), M, 2 * I, K, alpha, g2_inv,
                      h_codes, h_scales};
-  return hip_status(run_gemm(choose_path(NVFP4_MODE_W4A4, M), NVFP4_MODE_W4A4, nvfp4::kSwigluNvfp4, ga, as_stream(stream)),
+  return hip_status(run_gemm(choose_path(NVFP4_MODE_W4A4, M, true), NVFP4_MODE_W4A4, nvfp4::kSwigluNvfp4, ga, as_stream(stream)),
                     "gemm_swiglu_nvfp4_quant launch");
 }
 
@@ -458,7 +476,7 @@ int nvfp4_gemm_rowscale(const uint8_t* a_codes, const uint8_t* a_scales, const f
   nvfp4::GemmArgs ga{a_codes, a_scales, static_cast<const uint8_t*>(w_packed), M, N, K, g_w, nullptr, out, nullptr};
   ga.row_scale = row_g;
   const int epi = out_dtype == NVFP4_DTYPE_F32 ? nvfp4::kOutF32 : nvfp4::kOutBF16;
-  return hip_status(run_gemm(choose_path(NVFP4_MODE_W4A4, M), NVFP4_MODE_W4A4, epi, ga, as_stream(stream)),
+  return hip_status(run_gemm(choose_path(NVFP4_MODE_W4A4, M, false), NVFP4_MODE_W4A4, epi, ga, as_stream(stream)),
                     "gemm_rowscale launch");
 }
 
@@ -477,7 +495,7 @@ int gemm_swiglu_nvfp4_quant_rowscale(const uint8_t* a_codes, const uint8_t* a_sc
   nvfp4::GemmArgs ga{a_codes, a_scales, static_cast<const uint8_t*>(w_gu_packed), M, 2 * I, K, g_w, g2_inv,
                      h_codes, h_scales};
   ga.row_scale = row_g;
-  return hip_status(run_gemm(choose_path(NVFP4_MODE_W4A4, M), NVFP4_MODE_W4A4, nvfp4::kSwigluNvfp4, ga,
+  return hip_status(run_gemm(choose_path(NVFP4_MODE_W4A4, M, true), NVFP4_MODE_W4A4, nvfp4::kSwigluNvfp4, ga,
                              as_stream(stream)),
                     "gemm_swiglu_nvfp4_quant_rowscale launch");
 }
@@ -495,7 +513,7 @@ int gemm_swiglu(int mode, const void* a, const uint8_t* a_scales, const void* w_
   if (st) return st;
   nvfp4::GemmArgs ga{a, a_scales, static_cast<const uint8_t*>(w_gu_packed), M, 2 * I, K, alpha, nullptr, h, nullptr};
   const int epi = h_dtype == NVFP4_DTYPE_F32 ? nvfp4::kSwigluF32 : nvfp4::kSwigluBF16;
-  return hip_status(run_gemm(choose_path(mode, M), mode, epi, ga, as_stream(stream)), "gemm_swiglu launch");
+  return hip_status(run_gemm(choose_path(mode, M, true), mode, epi, ga, as_stream(stream)), "gemm_swiglu launch");
 }
 
 // Activation part of the workspace: W4A4 x and h as NVFP4 (W4A4_DYN then
@@ -553,7 +571,7 @@ static uint64_t* tail_records(void* ws, size_t ws_bytes, size_t record_bytes) {
 // every path, so the size does not depend on the path override.
 static size_t mlp_split_bytes(int mode, int64_t M, int64_t H, int64_t I) {
   size_t most = 0;
-  for (int path : {NVFP4_PATH_GEMV, NVFP4_PATH_STREAM, NVFP4_PATH_TILED, NVFP4_PATH_TILED64}) {
+  for (int path : {NVFP4_PATH_GEMV, NVFP4_PATH_STREAM, NVFP4_PATH_TILED, NVFP4_PATH_TILED64, NVFP4_PATH_MID}) {
     // The two GEMMs share the partials region (they run one after the
     // other) and have counters of their own.
     const SplitPlan d = split_plan(mlp_kernel(path, mode, M, H, I), mode, M, H, I, false);
@@ -565,10 +583,10 @@ static size_t mlp_split_bytes(int mode, int64_t M, int64_t H, int64_t I) {
 
 // Workspace of an mlp_forward call on one path (the size of mlp_workspace_bytes
 // with the split-K plan of that path's kernels only).
-static size_t mlp_path_bytes(int mode, int64_t M, int64_t H, int64_t I, int path) {
+static size_t mlp_path_bytes(int mode, int64_t M, int64_t H, int64_t I, int path_gu, int path_d) {
   const int kmode = (mode == NVFP4_MODE_W4A16 || mode == NVFP4_MODE_W4A16_AWQ) ? NVFP4_MODE_W4A16 : NVFP4_MODE_W4A4;
-  const SplitPlan d = split_plan(mlp_kernel(path, kmode, M, H, I), kmode, M, H, I, false);
-  const SplitPlan g = split_plan(mlp_kernel(path, kmode, M, 2 * I, H), kmode, M, 2 * I, H, true);
+  const SplitPlan d = split_plan(mlp_kernel(path_d, kmode, M, H, I), kmode, M, H, I, false);
+  const SplitPlan g = split_plan(mlp_kernel(path_gu, kmode, M, 2 * I, H), kmode, M, 2 * I, H, true);
   return mlp_act_bytes(mode, static_cast<size_t>(M), H, I) + std::max(d.part_bytes, g.part_bytes) + d.counter_bytes +
          g.counter_bytes + tail_bytes(H, I);
 }
@@ -678,7 +696,7 @@ static int mlp_forward_impl(int mode, const uint16_t* x, int64_t M, int64_t H, i
     return fail(NVFP4_ERR_INVALID_ARG, "buffers must be 16-byte aligned");
   if (use_scratch) {
     const int kmode = (mode == NVFP4_MODE_W4A16 || mode == NVFP4_MODE_W4A16_AWQ) ? NVFP4_MODE_W4A16 : NVFP4_MODE_W4A4;
-    const size_t need = mlp_path_bytes(mode, M, H, I, choose_path(kmode, M));
+    const size_t need = mlp_path_bytes(mode, M, H, I, choose_path(kmode, M, true), choose_path(kmode, M, false));
     if (need > NVFP4_NOALLOC_SCRATCH_BYTES)
       return fail(NVFP4_ERR_INVALID_ARG,
                   "mlp_forward_noalloc: M=%lld H=%lld I=%lld needs %zu bytes of workspace, more than the %zu of the "
@@ -701,7 +719,8 @@ static int mlp_forward_impl(int mode, const uint16_t* x, int64_t M, int64_t H, i
   const bool dyn = mode == NVFP4_MODE_W4A4_DYN;
   if (dyn) mode = NVFP4_MODE_W4A4;  // the W4A4 kernels, x quantized per token
   if (mode == NVFP4_MODE_W4A16_AWQ) mode = NVFP4_MODE_W4A16;  // the W4A16 kernels on pre-scaled inputs
-  const int path = choose_path(mode, M);
+  const int path = choose_path(mode, M, true);  // the gate_up GEMM's (and decode checks')
+  const int path_d = choose_path(mode, M, false);
   const int epi_out = out_dtype == NVFP4_DTYPE_F32 ? nvfp4::kOutF32 : nvfp4::kOutBF16;
   uint8_t* base = static_cast<uint8_t*>(ws);
   const size_t m = static_cast<size_t>(M);
@@ -712,7 +731,7 @@ static int mlp_forward_impl(int mode, const uint16_t* x, int64_t M, int64_t H, i
   // rounds first and its K-split tail tiles in a second launch); every split
   // GEMM also leaves its counters at zero.
   const Kernel k_gu = mlp_kernel(path, mode, M, 2 * I, H);
-  const Kernel k_d = mlp_kernel(path, mode, M, H, I);
+  const Kernel k_d = mlp_kernel(path_d, mode, M, H, I);
   SplitPlan sp = split_plan(k_d, mode, M, H, I, false);
   SplitPlan sg = split_plan(k_gu, mode, M, 2 * I, H, true);
   if (!clears_counters(k_gu)) sp = sg = SplitPlan{};
@@ -753,7 +772,7 @@ static int mlp_forward_impl(int mode, const uint16_t* x, int64_t M, int64_t H, i
       with_split(g1, g2);
       e = run_gemm(path, NVFP4_MODE_W4A4, nvfp4::kSwigluNvfp4, g1, s);
       if (e != hipSuccess) return hip_status(e, "mlp_forward gate_up");
-      return hip_status(run_gemm(path, NVFP4_MODE_W4A4, epi_out, g2, s), "mlp_forward down");
+      return hip_status(run_gemm(path_d, NVFP4_MODE_W4A4, epi_out, g2, s), "mlp_forward down");
     }
     // One token under the automatic path: the whole forward in one launch
     // (x quantized as it is staged, h handed from the gate_up workgroups to
@@ -790,7 +809,7 @@ static int mlp_forward_impl(int mode, const uint16_t* x, int64_t M, int64_t H, i
     with_split(g1, g2);
     e = run_gemm(path, NVFP4_MODE_W4A4, nvfp4::kSwigluNvfp4, g1, s);
     if (e != hipSuccess) return hip_status(e, "mlp_forward gate_up");
-    e = run_gemm(path, NVFP4_MODE_W4A4, epi_out, g2, s);
+    e = run_gemm(path_d, NVFP4_MODE_W4A4, epi_out, g2, s);
     return hip_status(e, "mlp_forward down");
   }
   uint8_t* hb = base;
@@ -823,7 +842,7 @@ static int mlp_forward_impl(int mode, const uint16_t* x, int64_t M, int64_t H, i
   with_split(g1, g2);
   e = run_gemm(path, NVFP4_MODE_W4A16, nvfp4::kSwigluBF16, g1, s);
   if (e != hipSuccess) return hip_status(e, "mlp_forward gate_up");
-  e = run_gemm(path, NVFP4_MODE_W4A16, epi_out, g2, s);
+  e = run_gemm(path_d, NVFP4_MODE_W4A16, epi_out, g2, s);
   return hip_status(e, "mlp_forward down");
 }
 

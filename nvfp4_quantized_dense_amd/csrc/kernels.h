@@ -132,6 +132,9 @@ constexpr int64_t kFp4GemvLdsBytes = 65536;
 bool fp4_gemv_supported(int64_t M, int64_t K);
 hipError_t launch_fp4_gemv(int epi, const GemmArgs& a, hipStream_t s);
 hipError_t launch_tiled_gemm(int mode, int epi, const GemmArgs& a, hipStream_t s);
+// mid.hip: the W4A4 mid-size kernel (unsplit, one expert).
+bool mid_supported(const GemmArgs& a);
+hipError_t launch_mid_gemm(int epi, const GemmArgs& a, hipStream_t s);
 
 // The tiled kernels run one workgroup per CU, so output tiles go in rounds
 // of kTiledSlots; tiled_tail(units) is the tile count of the last, partial

@@ -1,0 +1,220 @@
+// mid.hip -- W4A4 GEMM for mid token counts (tens of tokens), with the
+// activation dequantized once per workgroup.
+//
+// In the weight-streaming kernel every wave dequantizes the activation
+// fragments of its own K tiles for just the 16 or 32 weight rows of its
+// workgroup; at 64 tokens that is two thirds of its VALU. Here a workgroup
+// of 4 waves owns 128 weight rows (8 row groups; wave w: groups 2 w and
+// 2 w + 1, a gate/up pair for the SwiGLU epilogues) x 64 tokens, and all
+// its waves step through the K tiles together:
+//
+//  * each wave streams its own two weight tiles per K tile into registers
+//    (16-byte loads, one K tile ahead) and dequantizes them, as the
+//    streaming kernel does;
+//  * each wave also loads one of the 4 token groups' NVFP4 slice of the
+//    next K tile and writes it dequantized (exact f16) into an LDS image of
+//    the 64 tokens x 256 columns, double-buffered, so one barrier per K tile
+//    separates writing the next image from reading the current one;
+//  * the token fragments of every MFMA are read back from the image.
+//
+// Token rows past M lie past the end of the activation buffers and load as
+// zeros; row groups past N are clamped to the last one and never stored.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace nvfp4 {
+
+constexpr int kMidWaves = 4;
+constexpr int kMidTG = 4;                   // token groups per workgroup
+constexpr int kMidRowBytes = 512;           // one token's 256 f16 columns
+[[maybe_unused]] constexpr int kMidImg = kMidTG * 16 * kMidRowBytes;
+
+#if defined(__HIP_DEVICE_COMPILE__)
+namespace {
+
+// One K tile of one wave: its two weight tiles and its token group's slice.
+struct MidLoad {
+  u32x4 wc[2][2];
+  uint32_t wsd[2];
+  u32x4 xc[2];
+  uint32_t xs[2];
+};
+
+// Image offset of 16-byte chunk `chunk` (8 columns, 0..31) of token row r:
+// within each 128-column half the chunks sit at (chunk % 16) ^ key(r % 16),
+// key swapping the two 2-bit halves of its argument, so that a fragment read
+// (lane l: row l % 16, chunk 16 c + 4 (l / 16) + u) by a quarter-wave, and
+// by the 16 lanes of equal l % 4, hits 16 distinct 16-byte slots.
+__device__ __forceinline__ int mid_key(int r) { return ((r >> 2) & 3) ^ ((r & 3) << 2); }
+
+__device__ __forceinline__ void mid_load(MidLoad& d, Rsrc w, Rsrc a, Rsrc s, const uint32_t (&gbase)[2],
+                                         uint32_t a_lane, uint32_t s_lane, int64_t t, int64_t T, int lane) {
+  const bool in = t < T;
+  const uint32_t tw = in ? (uint32_t)(t * kTileBytes) : kOutOfRange;
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    d.wc[g][0] = bload16_nt(w, tw + 16 * lane, gbase[g]);
+    d.wc[g][1] = bload16_nt(w, tw + 1024 + 16 * lane, gbase[g]);
+    d.wsd[g] = bload4_nt(w, tw + kTileCodeBytes + 4 * lane, gbase[g]);
+  }
+  const uint32_t ta = in ? a_lane + (uint32_t)(t * 128) : kOutOfRange;
+  const uint32_t ts = in ? s_lane + (uint32_t)(t * 16) : kOutOfRange;
+  d.xc[0] = bload16(a, ta);
+  d.xc[1] = bload16(a, ta + 64);
+  d.xs[0] = bload2(s, ts);
+  d.xs[1] = bload2(s, ts + 8);
+}
+
+// This wave's token group (16 rows of the image) from the loaded slice.
+__device__ __forceinline__ void mid_put(uint8_t* img, const MidLoad& d, int wave, int lane) {
+  const int q = lane >> 4, tl = lane & 15;
+  const int key = mid_key(tl);
+  uint8_t* row = img + (16 * wave + tl) * kMidRowBytes;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const f16x2 sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d.xs[c], 1.0f, false);  // blocks 8 c + 2 q, + 1
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const _Float16 sv = (u >> 1) ? sc.y : sc.x;
+      *reinterpret_cast<f16x8*>(row + 256 * c + 16 * ((4 * q + u) ^ key)) = deq8_f16(d.xc[c][u], sv);
+    }
+  }
+}
+
+// One K tile: the wave's two weight tiles dequantized in registers, the 4
+// token groups' fragments read from the image.
+__device__ __forceinline__ void mid_compute(f32x4 (&acc)[2][kMidTG], const MidLoad& d, const uint8_t* img, int lane) {
+  const int q = lane >> 4, tl = lane & 15;
+  const int key = mid_key(tl);
+  _Float16 ws[2][4];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const f16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d.wsd[g], 1.0f, false);
+    const f16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d.wsd[g], 1.0f, true);
+    ws[g][0] = lo.x; ws[g][1] = lo.y; ws[g][2] = hi.x; ws[g][3] = hi.y;
+  }
+  const uint8_t* row = img + tl * kMidRowBytes;
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int sb = 2 * c + (u >> 1);
+      const int off = 256 * c + 16 * ((4 * q + u) ^ key);
+      f16x8 B[kMidTG];
+#pragma unroll
+      for (int j = 0; j < kMidTG; ++j) B[j] = *reinterpret_cast<const f16x8*>(row + j * 16 * kMidRowBytes + off);
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const f16x8 A = deq8_f16(d.wc[g][c][u], ws[g][sb]);
+#pragma unroll
+        for (int j = 0; j < kMidTG; ++j) acc[g][j] = mfma16x16x32(A, B[j], acc[g][j]);
+      }
+    }
+}
+
+}  // namespace
+#endif  // __HIP_DEVICE_COMPILE__
+
+// Grid (ceil(N / 128), ceil(M / 64)); workgroup (x, y) owns row groups
+// 8 x .. 8 x + 7 and tokens 64 y .. 64 y + 63. (8-wave workgroups whose two
+// halves take alternate K tiles, adding their partial sums in LDS at the
+// end, measured slower: gate_up at 64 tokens, hidden 7168, 68.9 against
+// 67.2 us.)
+template <int EPI>
+__global__ __launch_bounds__(kMidWaves * 64, 2) void k_mid(GemmArgs args) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __shared__ __attribute__((aligned(16))) uint8_t img[2][kMidImg];
+  clear_words(args.zero_ptr, args.zero_n);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int q = lane >> 4, tl = lane & 15;
+  const int64_t M = args.M, N = args.N, K = args.K, T = K / kTileK;
+  const int64_t ngroups = N / kTileRows;
+  const int64_t rg = (int64_t)blockIdx.x * 8 + 2 * wave;  // this wave's first row group
+  const int64_t tok0 = (int64_t)blockIdx.y * 16 * kMidTG;
+
+  const Rsrc w = make_rsrc(args.w, (uint32_t)(ngroups * T * kTileBytes));
+  const Rsrc a = make_rsrc(args.a, (uint32_t)(M * (K / 2)));
+  const Rsrc s = make_rsrc(args.a_scales, (uint32_t)(M * (K / 16)));
+  uint32_t gbase[2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const int64_t grp = rg + g < ngroups ? rg + g : ngroups - 1;
+    gbase[g] = __builtin_amdgcn_readfirstlane((uint32_t)(grp * T * kTileBytes));
+  }
+  // This wave's token group of the image: rows tok0 + 16 wave + l % 16 (past
+  // M: out of range, zeros).
+  const int64_t trow = tok0 + 16 * wave + tl;
+  const uint32_t a_lane = (uint32_t)(trow * (K / 2) + 16 * q);
+  const uint32_t s_lane = (uint32_t)(trow * (K / 16) + 2 * q);
+  const float alpha = uniform_now(args.alpha);
+  const float g2i = EPI == kSwigluNvfp4 ? uniform_now(args.g2_inv) : 0.0f;
+
+  f32x4 acc[2][kMidTG];
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int j = 0; j < kMidTG; ++j) acc[g][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // K tile t is multiplied from cur (weights) and image t % 2; nxt holds
+  // K tile t + 1, whose token slice goes into the other image once the tile
+  // t arithmetic is issued; the barrier then publishes it (and frees image
+  // t % 2 for K tile t + 2). (Loads two K tiles ahead, in three register
+  // sets, measured slower: 242 against 176 VGPRs.)
+  MidLoad cur, nxt;
+  mid_load(cur, w, a, s, gbase, a_lane, s_lane, 0, T, lane);
+  mid_load(nxt, w, a, s, gbase, a_lane, s_lane, 1, T, lane);
+  mid_put(img[0], cur, wave, lane);
+  __syncthreads();
+  for (int64_t t = 0; t < T; ++t) {
+    const int b = (int)(t & 1);
+    mid_compute(acc, cur, img[b], lane);
+    if (t + 1 < T) mid_put(img[b ^ 1], nxt, wave, lane);
+    cur = nxt;
+    mid_load(nxt, w, a, s, gbase, a_lane, s_lane, t + 2, T, lane);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int j = 0; j < kMidTG; ++j) {
+    const int64_t token = tok0 + 16 * j + tl;
+    const bool tv = token < M;
+    const float at = row_alpha(alpha, args.row_scale, tv, token);
+    if constexpr (EpiTraits<EPI>::swiglu) {
+      store_swiglu<EPI>(acc[0][j], acc[1][j], at, g2i, tv && rg < ngroups, token, (rg >> 1) * kTileRows, lane,
+                        N / 2, args.out, args.out_scales);
+    } else {
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+        store_dense<EPI>(acc[g][j], at, tv && rg + g < ngroups, token, (rg + g) * kTileRows + 4 * q, N, args.out);
+    }
+  }
+#endif  // __HIP_DEVICE_COMPILE__
+}
+
+template <int EPI>
+static hipError_t mid_launch(const GemmArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)((a.N / kTileRows + 7) / 8), (unsigned)((a.M + 16 * kMidTG - 1) / (16 * kMidTG)));
+  k_mid<EPI><<<grid, kMidWaves * 64, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+bool mid_supported(const GemmArgs& a) { return a.experts <= 1 && a.ksplit == 1 && a.M <= 65535 * 64; }
+
+// W4A4 only, unsplit, one expert. Needs the packed weight and the
+// activation rows below 2^31 bytes (32-bit buffer offsets); the caller
+// checks.
+hipError_t launch_mid_gemm(int epi, const GemmArgs& a, hipStream_t s) {
+  if (a.M == 0) return hipSuccess;
+  if (!mid_supported(a)) return hipErrorInvalidValue;
+  switch (epi) {
+    case kOutF32: return mid_launch<kOutF32>(a, s);
+    case kOutBF16: return mid_launch<kOutBF16>(a, s);
+    case kSwigluNvfp4: return mid_launch<kSwigluNvfp4>(a, s);
+    case kSwigluBF16: return mid_launch<kSwigluBF16>(a, s);
+    case kSwigluF32: return mid_launch<kSwigluF32>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace nvfp4

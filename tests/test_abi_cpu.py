@@ -112,7 +112,7 @@ def test_path_override_is_per_thread():
     t.join()
     assert seen == [nv.PATH_AUTO]           # another thread starts at AUTO
     assert nv.set_path(nv.PATH_AUTO) == nv.PATH_TILED64
-    assert nv.lib().nvfp4_set_path(5) == nv.NVFP4_ERR_INVALID_ARG
+    assert nv.lib().nvfp4_set_path(6) == nv.NVFP4_ERR_INVALID_ARG
 
 
 def _code(fn, *args):

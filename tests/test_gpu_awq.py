@@ -26,7 +26,7 @@ def _lib():
     nv.set_path(nv.PATH_AUTO)
 
 
-PATHS = {"gemv": 1, "stream": 2, "tiled": 3, "tiled64": 4}
+PATHS = {"gemv": 1, "stream": 2, "tiled": 3, "tiled64": 4, "mid": 5}
 
 
 def awq_scales(seed, n):

@@ -32,7 +32,7 @@ def _lib():
 
 # "tiled64" forces the 64-bit-addressed tiled kernel, which the other paths
 # run only for operands of 2^31 bytes or more.
-PATHS = {"gemv": 1, "stream": 2, "tiled": 3, "tiled64": 4}
+PATHS = {"gemv": 1, "stream": 2, "tiled": 3, "tiled64": 4, "mid": 5}
 
 
 @pytest.fixture(params=list(PATHS))
@@ -358,10 +358,11 @@ def test_mlp_tiny_workload(path, mode):
     _check_mlp(mode, 4, 256, 512)
 
 
-@pytest.mark.parametrize("M", [1, 7, 24, 48, 56, 64, 100, 128, 144, 200])
+@pytest.mark.parametrize("M", [1, 7, 24, 48, 56, 63, 64, 100, 128, 144, 200, 256, 257])
 def test_mlp_auto_dispatch(M):
     """Token counts on both sides of each automatic switch: W4A16 streams up
-    to 48 tokens, W4A4 up to 128; the tiled kernels take over above."""
+    to 48 tokens, W4A4 up to 128 (its gate_up from 64 to 256 tokens on the
+    mid-size kernel); the tiled kernels take over above."""
     nv.set_path(nv.PATH_AUTO)
     _check_mlp("w4a4", M, 512, 768, seed=M)
     _check_mlp("w4a16", M, 512, 768, seed=M)
@@ -394,7 +395,7 @@ def test_mlp_decode_full_size():
     assert to_host(nv.mlp_workspace_status(ws))[0] == 0
 
 
-@pytest.mark.parametrize("M", [1, 4, 16, 64, 128])
+@pytest.mark.parametrize("M", [1, 4, 16, 64, 128, 300])
 def test_mlp_small_batch_full_size(M):
     """Fused W4A4 MLP, hidden 7168, intermediate 18432."""
     nv.set_path(nv.PATH_AUTO)
