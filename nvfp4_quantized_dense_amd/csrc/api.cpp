@@ -568,15 +568,20 @@ static uint64_t* tail_records(void* ws, size_t ws_bytes, size_t record_bytes) {
 }
 
 // Split-K partials and counters of the largest plan over the kernels of
-// every path, so the size does not depend on the path override.
+// every path, for either GEMM on any path (the automatic path picks the
+// gate_up's and the down projection's separately), so the size does not
+// depend on the path override.
 static size_t mlp_split_bytes(int mode, int64_t M, int64_t H, int64_t I) {
   size_t most = 0;
-  for (int path : {NVFP4_PATH_GEMV, NVFP4_PATH_STREAM, NVFP4_PATH_TILED, NVFP4_PATH_TILED64, NVFP4_PATH_MID}) {
-    // The two GEMMs share the partials region (they run one after the
-    // other) and have counters of their own.
-    const SplitPlan d = split_plan(mlp_kernel(path, mode, M, H, I), mode, M, H, I, false);
-    const SplitPlan g = split_plan(mlp_kernel(path, mode, M, 2 * I, H), mode, M, 2 * I, H, true);
-    most = std::max(most, std::max(d.part_bytes, g.part_bytes) + d.counter_bytes + g.counter_bytes);
+  constexpr int kPaths[] = {NVFP4_PATH_GEMV, NVFP4_PATH_STREAM, NVFP4_PATH_TILED, NVFP4_PATH_TILED64, NVFP4_PATH_MID};
+  for (int pg : kPaths) {
+    const SplitPlan g = split_plan(mlp_kernel(pg, mode, M, 2 * I, H), mode, M, 2 * I, H, true);
+    for (int pd : kPaths) {
+      // The two GEMMs share the partials region (they run one after the
+      // other) and have counters of their own.
+      const SplitPlan d = split_plan(mlp_kernel(pd, mode, M, H, I), mode, M, H, I, false);
+      most = std::max(most, std::max(d.part_bytes, g.part_bytes) + d.counter_bytes + g.counter_bytes);
+    }
   }
   return most;
 }

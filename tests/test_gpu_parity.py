@@ -416,11 +416,14 @@ def test_mlp_small_batch_full_size(M):
 # The GEMV cases run the W4A4 gate_up with the quantization of x fused.
 
 @pytest.mark.parametrize("I", [6912, 8192])
-@pytest.mark.parametrize("kpath,M", [("gemv", 1), ("gemv", 2), ("stream", 3), ("stream", 16),
-                                     ("stream", 40), ("tiled", 200)])
+@pytest.mark.parametrize("kpath,M,H", [("gemv", 1, 512), ("gemv", 2, 512), ("stream", 3, 512), ("stream", 16, 512),
+                                       ("stream", 40, 512), ("tiled", 200, 512), ("mid", 64, 512),
+                                       ("mid", 100, 512), ("mid", 64, 2048), ("mid", 200, 2048)])
 @pytest.mark.parametrize("mode", ["w4a4", "w4a16"])
-def test_mlp_split_k(mode, kpath, M, I):
-    H = 512
+def test_mlp_split_k(mode, kpath, M, H, I):
+    """(The mid-size kernel does not split K; its cases run the forward with
+    it on the gate_up and the down projection through the dirty, reused
+    workspace all the same.)"""
     prev = nv.set_path(PATHS[kpath])
     try:
         w = mlp_weights(H, I, 0)
