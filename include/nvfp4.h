@@ -88,7 +88,7 @@ extern "C" {
                                 split-K; the grouped GEMM treats it as NVFP4_PATH_TILED) */
 #define NVFP4_PATH_MID 5     /* W4A4: 128 weight rows x 64 tokens per workgroup, the activation
                                 dequantized once per workgroup into LDS (any M; chosen for the
-                                W4A4 SwiGLU GEMMs of 64 to 256 tokens); W4A16 runs
+                                W4A4 SwiGLU GEMMs of 64 to 512 tokens); W4A16 runs
                                 NVFP4_PATH_STREAM; the grouped GEMM treats it as NVFP4_PATH_STREAM */
 
 /* Message of the last failed call on this thread ("" if none). */

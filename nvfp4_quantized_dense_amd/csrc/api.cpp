@@ -117,17 +117,16 @@ constexpr int64_t kGroupedStreamMaxM = 256;
 
 // Token counts at which a W4A4 GEMM with a SwiGLU epilogue (the gate_up of
 // the MLP) runs the mid-size kernel under the automatic path. Gate_up alone
-// (hidden 7168 / 5120): 64 tokens 78.9 / 61.0 us streaming against 68.8 /
-// 50.4; 128: 138.0 / 103.6 against 113.4 / 82.6; 192: 182.2 / 134.4 tiled
-// against 150.8 / 110.8; 256: 183.1 / 135.0 tiled against 192.5 / 138.6;
-// below 64 tokens streaming wins (48: 62.8 / 47.9 against 66.6 / 49.0).
-// Whole forward (hidden 7168): 256 tokens 287.9 -> 270.6 us, 144 tokens
-// 277.9 -> 224.1 us, 64 tokens 123.3 -> 108.3 us; at 512 tokens the tiled
-// gate_up with its K-split tail (mlp_forward) beats it: 439.7 against 468.0.
-// Dense GEMMs (the down projection, 5120 / 7168 rows: 40 / 56 mid-size
-// workgroups per 64 tokens) keep the streaming and tiled kernels, whose
-// split-K fills the CUs.
-constexpr int64_t kMidMinM = 64, kMidMaxM = 256;
+// (hidden 7168 / 5120): 64 tokens 78.9 / 61.0 us streaming against 69.0 /
+// 51.8; 128: 138.0 / 103.6 against 106.9 / 78.3; 256: 183.1 / 135.0 tiled
+// against 161.5 / 121.1; below 64 tokens streaming wins (48: 62.8 / 47.9
+// against 66.6 / 49.0). Whole forward, tiled gate_up (with its K-split tail)
+// against mid-size: 384 tokens 439.4 / 345.4 against 374.7 / 276.4 us, 512:
+// 463.7 / 362.9 against 441.9 / 322.9; 768: 608.7 / 442.7 against 633.9 /
+// 443.3, and the tiled kernel wins above. Dense GEMMs (the down projection,
+// 5120 / 7168 rows: 40 / 56 mid-size workgroups per 64 tokens) keep the
+// streaming and tiled kernels, whose split-K fills the CUs.
+constexpr int64_t kMidMinM = 64, kMidMaxM = 512;
 
 // Kernel class for a GEMM of M tokens: the decode GEMV up to M = 2 (W4A4,
 // whose FP4 GEMV carries two tokens per workgroup) or M = 1 (W4A16), the

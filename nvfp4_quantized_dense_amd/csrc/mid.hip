@@ -115,23 +115,31 @@ __device__ __forceinline__ void mid_compute(f32x4 (&acc)[2][kMidTG], const MidLo
 }  // namespace
 #endif  // __HIP_DEVICE_COMPILE__
 
-// Grid (ceil(N / 128), ceil(M / 64)); workgroup (x, y) owns row groups
-// 8 x .. 8 x + 7 and tokens 64 y .. 64 y + 63. (8-wave workgroups whose two
+// Grid: 8 * per_xcd workgroups over n_tiles x m_tiles output tiles (128
+// rows x 64 tokens). Workgroup ids are dealt round-robin to the 8 XCDs, so
+// logical workgroup f = (id % 8) * per_xcd + id / 8 takes tile (f / m_tiles,
+// f % m_tiles): the token tiles of one weight tile run side by side on one
+// XCD and read its weight through the same L2; f >= tiles exits. (8-wave workgroups whose two
 // halves take alternate K tiles, adding their partial sums in LDS at the
 // end, measured slower: gate_up at 64 tokens, hidden 7168, 68.9 against
 // 67.2 us.)
 template <int EPI>
-__global__ __launch_bounds__(kMidWaves * 64, 2) void k_mid(GemmArgs args) {
+__global__ __launch_bounds__(kMidWaves * 64, 2) void k_mid(GemmArgs args, int64_t m_tiles, int64_t tiles,
+                                                           int64_t per_xcd) {
 #if defined(__HIP_DEVICE_COMPILE__)
   __shared__ __attribute__((aligned(16))) uint8_t img[2][kMidImg];
   clear_words(args.zero_ptr, args.zero_n);
+  const int64_t id = blockIdx.x;
+  const int64_t f = (id & 7) * per_xcd + (id >> 3);
+  if (f >= tiles) return;
+  const int64_t n_tile = f / m_tiles, m_tile = f - n_tile * m_tiles;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int q = lane >> 4, tl = lane & 15;
   const int64_t M = args.M, N = args.N, K = args.K, T = K / kTileK;
   const int64_t ngroups = N / kTileRows;
-  const int64_t rg = (int64_t)blockIdx.x * 8 + 2 * wave;  // this wave's first row group
-  const int64_t tok0 = (int64_t)blockIdx.y * 16 * kMidTG;
+  const int64_t rg = n_tile * 8 + 2 * wave;  // this wave's first row group
+  const int64_t tok0 = m_tile * 16 * kMidTG;
 
   const Rsrc w = make_rsrc(args.w, (uint32_t)(ngroups * T * kTileBytes));
   const Rsrc a = make_rsrc(args.a, (uint32_t)(M * (K / 2)));
@@ -194,12 +202,14 @@ __global__ __launch_bounds__(kMidWaves * 64, 2) void k_mid(GemmArgs args) {
 
 template <int EPI>
 static hipError_t mid_launch(const GemmArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)((a.N / kTileRows + 7) / 8), (unsigned)((a.M + 16 * kMidTG - 1) / (16 * kMidTG)));
-  k_mid<EPI><<<grid, kMidWaves * 64, 0, s>>>(a);
+  const int64_t m_tiles = (a.M + 16 * kMidTG - 1) / (16 * kMidTG);
+  const int64_t tiles = (a.N / kTileRows + 7) / 8 * m_tiles;
+  const int64_t per_xcd = (tiles + 7) / 8;
+  k_mid<EPI><<<dim3((unsigned)(8 * per_xcd)), kMidWaves * 64, 0, s>>>(a, m_tiles, tiles, per_xcd);
   return hipGetLastError();
 }
 
-bool mid_supported(const GemmArgs& a) { return a.experts <= 1 && a.ksplit == 1 && a.M <= 65535 * 64; }
+bool mid_supported(const GemmArgs& a) { return a.experts <= 1 && a.ksplit == 1; }
 
 // W4A4 only, unsplit, one expert. Needs the packed weight and the
 // activation rows below 2^31 bytes (32-bit buffer offsets); the caller

@@ -358,10 +358,10 @@ def test_mlp_tiny_workload(path, mode):
     _check_mlp(mode, 4, 256, 512)
 
 
-@pytest.mark.parametrize("M", [1, 7, 24, 48, 56, 63, 64, 100, 128, 144, 200, 256, 257])
+@pytest.mark.parametrize("M", [1, 7, 24, 48, 56, 63, 64, 100, 128, 144, 200, 512, 513])
 def test_mlp_auto_dispatch(M):
     """Token counts on both sides of each automatic switch: W4A16 streams up
-    to 48 tokens, W4A4 up to 128 (its gate_up from 64 to 256 tokens on the
+    to 48 tokens, W4A4 up to 128 (its gate_up from 64 to 512 tokens on the
     mid-size kernel); the tiled kernels take over above."""
     nv.set_path(nv.PATH_AUTO)
     _check_mlp("w4a4", M, 512, 768, seed=M)
