@@ -187,30 +187,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void k_decode_mlp(DecodeArgs d) 
   }
   if (d.ksplit > 1) {
     // The last split adds the S partials of rows 16 r.. in split order.
-    f32x4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int sp = 0; sp + 1 < d.ksplit; ++sp) {
-      const uint64_t* p = rec_part + (sp * RG + r) * 16 + 4 * q;
-      uint64_t v[4] = {0, 0, 0, 0};
-      for (int spin = 0;; ++spin) {
-        bool ok = true;
-        if (lvalid) {
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            v[k] = get_record(p + k);
-            ok &= (uint32_t)(v[k] >> 32) == tag;
-          }
-        }
-        if (__all(ok)) break;
-        if (spin >= d.spin_limit) {
-          v[0] = v[1] = v[2] = v[3] = __float_as_uint(__builtin_nanf(""));
-          if (lane == 0) report_expired(d.status);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-      }
-#pragma unroll
-      for (int k = 0; k < 4; ++k) sum[k] += __uint_as_float((uint32_t)v[k]);
-    }
+    const f32x4 sum = sum_split_partials(rec_part, RG, r, d.ksplit, tag, d.spin_limit, d.status, lane);
 #pragma unroll
     for (int k = 0; k < 4; ++k) res[0][k] = sum[k] + res[0][k];
   }
