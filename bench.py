@@ -257,6 +257,7 @@ def main():
     default_line = args.workload is None and args.M is None and args.sweep is None
     if args.workload is None:
         args.workload = "decode_w4a4"
+    nv.set_path(args.path)
     if args.workload == "silu_quant":
         print(json.dumps(run_silu_quant(args)), flush=True)
         return
@@ -264,7 +265,6 @@ def main():
         print(json.dumps(run_grouped(args)), flush=True)
         return
     dev = torch.device("cuda:0")
-    nv.set_path(args.path)
     if not default_line:
         M0 = WORKLOADS[args.workload][0]
         Ms = [int(v) for v in args.sweep.split(",")] if args.sweep else [args.M if args.M is not None else M0]

@@ -88,8 +88,9 @@ extern "C" {
                                 split-K; the grouped GEMM treats it as NVFP4_PATH_TILED) */
 #define NVFP4_PATH_MID 5     /* W4A4: 128 weight rows x 64 tokens per workgroup, the activation
                                 dequantized once per workgroup into LDS (any M; chosen for the
-                                W4A4 SwiGLU GEMMs of 64 to 512 tokens); W4A16 runs
-                                NVFP4_PATH_STREAM; the grouped GEMM treats it as NVFP4_PATH_STREAM */
+                                W4A4 SwiGLU GEMMs of 64 to 512 tokens and the W4A4 grouped
+                                GEMMs of 64 to 512 tokens per expert); W4A16 runs
+                                NVFP4_PATH_STREAM */
 
 /* Message of the last failed call on this thread ("" if none). */
 const char* nvfp4_last_error(void);
@@ -339,10 +340,11 @@ int silu_mul_nvfp4_quant(const void* gate_up, int64_t E, int64_t M, int64_t I, c
  *   nvfp4_repack_bytes(NVFP4_REPACK_PLAIN, N, K) bytes.
  * masked_m: device int32 [E] (NULL: every row valid); alpha: device fp32 [E].
  * out: [E, M, N] of out_dtype; rows past masked_m[e] are not written.
- * All experts run in one launch (0 <= E <= 65535): of the weight-streaming
- * kernel up to 256 tokens per expert under NVFP4_PATH_AUTO, of the tiled
- * kernel above (or under NVFP4_PATH_TILED). Every workgroup reads its
- * expert's row count on the device. Errors as nvfp4_gemm;
+ * All experts run in one launch (0 <= E <= 65535). Under NVFP4_PATH_AUTO:
+ * W4A4 on the mid-size kernel from 64 to 512 tokens per expert (M),
+ * otherwise the weight-streaming kernel up to 256 tokens and the tiled
+ * kernel above; NVFP4_PATH_STREAM / _TILED / _MID (W4A4) force one. Every
+ * workgroup reads its expert's row count on the device. Errors as nvfp4_gemm;
  * NVFP4_ERR_UNSUPPORTED when one expert's operands reach 2^31 bytes.
  */
 int nvfp4_grouped_gemm(int mode, const void* a, const uint8_t* a_scales, const void* w_packed, int64_t E,

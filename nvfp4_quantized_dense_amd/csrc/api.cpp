@@ -114,6 +114,7 @@ int64_t stream_max_m(int mode) { return mode == NVFP4_MODE_W4A4 ? 128 : 48; }
 // Largest tokens per expert a grouped GEMM runs as one streaming launch
 // over all experts under the automatic path.
 constexpr int64_t kGroupedStreamMaxM = 256;
+constexpr int64_t kGroupedMidMinM = 64, kGroupedMidMaxM = 512;
 
 // Token counts at which a W4A4 GEMM with a SwiGLU epilogue (the gate_up of
 // the MLP) runs the mid-size kernel under the automatic path. Gate_up alone
@@ -904,12 +905,18 @@ int nvfp4_grouped_gemm(int mode, const void* a, const uint8_t* a_scales, const v
   // y of the tiled ones), each workgroup reading its expert's valid row
   // count from masked_m: an expert's GEMM alone is too narrow to fill the
   // CUs (4096 rows: 128 streaming workgroups, 16 x (M / 256) tiled ones).
-  // The weight-streaming kernel up to kGroupedStreamMaxM tokens per expert
-  // (under the automatic path; always under the stream or GEMV override),
-  // the tiled kernel above (always under the tiled override).
+  // W4A4 from kGroupedMidMinM to kGroupedMidMaxM tokens per expert on the
+  // mid-size kernel (always under its override; 8 experts of 4096 x 7168:
+  // 47 / 68 / 121 / 127 / 175 us at 64 / 128 / 256 / 384 / 512 tokens
+  // against 53 / 84 / 128 / 171 / 228 streaming and 185 tiled at 512);
+  // otherwise the weight-streaming kernel up to kGroupedStreamMaxM tokens
+  // per expert (under the automatic path; always under the stream or GEMV
+  // override), the tiled kernel above (always under the tiled override).
   const int p = g_path;
+  const bool mid = mode == NVFP4_MODE_W4A4 &&
+                   (p == NVFP4_PATH_AUTO ? M >= kGroupedMidMinM && M <= kGroupedMidMaxM : p == NVFP4_PATH_MID);
   const bool streaming =
-      p == NVFP4_PATH_AUTO ? M <= kGroupedStreamMaxM : (p != NVFP4_PATH_TILED && p != NVFP4_PATH_TILED64);
+      !mid && (p == NVFP4_PATH_AUTO ? M <= kGroupedStreamMaxM : (p != NVFP4_PATH_TILED && p != NVFP4_PATH_TILED64));
   nvfp4::GemmArgs g{a, a_scales, static_cast<const uint8_t*>(w_packed), M, N, K, alpha, nullptr, out, nullptr};
   g.m_dev = masked_m;
   if (E > 1) {
@@ -919,7 +926,8 @@ int nvfp4_grouped_gemm(int mode, const void* a, const uint8_t* a_scales, const v
     g.e_w = (int64_t)wbytes;
     g.e_out = (int64_t)(M * out_row);
   }
-  hipError_t err = streaming ? nvfp4::launch_stream_gemm(mode, epi, g, sm)
+  hipError_t err = mid         ? nvfp4::launch_mid_gemm(epi, g, sm)
+                   : streaming ? nvfp4::launch_stream_gemm(mode, epi, g, sm)
                    : mode == NVFP4_MODE_W4A4 ? nvfp4::launch_tiled2_gemm(epi, g, sm)
                                              : nvfp4::launch_tiled16_gemm(epi, g, sm);
   if (err != hipSuccess) return hip_status(err, "grouped_gemm launch");

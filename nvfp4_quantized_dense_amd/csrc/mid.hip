@@ -18,7 +18,8 @@
 //  * the token fragments of every MFMA are read back from the image.
 //
 // Token rows past M lie past the end of the activation buffers and load as
-// zeros; row groups past N are clamped to the last one and never stored.
+// zeros; row groups past N are clamped to the last one and never stored. A
+// grouped GEMM runs all its experts in one launch (grid y).
 #include "device_common.h"
 #include "kernels.h"
 
@@ -124,22 +125,27 @@ __device__ __forceinline__ void mid_compute(f32x4 (&acc)[2][kMidTG], const MidLo
 // end, measured slower: gate_up at 64 tokens, hidden 7168, 68.9 against
 // 67.2 us.)
 template <int EPI>
-__global__ __launch_bounds__(kMidWaves * 64, 2) void k_mid(GemmArgs args, int64_t m_tiles, int64_t tiles,
+__global__ __launch_bounds__(kMidWaves * 64, 2) void k_mid(GemmArgs args_in, int64_t m_tiles, int64_t tiles,
                                                            int64_t per_xcd) {
 #if defined(__HIP_DEVICE_COMPILE__)
   __shared__ __attribute__((aligned(16))) uint8_t img[2][kMidImg];
+  GemmArgs args = args_in;
   clear_words(args.zero_ptr, args.zero_n);
   const int64_t id = blockIdx.x;
   const int64_t f = (id & 7) * per_xcd + (id >> 3);
   if (f >= tiles) return;
+  if (args.experts > 1) expert_slice(args, blockIdx.y);  // grouped GEMM: grid y walks the experts
   const int64_t n_tile = f / m_tiles, m_tile = f - n_tile * m_tiles;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int q = lane >> 4, tl = lane & 15;
-  const int64_t M = args.M, N = args.N, K = args.K, T = K / kTileK;
+  // Valid token rows: M, or an expert's masked_m (rows past it read as
+  // zeros and are not stored; a token tile wholly past it has no work).
+  const int64_t M = valid_rows(args), N = args.N, K = args.K, T = K / kTileK;
   const int64_t ngroups = N / kTileRows;
   const int64_t rg = n_tile * 8 + 2 * wave;  // this wave's first row group
   const int64_t tok0 = m_tile * 16 * kMidTG;
+  if (tok0 >= M) return;
 
   const Rsrc w = make_rsrc(args.w, (uint32_t)(ngroups * T * kTileBytes));
   const Rsrc a = make_rsrc(args.a, (uint32_t)(M * (K / 2)));
@@ -205,15 +211,17 @@ static hipError_t mid_launch(const GemmArgs& a, hipStream_t s) {
   const int64_t m_tiles = (a.M + 16 * kMidTG - 1) / (16 * kMidTG);
   const int64_t tiles = (a.N / kTileRows + 7) / 8 * m_tiles;
   const int64_t per_xcd = (tiles + 7) / 8;
-  k_mid<EPI><<<dim3((unsigned)(8 * per_xcd)), kMidWaves * 64, 0, s>>>(a, m_tiles, tiles, per_xcd);
+  const unsigned ex = a.experts > 1 ? (unsigned)a.experts : 1u;
+  k_mid<EPI><<<dim3((unsigned)(8 * per_xcd), ex), kMidWaves * 64, 0, s>>>(a, m_tiles, tiles, per_xcd);
   return hipGetLastError();
 }
 
-bool mid_supported(const GemmArgs& a) { return a.experts <= 1 && a.ksplit == 1; }
+bool mid_supported(const GemmArgs& a) { return a.ksplit == 1; }
 
-// W4A4 only, unsplit, one expert. Needs the packed weight and the
-// activation rows below 2^31 bytes (32-bit buffer offsets); the caller
-// checks.
+// W4A4 only, unsplit; several experts (grid y, dense epilogues, each
+// expert's valid rows from masked_m) or one. Needs each expert's packed
+// weight and activation rows below 2^31 bytes (32-bit buffer offsets); the
+// caller checks.
 hipError_t launch_mid_gemm(int epi, const GemmArgs& a, hipStream_t s) {
   if (a.M == 0) return hipSuccess;
   if (!mid_supported(a)) return hipErrorInvalidValue;

@@ -1,6 +1,6 @@
 """GPU parity of the grouped (expert) NVFP4 GEMM with masked_m against the
-CPU oracle, W4A4 and W4A16, on the weight-streaming kernel (every expert in
-one launch) and the tiled kernels (one launch per expert): rows past
+CPU oracle, W4A4 and W4A16, on the weight-streaming, mid-size (W4A4) and
+tiled kernels (every expert in one launch): rows past
 masked_m keep the sentinel the output held, valid rows
 meet the fp32 tolerance, and each expert matches the plain GEMM entry."""
 import numpy as np
@@ -48,12 +48,14 @@ def _packed(wc, ws):
     (3, 300, 288, 512, [300, 1, 129]), (2, 64, 256, 256, None),
     (20, 16, 256, 512, [16, 0, 3, 16, 9, 0, 1, 12, 16, 5, 7, 0, 16, 2, 11, 16, 4, 8, 0, 15]),
     (4, 200, 256, 512, [200, 77, 0, 130])])
-@pytest.mark.parametrize("kpath", ["auto", "tiled", "stream"])
+@pytest.mark.parametrize("kpath", ["auto", "tiled", "stream", "mid"])
 def test_grouped_gemm_matches_oracle(kpath, mode, E, M, N, K, mm):
-    """Every expert runs in one launch: under the automatic path on the
-    weight-streaming kernel up to 256 tokens per expert and on the tiled
-    kernel above; the overrides force either kernel at any size."""
-    prev = nv.set_path({"tiled": nv.PATH_TILED, "stream": nv.PATH_STREAM}.get(kpath, nv.PATH_AUTO))
+    """Every expert runs in one launch: under the automatic path W4A4 on the
+    mid-size kernel from 64 to 512 tokens per expert, otherwise on the
+    weight-streaming kernel up to 256 tokens and on the tiled kernel above;
+    the overrides force a kernel at any size (W4A16 has no mid-size kernel:
+    its override runs the streaming one)."""
+    prev = nv.set_path({"tiled": nv.PATH_TILED, "stream": nv.PATH_STREAM, "mid": nv.PATH_MID}.get(kpath, nv.PATH_AUTO))
     try:
         _grouped_vs_oracle(mode, E, M, N, K, mm)
     finally:
