@@ -129,15 +129,28 @@ constexpr int64_t kGroupedMidMinM = 64, kGroupedMidMaxM = 512;
 // streaming and tiled kernels, whose split-K fills the CUs.
 constexpr int64_t kMidMinM = 64, kMidMaxM = 512;
 
+// W4A16 SwiGLU GEMMs take the mid-size kernel from 33 to 64 tokens, where
+// its 64-token tile beats the streaming kernel and the 128-token tiled one.
+// Gate_up alone, hidden 5120: 33 / 40 / 64 tokens 62.7 / 64.9 / 64.8 us
+// (streaming up to 48, then tiled) against 56.7 / 58.0 / 61.0; whole
+// forward at 40 / 48 / 64 tokens 96.2 / 98.9 / 121.6 against 88.4 / 89.6 /
+// 118.3 us. It loses at 32 (50.0 against 56.5) and from 65 to 128 (65.9
+// against 96.6 at 128: one tiled token tile). From 129 to 192 tokens it
+// beats the tiled gate_up alone (113.8 against 128.9 at 192) but not the
+// forward's, whose tail tiles are K-split (184.9 against 168.7 us).
+bool mid_w4a16(int64_t M) { return M >= 33 && M <= 64; }
+
 // Kernel class for a GEMM of M tokens: the decode GEMV up to M = 2 (W4A4,
 // whose FP4 GEMV carries two tokens per workgroup) or M = 1 (W4A16), the
-// mid-size kernel for W4A4 SwiGLU GEMMs of kMidMinM..kMidMaxM tokens, the
-// weight-streaming MFMA kernel up to stream_max_m, the LDS-tiled kernel above.
+// mid-size kernel for the SwiGLU GEMMs of kMidMinM..kMidMaxM tokens (W4A4)
+// or mid_w4a16 (W4A16), the weight-streaming MFMA kernel up to
+// stream_max_m, the LDS-tiled kernel above.
 int choose_path(int mode, int64_t M, bool swiglu) {
   int p = g_path;
   if (p != NVFP4_PATH_AUTO) return p;
   if (M <= (mode == NVFP4_MODE_W4A4 ? 2 : 1)) return NVFP4_PATH_GEMV;
   if (mode == NVFP4_MODE_W4A4 && swiglu && M >= kMidMinM && M <= kMidMaxM) return NVFP4_PATH_MID;
+  if (mode != NVFP4_MODE_W4A4 && swiglu && mid_w4a16(M)) return NVFP4_PATH_MID;
   if (M <= stream_max_m(mode)) return NVFP4_PATH_STREAM;
   return NVFP4_PATH_TILED;
 }
@@ -162,7 +175,7 @@ Kernel select_kernel(int path, int mode, const nvfp4::GemmArgs& a) {
       return kStream;
     }
     if (path == NVFP4_PATH_STREAM) return kStream;
-    if (path == NVFP4_PATH_MID) return mode == NVFP4_MODE_W4A4 && nvfp4::mid_supported(a) ? kMid : kStream;
+    if (path == NVFP4_PATH_MID) return nvfp4::mid_supported(a) ? kMid : kStream;
     return mode == NVFP4_MODE_W4A4 ? kTiled2 : kTiled16;
   }
   // Beyond 2^31-byte operands only the 64-bit-addressed tiled kernel runs
@@ -177,7 +190,7 @@ hipError_t run_gemm(int path, int mode, int epi, const nvfp4::GemmArgs& a, hipSt
     case kStream: return nvfp4::launch_stream_gemm(mode, epi, a, s);
     case kTiled2: return nvfp4::launch_tiled2_gemm(epi, a, s);
     case kTiled16: return nvfp4::launch_tiled16_gemm(epi, a, s);
-    case kMid: return nvfp4::launch_mid_gemm(epi, a, s);
+    case kMid: return nvfp4::launch_mid_gemm(mode, epi, a, s);
     default: return nvfp4::launch_tiled_gemm(mode, epi, a, s);
   }
 }
@@ -926,7 +939,7 @@ int nvfp4_grouped_gemm(int mode, const void* a, const uint8_t* a_scales, const v
     g.e_w = (int64_t)wbytes;
     g.e_out = (int64_t)(M * out_row);
   }
-  hipError_t err = mid         ? nvfp4::launch_mid_gemm(epi, g, sm)
+  hipError_t err = mid         ? nvfp4::launch_mid_gemm(mode, epi, g, sm)
                    : streaming ? nvfp4::launch_stream_gemm(mode, epi, g, sm)
                    : mode == NVFP4_MODE_W4A4 ? nvfp4::launch_tiled2_gemm(epi, g, sm)
                                              : nvfp4::launch_tiled16_gemm(epi, g, sm);

@@ -134,7 +134,7 @@ hipError_t launch_fp4_gemv(int epi, const GemmArgs& a, hipStream_t s);
 hipError_t launch_tiled_gemm(int mode, int epi, const GemmArgs& a, hipStream_t s);
 // mid.hip: the W4A4 mid-size kernel (unsplit, one expert).
 bool mid_supported(const GemmArgs& a);
-hipError_t launch_mid_gemm(int epi, const GemmArgs& a, hipStream_t s);
+hipError_t launch_mid_gemm(int mode, int epi, const GemmArgs& a, hipStream_t s);
 
 // The tiled kernels run one workgroup per CU, so output tiles go in rounds
 // of kTiledSlots; tiled_tail(units) is the tile count of the last, partial

@@ -1,20 +1,22 @@
-// mid.hip -- W4A4 GEMM for mid token counts (tens of tokens), with the
-// activation dequantized once per workgroup.
+// mid.hip -- GEMM for mid token counts (tens to hundreds of tokens), with
+// the activation brought into LDS once per workgroup.
 //
-// In the weight-streaming kernel every wave dequantizes the activation
-// fragments of its own K tiles for just the 16 or 32 weight rows of its
-// workgroup; at 64 tokens that is two thirds of its VALU. Here a workgroup
-// of 4 waves owns 128 weight rows (8 row groups; wave w: groups 2 w and
-// 2 w + 1, a gate/up pair for the SwiGLU epilogues) x 64 tokens, and all
-// its waves step through the K tiles together:
+// In the weight-streaming kernel every wave loads (and, for W4A4,
+// dequantizes) the activation fragments of its own K tiles for just the 16
+// or 32 weight rows of its workgroup; at 64 tokens that is two thirds of
+// its VALU (W4A4), or bf16 slices of more bytes than the weight (W4A16).
+// Here a workgroup of 4 waves owns 128 weight rows (8 row groups; wave w:
+// groups 2 w and 2 w + 1, a gate/up pair for the SwiGLU epilogues) x 64
+// tokens, and all its waves step through the K tiles together:
 //
 //  * each wave streams its own two weight tiles per K tile into registers
 //    (16-byte loads, one K tile ahead) and dequantizes them, as the
-//    streaming kernel does;
-//  * each wave also loads one of the 4 token groups' NVFP4 slice of the
-//    next K tile and writes it dequantized (exact f16) into an LDS image of
-//    the 64 tokens x 256 columns, double-buffered, so one barrier per K tile
-//    separates writing the next image from reading the current one;
+//    streaming kernel does (f16 for W4A4, bf16 for W4A16);
+//  * each wave also loads one of the 4 token groups' slice of the next K
+//    tile and writes it into an LDS image of the 64 tokens x 256 columns
+//    (W4A4: dequantized from NVFP4, exact f16; W4A16: the bf16 values as
+//    they are), double-buffered, so one barrier per K tile separates
+//    writing the next image from reading the current one;
 //  * the token fragments of every MFMA are read back from the image.
 //
 // Token rows past M lie past the end of the activation buffers and load as
@@ -27,17 +29,20 @@ namespace nvfp4 {
 
 constexpr int kMidWaves = 4;
 constexpr int kMidTG = 4;                   // token groups per workgroup
-constexpr int kMidRowBytes = 512;           // one token's 256 f16 columns
+constexpr int kMidRowBytes = 512;           // one token's 256 f16 or bf16 columns
 [[maybe_unused]] constexpr int kMidImg = kMidTG * 16 * kMidRowBytes;
 
 #if defined(__HIP_DEVICE_COMPILE__)
 namespace {
 
-// One K tile of one wave: its two weight tiles and its token group's slice.
+// One K tile of one wave: its two weight tiles and its token group's slice
+// (W4A4: 16 code bytes and 2 scale bytes per lane and half tile; W4A16: the
+// lane's four 16-byte chunks of bf16 per half tile).
+template <int MODE>
 struct MidLoad {
   u32x4 wc[2][2];
   uint32_t wsd[2];
-  u32x4 xc[2];
+  u32x4 xc[MODE == kW4A4 ? 2 : 8];
   uint32_t xs[2];
 };
 
@@ -48,7 +53,8 @@ struct MidLoad {
 // by the 16 lanes of equal l % 4, hits 16 distinct 16-byte slots.
 __device__ __forceinline__ int mid_key(int r) { return ((r >> 2) & 3) ^ ((r & 3) << 2); }
 
-__device__ __forceinline__ void mid_load(MidLoad& d, Rsrc w, Rsrc a, Rsrc s, const uint32_t (&gbase)[2],
+template <int MODE>
+__device__ __forceinline__ void mid_load(MidLoad<MODE>& d, Rsrc w, Rsrc a, Rsrc s, const uint32_t (&gbase)[2],
                                          uint32_t a_lane, uint32_t s_lane, int64_t t, int64_t T, int lane) {
   const bool in = t < T;
   const uint32_t tw = in ? (uint32_t)(t * kTileBytes) : kOutOfRange;
@@ -58,19 +64,37 @@ __device__ __forceinline__ void mid_load(MidLoad& d, Rsrc w, Rsrc a, Rsrc s, con
     d.wc[g][1] = bload16_nt(w, tw + 1024 + 16 * lane, gbase[g]);
     d.wsd[g] = bload4_nt(w, tw + kTileCodeBytes + 4 * lane, gbase[g]);
   }
-  const uint32_t ta = in ? a_lane + (uint32_t)(t * 128) : kOutOfRange;
-  const uint32_t ts = in ? s_lane + (uint32_t)(t * 16) : kOutOfRange;
-  d.xc[0] = bload16(a, ta);
-  d.xc[1] = bload16(a, ta + 64);
-  d.xs[0] = bload2(s, ts);
-  d.xs[1] = bload2(s, ts + 8);
+  if constexpr (MODE == kW4A4) {
+    const uint32_t ta = in ? a_lane + (uint32_t)(t * 128) : kOutOfRange;
+    const uint32_t ts = in ? s_lane + (uint32_t)(t * 16) : kOutOfRange;
+    d.xc[0] = bload16(a, ta);
+    d.xc[1] = bload16(a, ta + 64);
+    d.xs[0] = bload2(s, ts);
+    d.xs[1] = bload2(s, ts + 8);
+  } else {
+    // chunks 16 c + 4 q + u of the token row: bytes 256 c + 64 q + 16 u
+    const uint32_t ta = in ? a_lane + (uint32_t)(t * 512) : kOutOfRange;
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) d.xc[4 * c + u] = bload16(a, ta + 256 * c + 16 * u);
+  }
 }
 
 // This wave's token group (16 rows of the image) from the loaded slice.
-__device__ __forceinline__ void mid_put(uint8_t* img, const MidLoad& d, int wave, int lane) {
+template <int MODE>
+__device__ __forceinline__ void mid_put(uint8_t* img, const MidLoad<MODE>& d, int wave, int lane) {
   const int q = lane >> 4, tl = lane & 15;
   const int key = mid_key(tl);
   uint8_t* row = img + (16 * wave + tl) * kMidRowBytes;
+  if constexpr (MODE == kW4A16) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        *reinterpret_cast<u32x4*>(row + 256 * c + 16 * ((4 * q + u) ^ key)) = d.xc[4 * c + u];
+    return;
+  }
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     const f16x2 sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d.xs[c], 1.0f, false);  // blocks 8 c + 2 q, + 1
@@ -84,9 +108,37 @@ __device__ __forceinline__ void mid_put(uint8_t* img, const MidLoad& d, int wave
 
 // One K tile: the wave's two weight tiles dequantized in registers, the 4
 // token groups' fragments read from the image.
-__device__ __forceinline__ void mid_compute(f32x4 (&acc)[2][kMidTG], const MidLoad& d, const uint8_t* img, int lane) {
+template <int MODE>
+__device__ __forceinline__ void mid_compute(f32x4 (&acc)[2][kMidTG], const MidLoad<MODE>& d, const uint8_t* img,
+                                            int lane) {
   const int q = lane >> 4, tl = lane & 15;
   const int key = mid_key(tl);
+  if constexpr (MODE == kW4A16) {
+    float ws[2][4];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      ws[g][0] = e4m3_to_f32<0>(d.wsd[g]); ws[g][1] = e4m3_to_f32<1>(d.wsd[g]);
+      ws[g][2] = e4m3_to_f32<2>(d.wsd[g]); ws[g][3] = e4m3_to_f32<3>(d.wsd[g]);
+    }
+    const uint8_t* row = img + tl * kMidRowBytes;
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int sb = 2 * c + (u >> 1);
+        const int off = 256 * c + 16 * ((4 * q + u) ^ key);
+        bf16x8 B[kMidTG];
+#pragma unroll
+        for (int j = 0; j < kMidTG; ++j) B[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(row + j * 16 * kMidRowBytes + off));
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          const bf16x8 A = deq8_bf16(d.wc[g][c][u], ws[g][sb]);
+#pragma unroll
+          for (int j = 0; j < kMidTG; ++j) acc[g][j] = mfma16x16x32(A, B[j], acc[g][j]);
+        }
+      }
+    return;
+  }
   _Float16 ws[2][4];
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
@@ -124,7 +176,7 @@ __device__ __forceinline__ void mid_compute(f32x4 (&acc)[2][kMidTG], const MidLo
 // halves take alternate K tiles, adding their partial sums in LDS at the
 // end, measured slower: gate_up at 64 tokens, hidden 7168, 68.9 against
 // 67.2 us.)
-template <int EPI>
+template <int MODE, int EPI>
 __global__ __launch_bounds__(kMidWaves * 64, 2) void k_mid(GemmArgs args_in, int64_t m_tiles, int64_t tiles,
                                                            int64_t per_xcd) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -148,8 +200,8 @@ __global__ __launch_bounds__(kMidWaves * 64, 2) void k_mid(GemmArgs args_in, int
   if (tok0 >= M) return;
 
   const Rsrc w = make_rsrc(args.w, (uint32_t)(ngroups * T * kTileBytes));
-  const Rsrc a = make_rsrc(args.a, (uint32_t)(M * (K / 2)));
-  const Rsrc s = make_rsrc(args.a_scales, (uint32_t)(M * (K / 16)));
+  const Rsrc a = make_rsrc(args.a, (uint32_t)(M * (MODE == kW4A4 ? K / 2 : K * 2)));
+  const Rsrc s = MODE == kW4A4 ? make_rsrc(args.a_scales, (uint32_t)(M * (K / 16))) : a;
   uint32_t gbase[2];
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
@@ -159,7 +211,7 @@ __global__ __launch_bounds__(kMidWaves * 64, 2) void k_mid(GemmArgs args_in, int
   // This wave's token group of the image: rows tok0 + 16 wave + l % 16 (past
   // M: out of range, zeros).
   const int64_t trow = tok0 + 16 * wave + tl;
-  const uint32_t a_lane = (uint32_t)(trow * (K / 2) + 16 * q);
+  const uint32_t a_lane = MODE == kW4A4 ? (uint32_t)(trow * (K / 2) + 16 * q) : (uint32_t)(trow * K * 2 + 64 * q);
   const uint32_t s_lane = (uint32_t)(trow * (K / 16) + 2 * q);
   const float alpha = uniform_now(args.alpha);
   const float g2i = EPI == kSwigluNvfp4 ? uniform_now(args.g2_inv) : 0.0f;
@@ -175,7 +227,7 @@ __global__ __launch_bounds__(kMidWaves * 64, 2) void k_mid(GemmArgs args_in, int
   // t arithmetic is issued; the barrier then publishes it (and frees image
   // t % 2 for K tile t + 2). (Loads two K tiles ahead, in three register
   // sets, measured slower: 242 against 176 VGPRs.)
-  MidLoad cur, nxt;
+  MidLoad<MODE> cur, nxt;
   mid_load(cur, w, a, s, gbase, a_lane, s_lane, 0, T, lane);
   mid_load(nxt, w, a, s, gbase, a_lane, s_lane, 1, T, lane);
   mid_put(img[0], cur, wave, lane);
@@ -196,7 +248,7 @@ __global__ __launch_bounds__(kMidWaves * 64, 2) void k_mid(GemmArgs args_in, int
     const float at = row_alpha(alpha, args.row_scale, tv, token);
     if constexpr (EpiTraits<EPI>::swiglu) {
       store_swiglu<EPI>(acc[0][j], acc[1][j], at, g2i, tv && rg < ngroups, token, (rg >> 1) * kTileRows, lane,
-                        N / 2, args.out, args.out_scales);
+                        N / 2, args.out, args.out_scales, args.h_prescale);
     } else {
 #pragma unroll
       for (int g = 0; g < 2; ++g)
@@ -206,33 +258,38 @@ __global__ __launch_bounds__(kMidWaves * 64, 2) void k_mid(GemmArgs args_in, int
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-template <int EPI>
+template <int MODE, int EPI>
 static hipError_t mid_launch(const GemmArgs& a, hipStream_t s) {
   const int64_t m_tiles = (a.M + 16 * kMidTG - 1) / (16 * kMidTG);
   const int64_t tiles = (a.N / kTileRows + 7) / 8 * m_tiles;
   const int64_t per_xcd = (tiles + 7) / 8;
   const unsigned ex = a.experts > 1 ? (unsigned)a.experts : 1u;
-  k_mid<EPI><<<dim3((unsigned)(8 * per_xcd), ex), kMidWaves * 64, 0, s>>>(a, m_tiles, tiles, per_xcd);
+  k_mid<MODE, EPI><<<dim3((unsigned)(8 * per_xcd), ex), kMidWaves * 64, 0, s>>>(a, m_tiles, tiles, per_xcd);
   return hipGetLastError();
 }
 
 bool mid_supported(const GemmArgs& a) { return a.ksplit == 1; }
 
-// W4A4 only, unsplit; several experts (grid y, dense epilogues, each
-// expert's valid rows from masked_m) or one. Needs each expert's packed
-// weight and activation rows below 2^31 bytes (32-bit buffer offsets); the
-// caller checks.
-hipError_t launch_mid_gemm(int epi, const GemmArgs& a, hipStream_t s) {
-  if (a.M == 0) return hipSuccess;
-  if (!mid_supported(a)) return hipErrorInvalidValue;
+template <int MODE>
+static hipError_t mid_launch_m(int epi, const GemmArgs& a, hipStream_t s) {
   switch (epi) {
-    case kOutF32: return mid_launch<kOutF32>(a, s);
-    case kOutBF16: return mid_launch<kOutBF16>(a, s);
-    case kSwigluNvfp4: return mid_launch<kSwigluNvfp4>(a, s);
-    case kSwigluBF16: return mid_launch<kSwigluBF16>(a, s);
-    case kSwigluF32: return mid_launch<kSwigluF32>(a, s);
+    case kOutF32: return mid_launch<MODE, kOutF32>(a, s);
+    case kOutBF16: return mid_launch<MODE, kOutBF16>(a, s);
+    case kSwigluNvfp4: return mid_launch<MODE, kSwigluNvfp4>(a, s);
+    case kSwigluBF16: return mid_launch<MODE, kSwigluBF16>(a, s);
+    case kSwigluF32: return mid_launch<MODE, kSwigluF32>(a, s);
   }
   return hipErrorInvalidValue;
+}
+
+// Unsplit; several experts (grid y, dense epilogues, each expert's valid
+// rows from masked_m) or one. Needs each expert's packed weight and
+// activation rows below 2^31 bytes (32-bit buffer offsets); the caller
+// checks.
+hipError_t launch_mid_gemm(int mode, int epi, const GemmArgs& a, hipStream_t s) {
+  if (a.M == 0) return hipSuccess;
+  if (!mid_supported(a)) return hipErrorInvalidValue;
+  return mode == kW4A4 ? mid_launch_m<kW4A4>(epi, a, s) : mid_launch_m<kW4A16>(epi, a, s);
 }
 
 }  // namespace nvfp4

@@ -358,11 +358,12 @@ def test_mlp_tiny_workload(path, mode):
     _check_mlp(mode, 4, 256, 512)
 
 
-@pytest.mark.parametrize("M", [1, 7, 24, 48, 56, 63, 64, 100, 128, 144, 200, 512, 513])
+@pytest.mark.parametrize("M", [1, 7, 24, 32, 33, 48, 56, 63, 64, 100, 128, 129, 144, 192, 193, 200, 512, 513])
 def test_mlp_auto_dispatch(M):
     """Token counts on both sides of each automatic switch: W4A16 streams up
-    to 48 tokens, W4A4 up to 128 (its gate_up from 64 to 512 tokens on the
-    mid-size kernel); the tiled kernels take over above."""
+    to 48 tokens (its gate_up from 33 to 64 tokens on the mid-size kernel),
+    W4A4 up to 128 (its gate_up from 64 to 512 tokens
+    on the mid-size kernel); the tiled kernels take over above."""
     nv.set_path(nv.PATH_AUTO)
     _check_mlp("w4a4", M, 512, 768, seed=M)
     _check_mlp("w4a16", M, 512, 768, seed=M)
