@@ -80,17 +80,16 @@ extern "C" {
 #define NVFP4_PATH_AUTO 0    /* choose by M */
 #define NVFP4_PATH_GEMV 1    /* decode GEMV sized for M <= 2: W4A4 on the FP4 matrix core with the
                                 blocks kept apart, W4A16 on the vector ALU (any M) */
-#define NVFP4_PATH_STREAM 2  /* weight-streaming MFMA kernel (any M; chosen for W4A4 M <= 128 except
-                                the SwiGLU GEMMs of 64 tokens and more, W4A16 M <= 48 except the
-                                SwiGLU GEMMs of 33 tokens and more) */
+#define NVFP4_PATH_STREAM 2  /* weight-streaming MFMA kernel (any M; chosen for W4A4 M <= 128 and
+                                W4A16 M <= 48, except the SwiGLU GEMMs of 33 tokens and more) */
 #define NVFP4_PATH_TILED 3   /* LDS-tiled MFMA GEMM (any M) */
 #define NVFP4_PATH_TILED64 4 /* the tiled GEMM with 64-bit addressing, which AUTO and the other
                                 paths run only for operands of 2^31 bytes or more (any M; no
                                 split-K; the grouped GEMM treats it as NVFP4_PATH_TILED) */
-#define NVFP4_PATH_MID 5     /* 128 weight rows x 64 tokens per workgroup, the activation
-                                brought into LDS once per workgroup (any M; chosen for the
-                                W4A4 SwiGLU GEMMs of 64 to 512 tokens, the W4A16 SwiGLU GEMMs
-                                of 33 to 64 tokens and the W4A4 grouped GEMMs
+#define NVFP4_PATH_MID 5     /* 128 weight rows x 48 (M <= 48) or 64 tokens per workgroup, the
+                                activation brought into LDS once per workgroup (any M; chosen
+                                for the W4A4 SwiGLU GEMMs of 33 to 512 tokens, the W4A16 SwiGLU
+                                GEMMs of 33 to 64 tokens and the W4A4 grouped GEMMs
                                 of 64 to 512 tokens per expert; the W4A16 grouped GEMM runs
                                 NVFP4_PATH_STREAM under it) */
 

@@ -120,22 +120,25 @@ constexpr int64_t kGroupedMidMinM = 64, kGroupedMidMaxM = 512;
 // the MLP) runs the mid-size kernel under the automatic path. Gate_up alone
 // (hidden 7168 / 5120): 64 tokens 78.9 / 61.0 us streaming against 69.0 /
 // 51.8; 128: 138.0 / 103.6 against 106.9 / 78.3; 256: 183.1 / 135.0 tiled
-// against 161.5 / 121.1; below 64 tokens streaming wins (48: 62.8 / 47.9
-// against 66.6 / 49.0). Whole forward, tiled gate_up (with its K-split tail)
+// against 161.5 / 121.1; up to 48 tokens the 48-token tile: 40 / 48 tokens
+// 56.5 / 62.1 and 42.3 / 46.6 streaming against 52.2 / 53.2 and 39.4 /
+// 40.2, a tie at 33 (51.9 / 39.0 against 51.6 / 39.2) and streaming ahead
+// at 32 (41.9 / 32.2 against 51.3 / 38.6). Whole forward, tiled gate_up (with its K-split tail)
 // against mid-size: 384 tokens 439.4 / 345.4 against 374.7 / 276.4 us, 512:
 // 463.7 / 362.9 against 441.9 / 322.9; 768: 608.7 / 442.7 against 633.9 /
 // 443.3, and the tiled kernel wins above. Dense GEMMs (the down projection,
 // 5120 / 7168 rows: 40 / 56 mid-size workgroups per 64 tokens) keep the
 // streaming and tiled kernels, whose split-K fills the CUs.
-constexpr int64_t kMidMinM = 64, kMidMaxM = 512;
+constexpr int64_t kMidMinM = 33, kMidMaxM = 512;
 
 // W4A16 SwiGLU GEMMs take the mid-size kernel from 33 to 64 tokens, where
-// its 64-token tile beats the streaming kernel and the 128-token tiled one.
-// Gate_up alone, hidden 5120: 33 / 40 / 64 tokens 62.7 / 64.9 / 64.8 us
-// (streaming up to 48, then tiled) against 56.7 / 58.0 / 61.0; whole
-// forward at 40 / 48 / 64 tokens 96.2 / 98.9 / 121.6 against 88.4 / 89.6 /
-// 118.3 us. It loses at 32 (50.0 against 56.5) and from 65 to 128 (65.9
-// against 96.6 at 128: one tiled token tile). From 129 to 192 tokens it
+// its 48- and 64-token tiles beat the streaming kernel and the 128-token
+// tiled one. Gate_up alone, hidden 5120: 33 / 40 / 48 / 64 tokens 62.7 /
+// 64.9 / 67.3 / 64.8 us (streaming up to 48, then tiled) against 50.5 /
+// 51.6 / 54.0 / 61.1; whole forward at 40 / 48 / 64 tokens 96.2 / 98.9 /
+// 121.6 against 83.4 / 85.0 / 118.6 us. It loses at 32 (50.0 against
+// 56.5 with the 64-token tile) and from 65 to 128 (65.9 against 96.6 at
+// 128: one tiled token tile). From 129 to 192 tokens it
 // beats the tiled gate_up alone (113.8 against 128.9 at 192) but not the
 // forward's, whose tail tiles are K-split (184.9 against 168.7 us).
 bool mid_w4a16(int64_t M) { return M >= 33 && M <= 64; }

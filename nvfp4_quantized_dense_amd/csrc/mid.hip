@@ -28,9 +28,7 @@
 namespace nvfp4 {
 
 constexpr int kMidWaves = 4;
-constexpr int kMidTG = 4;                   // token groups per workgroup
 constexpr int kMidRowBytes = 512;           // one token's 256 f16 or bf16 columns
-[[maybe_unused]] constexpr int kMidImg = kMidTG * 16 * kMidRowBytes;
 
 #if defined(__HIP_DEVICE_COMPILE__)
 namespace {
@@ -108,8 +106,8 @@ __device__ __forceinline__ void mid_put(uint8_t* img, const MidLoad<MODE>& d, in
 
 // One K tile: the wave's two weight tiles dequantized in registers, the 4
 // token groups' fragments read from the image.
-template <int MODE>
-__device__ __forceinline__ void mid_compute(f32x4 (&acc)[2][kMidTG], const MidLoad<MODE>& d, const uint8_t* img,
+template <int MODE, int TG>
+__device__ __forceinline__ void mid_compute(f32x4 (&acc)[2][TG], const MidLoad<MODE>& d, const uint8_t* img,
                                             int lane) {
   const int q = lane >> 4, tl = lane & 15;
   const int key = mid_key(tl);
@@ -127,14 +125,14 @@ __device__ __forceinline__ void mid_compute(f32x4 (&acc)[2][kMidTG], const MidLo
       for (int u = 0; u < 4; ++u) {
         const int sb = 2 * c + (u >> 1);
         const int off = 256 * c + 16 * ((4 * q + u) ^ key);
-        bf16x8 B[kMidTG];
+        bf16x8 B[TG];
 #pragma unroll
-        for (int j = 0; j < kMidTG; ++j) B[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(row + j * 16 * kMidRowBytes + off));
+        for (int j = 0; j < TG; ++j) B[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(row + j * 16 * kMidRowBytes + off));
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
           const bf16x8 A = deq8_bf16(d.wc[g][c][u], ws[g][sb]);
 #pragma unroll
-          for (int j = 0; j < kMidTG; ++j) acc[g][j] = mfma16x16x32(A, B[j], acc[g][j]);
+          for (int j = 0; j < TG; ++j) acc[g][j] = mfma16x16x32(A, B[j], acc[g][j]);
         }
       }
     return;
@@ -153,14 +151,14 @@ __device__ __forceinline__ void mid_compute(f32x4 (&acc)[2][kMidTG], const MidLo
     for (int u = 0; u < 4; ++u) {
       const int sb = 2 * c + (u >> 1);
       const int off = 256 * c + 16 * ((4 * q + u) ^ key);
-      f16x8 B[kMidTG];
+      f16x8 B[TG];
 #pragma unroll
-      for (int j = 0; j < kMidTG; ++j) B[j] = *reinterpret_cast<const f16x8*>(row + j * 16 * kMidRowBytes + off);
+      for (int j = 0; j < TG; ++j) B[j] = *reinterpret_cast<const f16x8*>(row + j * 16 * kMidRowBytes + off);
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
         const f16x8 A = deq8_f16(d.wc[g][c][u], ws[g][sb]);
 #pragma unroll
-        for (int j = 0; j < kMidTG; ++j) acc[g][j] = mfma16x16x32(A, B[j], acc[g][j]);
+        for (int j = 0; j < TG; ++j) acc[g][j] = mfma16x16x32(A, B[j], acc[g][j]);
       }
     }
 }
@@ -176,11 +174,11 @@ __device__ __forceinline__ void mid_compute(f32x4 (&acc)[2][kMidTG], const MidLo
 // halves take alternate K tiles, adding their partial sums in LDS at the
 // end, measured slower: gate_up at 64 tokens, hidden 7168, 68.9 against
 // 67.2 us.)
-template <int MODE, int EPI>
+template <int MODE, int EPI, int TG>
 __global__ __launch_bounds__(kMidWaves * 64, 2) void k_mid(GemmArgs args_in, int64_t m_tiles, int64_t tiles,
                                                            int64_t per_xcd) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __shared__ __attribute__((aligned(16))) uint8_t img[2][kMidImg];
+  __shared__ __attribute__((aligned(16))) uint8_t img[2][TG * 16 * kMidRowBytes];
   GemmArgs args = args_in;
   clear_words(args.zero_ptr, args.zero_n);
   const int64_t id = blockIdx.x;
@@ -196,7 +194,7 @@ __global__ __launch_bounds__(kMidWaves * 64, 2) void k_mid(GemmArgs args_in, int
   const int64_t M = valid_rows(args), N = args.N, K = args.K, T = K / kTileK;
   const int64_t ngroups = N / kTileRows;
   const int64_t rg = n_tile * 8 + 2 * wave;  // this wave's first row group
-  const int64_t tok0 = m_tile * 16 * kMidTG;
+  const int64_t tok0 = m_tile * 16 * TG;
   if (tok0 >= M) return;
 
   const Rsrc w = make_rsrc(args.w, (uint32_t)(ngroups * T * kTileBytes));
@@ -209,18 +207,21 @@ __global__ __launch_bounds__(kMidWaves * 64, 2) void k_mid(GemmArgs args_in, int
     gbase[g] = __builtin_amdgcn_readfirstlane((uint32_t)(grp * T * kTileBytes));
   }
   // This wave's token group of the image: rows tok0 + 16 wave + l % 16 (past
-  // M: out of range, zeros).
+  // M: out of range, zeros). With fewer token groups than waves the other
+  // waves load no slice (out of range) and put none.
   const int64_t trow = tok0 + 16 * wave + tl;
-  const uint32_t a_lane = MODE == kW4A4 ? (uint32_t)(trow * (K / 2) + 16 * q) : (uint32_t)(trow * K * 2 + 64 * q);
-  const uint32_t s_lane = (uint32_t)(trow * (K / 16) + 2 * q);
+  const bool puts = wave < TG;
+  const uint32_t a_lane = !puts ? kOutOfRange
+                          : MODE == kW4A4 ? (uint32_t)(trow * (K / 2) + 16 * q) : (uint32_t)(trow * K * 2 + 64 * q);
+  const uint32_t s_lane = puts ? (uint32_t)(trow * (K / 16) + 2 * q) : kOutOfRange;
   const float alpha = uniform_now(args.alpha);
   const float g2i = EPI == kSwigluNvfp4 ? uniform_now(args.g2_inv) : 0.0f;
 
-  f32x4 acc[2][kMidTG];
+  f32x4 acc[2][TG];
 #pragma unroll
   for (int g = 0; g < 2; ++g)
 #pragma unroll
-    for (int j = 0; j < kMidTG; ++j) acc[g][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < TG; ++j) acc[g][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // K tile t is multiplied from cur (weights) and image t % 2; nxt holds
   // K tile t + 1, whose token slice goes into the other image once the tile
@@ -230,19 +231,19 @@ __global__ __launch_bounds__(kMidWaves * 64, 2) void k_mid(GemmArgs args_in, int
   MidLoad<MODE> cur, nxt;
   mid_load(cur, w, a, s, gbase, a_lane, s_lane, 0, T, lane);
   mid_load(nxt, w, a, s, gbase, a_lane, s_lane, 1, T, lane);
-  mid_put(img[0], cur, wave, lane);
+  if (puts) mid_put(img[0], cur, wave, lane);
   __syncthreads();
   for (int64_t t = 0; t < T; ++t) {
     const int b = (int)(t & 1);
-    mid_compute(acc, cur, img[b], lane);
-    if (t + 1 < T) mid_put(img[b ^ 1], nxt, wave, lane);
+    mid_compute<MODE, TG>(acc, cur, img[b], lane);
+    if (puts && t + 1 < T) mid_put(img[b ^ 1], nxt, wave, lane);
     cur = nxt;
     mid_load(nxt, w, a, s, gbase, a_lane, s_lane, t + 2, T, lane);
     __syncthreads();
   }
 
 #pragma unroll
-  for (int j = 0; j < kMidTG; ++j) {
+  for (int j = 0; j < TG; ++j) {
     const int64_t token = tok0 + 16 * j + tl;
     const bool tv = token < M;
     const float at = row_alpha(alpha, args.row_scale, tv, token);
@@ -258,14 +259,20 @@ __global__ __launch_bounds__(kMidWaves * 64, 2) void k_mid(GemmArgs args_in, int
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
-template <int MODE, int EPI>
-static hipError_t mid_launch(const GemmArgs& a, hipStream_t s) {
-  const int64_t m_tiles = (a.M + 16 * kMidTG - 1) / (16 * kMidTG);
+template <int MODE, int EPI, int TG>
+static hipError_t mid_launch_tg(const GemmArgs& a, hipStream_t s) {
+  const int64_t m_tiles = (a.M + 16 * TG - 1) / (16 * TG);
   const int64_t tiles = (a.N / kTileRows + 7) / 8 * m_tiles;
   const int64_t per_xcd = (tiles + 7) / 8;
   const unsigned ex = a.experts > 1 ? (unsigned)a.experts : 1u;
-  k_mid<MODE, EPI><<<dim3((unsigned)(8 * per_xcd), ex), kMidWaves * 64, 0, s>>>(a, m_tiles, tiles, per_xcd);
+  k_mid<MODE, EPI, TG><<<dim3((unsigned)(8 * per_xcd), ex), kMidWaves * 64, 0, s>>>(a, m_tiles, tiles, per_xcd);
   return hipGetLastError();
+}
+
+// Token tiles of 48 up to 48 tokens, else of 64.
+template <int MODE, int EPI>
+static hipError_t mid_launch(const GemmArgs& a, hipStream_t s) {
+  return a.M <= 48 ? mid_launch_tg<MODE, EPI, 3>(a, s) : mid_launch_tg<MODE, EPI, 4>(a, s);
 }
 
 bool mid_supported(const GemmArgs& a) { return a.ksplit == 1; }

@@ -361,9 +361,10 @@ def test_mlp_tiny_workload(path, mode):
 @pytest.mark.parametrize("M", [1, 7, 24, 32, 33, 48, 56, 63, 64, 100, 128, 129, 144, 192, 193, 200, 512, 513])
 def test_mlp_auto_dispatch(M):
     """Token counts on both sides of each automatic switch: W4A16 streams up
-    to 48 tokens (its gate_up from 33 to 64 tokens on the mid-size kernel),
-    W4A4 up to 128 (its gate_up from 64 to 512 tokens
-    on the mid-size kernel); the tiled kernels take over above."""
+    to 48 tokens, W4A4 up to 128, the gate_up from 33 tokens on the
+    mid-size kernel (48-token tiles up to 48 tokens, 64-token tiles above;
+    W4A16 up to 64 tokens, W4A4 up to 512); the tiled kernels take over
+    above."""
     nv.set_path(nv.PATH_AUTO)
     _check_mlp("w4a4", M, 512, 768, seed=M)
     _check_mlp("w4a16", M, 512, 768, seed=M)
