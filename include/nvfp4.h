@@ -86,12 +86,12 @@ extern "C" {
 #define NVFP4_PATH_TILED64 4 /* the tiled GEMM with 64-bit addressing, which AUTO and the other
                                 paths run only for operands of 2^31 bytes or more (any M; no
                                 split-K; the grouped GEMM treats it as NVFP4_PATH_TILED) */
-#define NVFP4_PATH_MID 5     /* 128 weight rows x 48 (M <= 48) or 64 tokens per workgroup, the
-                                activation brought into LDS once per workgroup (any M; chosen
-                                for the W4A4 SwiGLU GEMMs of 33 to 512 tokens, the W4A16 SwiGLU
-                                GEMMs of 33 to 64 tokens and the W4A4 grouped GEMMs
-                                of 64 to 512 tokens per expert; the W4A16 grouped GEMM runs
-                                NVFP4_PATH_STREAM under it) */
+#define NVFP4_PATH_MID 5     /* 128 weight rows x 48 or 64 tokens per workgroup (whichever pads M
+                                less; 48 on a tie), the activation brought into LDS once per
+                                workgroup (any M; chosen for the W4A4 SwiGLU GEMMs of 33 to 512
+                                tokens, the W4A16 SwiGLU GEMMs of 33 to 64 tokens and the W4A4
+                                grouped GEMMs of 64 to 512 tokens per expert; the W4A16 grouped
+                                GEMM runs NVFP4_PATH_STREAM under it) */
 
 /* Message of the last failed call on this thread ("" if none). */
 const char* nvfp4_last_error(void);

@@ -269,10 +269,15 @@ static hipError_t mid_launch_tg(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Token tiles of 48 up to 48 tokens, else of 64.
+// Token tiles of 48 where they pad M no more than tiles of 64 do (48-token
+// workgroups also fit three to a CU against two): W4A4 gate_up at 96 / 144 /
+// 192 tokens, hidden 7168, 97.0 / 119.9 / 121.8 us with 64-token tiles
+// against 71.2 / 98.1 / 113.9; at 64 / 256 / 512 tokens the 64-token tiles
+// win (64.4 / 152.0 / 274.4 against 71.0 / 163.2 / 293.0 us).
 template <int MODE, int EPI>
 static hipError_t mid_launch(const GemmArgs& a, hipStream_t s) {
-  return a.M <= 48 ? mid_launch_tg<MODE, EPI, 3>(a, s) : mid_launch_tg<MODE, EPI, 4>(a, s);
+  const int64_t pad48 = (a.M + 47) / 48 * 48, pad64 = (a.M + 63) / 64 * 64;
+  return pad48 <= pad64 ? mid_launch_tg<MODE, EPI, 3>(a, s) : mid_launch_tg<MODE, EPI, 4>(a, s);
 }
 
 bool mid_supported(const GemmArgs& a) { return a.ksplit == 1; }
