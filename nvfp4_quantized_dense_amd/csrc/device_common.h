@@ -38,14 +38,14 @@ struct EpiTraits {
 // mantissa to 3 bits with the carry running into the exponent; below 2^-6 the
 // quantum is 2^-9, so rint(v * 512) is the subnormal mantissa (8 = 2^-6 is
 // byte 0x08 as well). Values at or above 448 saturate to 0x7E.
+// Both roundings are computed and the right one selected (no branch: the
+// lanes of a wave hold different blocks).
 __device__ __forceinline__ uint32_t e4m3_from_f32(float v) {
-  uint32_t u = __float_as_uint(v) & 0x7FFFFFFFu;
-  if (u >= 0x43E00000u) return 0x7Eu;  // >= 448
-  if (u < 0x3C800000u) {               // < 2^-6
-    return (uint32_t)__builtin_rintf(__uint_as_float(u) * 512.0f);
-  }
-  u += 0x7FFFFu + ((u >> 20) & 1u);
-  return (((u >> 23) - 120u) << 3) | ((u >> 20) & 7u);
+  const uint32_t u = __float_as_uint(v) & 0x7FFFFFFFu;
+  const uint32_t sub = (uint32_t)__builtin_rintf(__uint_as_float(u) * 512.0f);  // < 2^-6
+  const uint32_t un = u + 0x7FFFFu + ((u >> 20) & 1u);
+  const uint32_t nrm = (((un >> 23) - 120u) << 3) | ((un >> 20) & 7u);
+  return u >= 0x43E00000u ? 0x7Eu : (u < 0x3C800000u ? sub : nrm);  // >= 448 saturates
 }
 
 // E4M3FN byte (selected byte of a dword) -> fp32, hardware OCP decode.
@@ -91,8 +91,18 @@ struct BlockScale {
   uint32_t byte;
   float r;
 };
+// x / 6 as RN(x * y) corrected by one fused multiply-add of its remainder,
+// y = RN(1/6): the correctly rounded quotient for every fp32 x >= 2^-125
+// (checked over every such input); below that both are under 2^-120 and
+// encode to the E4M3 byte 0, so the scale byte is the one x / 6 gives.
+__device__ __forceinline__ float div6(float x) {
+  const float y = 0x1.555556p-3f;
+  const float q0 = x * y;
+  return __builtin_fmaf(__builtin_fmaf(-q0, 6.0f, x), y, q0);
+}
+
 __device__ __forceinline__ BlockScale block_scale(float amax, float g_inv) {
-  float sv = (amax * g_inv) / 6.0f;
+  float sv = div6(amax * g_inv);
   BlockScale b;
   b.byte = e4m3_from_f32(sv);
   float s = __builtin_amdgcn_cvt_f32_fp8((int)b.byte, 0);
@@ -359,6 +369,18 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
   return s * u;
 }
 
+// max(v, v of lane l ^ 16) and max(v, v of lane l ^ 32) on the VALU (no LDS
+// round trip): a permlane swap of v with itself leaves v and its partner's v
+// in the two results, in either order depending on the lane.
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __builtin_fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __builtin_fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+
 // SwiGLU of matching gate/up tiles re-quantized to NVFP4. Lane l holds
 // outputs j0 + 4(l/16) + r of token l % 16 (j0 a multiple of 16), so the 64
 // lanes of the wave hold whole 16-element blocks of h, one per token column.
@@ -376,8 +398,8 @@ __device__ __forceinline__ SwigluBlock swiglu_nvfp4(const f32x4& gate, const f32
   for (int r = 0; r < 4; ++r) h[r] = silu_mul(alpha * gate[r], alpha * up[r]);
   float amax = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(h[0]), __builtin_fabsf(h[1])),
                                __builtin_fmaxf(__builtin_fabsf(h[2]), __builtin_fabsf(h[3])));
-  amax = __builtin_fmaxf(amax, __shfl_xor(amax, 16));
-  amax = __builtin_fmaxf(amax, __shfl_xor(amax, 32));
+  amax = max_xor16(amax);
+  amax = max_xor32(amax);
   BlockScale bs = block_scale(amax, g2_inv);
   SwigluBlock b;
   b.codes = e2m1_pack4(h[0] * bs.r, h[1] * bs.r, h[2] * bs.r, h[3] * bs.r);
