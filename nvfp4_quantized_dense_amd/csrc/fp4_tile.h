@@ -35,7 +35,6 @@ namespace nvfp4 {
 
 #if defined(__HIP_DEVICE_COMPILE__)
 
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 // C + A * B over 128 E2M1 codes per row and column (unit E8M0 scales).
