@@ -80,8 +80,10 @@ extern "C" {
 #define NVFP4_PATH_AUTO 0    /* choose by M */
 #define NVFP4_PATH_GEMV 1    /* decode GEMV sized for M <= 2: W4A4 on the FP4 matrix core with the
                                 blocks kept apart, W4A16 on the vector ALU (any M) */
-#define NVFP4_PATH_STREAM 2  /* weight-streaming MFMA kernel (any M; chosen for W4A4 M <= 128 and
-                                W4A16 M <= 48, except the SwiGLU GEMMs of 33 tokens and more) */
+#define NVFP4_PATH_STREAM 2  /* weight-streaming MFMA kernel (any M; chosen for W4A4 M <= 128,
+                                W4A16 SwiGLU GEMMs M <= 32 and W4A16 dense GEMMs M <= 96, except
+                                the W4A4 SwiGLU GEMMs of 33 tokens and more and the down
+                                projections of mlp_forward that run NVFP4_PATH_MID) */
 #define NVFP4_PATH_TILED 3   /* LDS-tiled MFMA GEMM (any M) */
 #define NVFP4_PATH_TILED64 4 /* the tiled GEMM with 64-bit addressing, which AUTO and the other
                                 paths run only for operands of 2^31 bytes or more (any M; no
@@ -89,9 +91,12 @@ extern "C" {
 #define NVFP4_PATH_MID 5     /* 128 weight rows x 48 or 64 tokens per workgroup (whichever pads M
                                 less; 48 on a tie), the activation brought into LDS once per
                                 workgroup (any M; chosen for the W4A4 SwiGLU GEMMs of 33 to 512
-                                tokens, the W4A16 SwiGLU GEMMs of 33 to 64 tokens and the W4A4
-                                grouped GEMMs of 64 to 512 tokens per expert; the W4A16 grouped
-                                GEMM runs NVFP4_PATH_STREAM under it) */
+                                tokens, the W4A16 SwiGLU GEMMs of 33 to 64 tokens, the W4A4
+                                grouped GEMMs of 64 to 512 tokens per expert, and mlp_forward's
+                                down projection (W4A4 from 17 tokens, W4A16 from 65 to 192)
+                                wherever its grid has at most 256 output tiles and K splits into
+                                two or more parts of 8 K tiles, split over the workspace; the
+                                W4A16 grouped GEMM runs NVFP4_PATH_STREAM under it) */
 
 /* Message of the last failed call on this thread ("" if none). */
 const char* nvfp4_last_error(void);

@@ -109,7 +109,7 @@ size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 // 5120, a tie at 7168) and loses from 144 (349 against 279 us); W4A16
 // streaming wins up to 48 (117 against 122 us) and loses at 56 (148 against
 // 124 us) to the 128-token tiled kernel.
-int64_t stream_max_m(int mode) { return mode == NVFP4_MODE_W4A4 ? 128 : 48; }
+int64_t stream_max_m(int mode, bool swiglu) { return mode == NVFP4_MODE_W4A4 ? 128 : swiglu ? 48 : 96; }
 
 // Largest tokens per expert a grouped GEMM runs as one streaming launch
 // over all experts under the automatic path.
@@ -154,8 +154,36 @@ int choose_path(int mode, int64_t M, bool swiglu) {
   if (M <= (mode == NVFP4_MODE_W4A4 ? 2 : 1)) return NVFP4_PATH_GEMV;
   if (mode == NVFP4_MODE_W4A4 && swiglu && M >= kMidMinM && M <= kMidMaxM) return NVFP4_PATH_MID;
   if (mode != NVFP4_MODE_W4A4 && swiglu && mid_w4a16(M)) return NVFP4_PATH_MID;
-  if (M <= stream_max_m(mode)) return NVFP4_PATH_STREAM;
+  if (M <= stream_max_m(mode, swiglu)) return NVFP4_PATH_STREAM;
   return NVFP4_PATH_TILED;
+}
+
+// K splits of a dense GEMM on the mid-size kernel: as many as bring the grid
+// to about two workgroups per CU (its occupancy at 64-token tiles), at most
+// 8, every split non-empty and at least 8 K tiles long.
+int64_t mid_ways(int64_t M, int64_t N, int64_t K) {
+  const int64_t units = nvfp4::mid_shape(M, N).units, T = K / 256;
+  int64_t ks = std::min<int64_t>(2 * nvfp4::kTiledSlots / std::max<int64_t>(units, 1), 8);
+  while (ks > 1 && ((ks - 1) * ((T + ks - 1) / ks) >= T || (T + ks - 1) / ks < 8)) --ks;
+  return std::max<int64_t>(ks, 1);
+}
+
+// Path of mlp_forward's down projection (a dense GEMM that can split K
+// through the workspace): the mid-size kernel wherever it K-splits (at
+// most 256 output tiles of 128 rows x 48 or 64 tokens), W4A4 from 17
+// tokens and W4A16 from 65 to 192, else as choose_path. The W4A4 forward
+// at hidden 7168 / 5120 (same box, same run): 17 tokens 69.1 / 57.7 -> 67.3
+// / 56.4 us, 64: 109.4 / 90.1 -> 102.6 / 83.8, 96: 144.2 -> 118.6 (7168),
+// 128: 179.0 / 148.3 -> 153.6 / 114.9, 256: 258.7 / 213.8 -> 246.8 / 177.3,
+// 320: 246.1 -> 216.5 (5120); unsplit it lost at 320 (7168), 384 (5120),
+// 448 and 512 (both). W4A16, hidden 5120: 80 / 96 / 128 / 192 tokens
+// 119.9 / 121.3 / 125.9 / 169.4 -> 105.2 / 106.4 / 113.5 / 164.1 us; at
+// 49-64 tokens the streaming kernel's one-round grid wins (95.2 against
+// 98.4 us at 49), at 256-320 the tiled kernel (174.2 against 177.2 at 256).
+int choose_path_down(int mode, int64_t M, int64_t H, int64_t I) {
+  const bool mid = mode == NVFP4_MODE_W4A4 ? M >= 17 : (M >= 65 && M <= 192);
+  if (g_path == NVFP4_PATH_AUTO && mid && mid_ways(M, H, I) > 1) return NVFP4_PATH_MID;
+  return choose_path(mode, M, false);
 }
 
 // Kernels that address their operands with 32-bit buffer offsets: the packed
@@ -276,6 +304,19 @@ SplitPlan split_plan(Kernel k, int mode, int64_t M, int64_t N, int64_t K, bool s
     if (p.ways > 1) {
       p.units = ts.units;
       p.part_bytes = align256((size_t)(ts.units * p.ways * ts.tile_floats) * sizeof(float));
+      p.counter_bytes = align256((size_t)ts.units * sizeof(uint32_t));
+    }
+    return p;
+  }
+  if (k == kMid) {
+    // Dense epilogues only (mid_ways).
+    if (swiglu) return p;
+    const nvfp4::TileShape ts = nvfp4::mid_shape(M, N);
+    const int64_t ks = mid_ways(M, N, K);
+    if (ks > 1) {
+      p.ways = (int)ks;
+      p.units = ts.units;
+      p.part_bytes = align256((size_t)(ts.units * ks * ts.tile_floats) * sizeof(float));
       p.counter_bytes = align256((size_t)ts.units * sizeof(uint32_t));
     }
     return p;
@@ -717,7 +758,7 @@ static int mlp_forward_impl(int mode, const uint16_t* x, int64_t M, int64_t H, i
     return fail(NVFP4_ERR_INVALID_ARG, "buffers must be 16-byte aligned");
   if (use_scratch) {
     const int kmode = (mode == NVFP4_MODE_W4A16 || mode == NVFP4_MODE_W4A16_AWQ) ? NVFP4_MODE_W4A16 : NVFP4_MODE_W4A4;
-    const size_t need = mlp_path_bytes(mode, M, H, I, choose_path(kmode, M, true), choose_path(kmode, M, false));
+    const size_t need = mlp_path_bytes(mode, M, H, I, choose_path(kmode, M, true), choose_path_down(kmode, M, H, I));
     if (need > NVFP4_NOALLOC_SCRATCH_BYTES)
       return fail(NVFP4_ERR_INVALID_ARG,
                   "mlp_forward_noalloc: M=%lld H=%lld I=%lld needs %zu bytes of workspace, more than the %zu of the "
@@ -741,7 +782,7 @@ static int mlp_forward_impl(int mode, const uint16_t* x, int64_t M, int64_t H, i
   if (dyn) mode = NVFP4_MODE_W4A4;  // the W4A4 kernels, x quantized per token
   if (mode == NVFP4_MODE_W4A16_AWQ) mode = NVFP4_MODE_W4A16;  // the W4A16 kernels on pre-scaled inputs
   const int path = choose_path(mode, M, true);  // the gate_up GEMM's (and decode checks')
-  const int path_d = choose_path(mode, M, false);
+  const int path_d = choose_path_down(mode, M, H, I);
   const int epi_out = out_dtype == NVFP4_DTYPE_F32 ? nvfp4::kOutF32 : nvfp4::kOutBF16;
   uint8_t* base = static_cast<uint8_t*>(ws);
   const size_t m = static_cast<size_t>(M);

@@ -50,8 +50,9 @@ struct GemmArgs {
   const float* g2_inv;       // SwiGLU + NVFP4 output only
   void* out;                 // [M, N] dense, or h [M, I] (dense or codes)
   uint8_t* out_scales;       // h scales [M, I/16]
-  // Split-K (weight-streaming kernel: dense epilogues; tiled kernels: any
-  // epilogue, on the tiles their launcher splits): ksplit > 1 divides the K
+  // Split-K (weight-streaming and mid-size kernels: dense epilogues; tiled
+  // kernels: any epilogue, on the tiles their launcher splits): ksplit > 1
+  // divides the K
   // tiles over that many workgroups per output tile. Each workgroup stores
   // its partial result tile to part (split tile u, split s at
   // ((u * ksplit + s) * tile_floats)); the last of the ksplit workgroups of
@@ -108,6 +109,7 @@ struct TileShape {
 };
 TileShape stream_shape(int mode, int64_t M, int64_t N);
 TileShape tiled16_shape(int64_t M, int64_t N);
+TileShape mid_shape(int64_t M, int64_t N);
 
 // The number of K splits that brings a dense GEMM of `units` output tiles to
 // about `target` workgroups, each split keeping at least `min_tiles` tiles.

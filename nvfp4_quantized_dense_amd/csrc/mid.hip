@@ -21,7 +21,12 @@
 //
 // Token rows past M lie past the end of the activation buffers and load as
 // zeros; row groups past N are clamped to the last one and never stored. A
-// grouped GEMM runs all its experts in one launch (grid y).
+// grouped GEMM runs all its experts in one launch (grid y). With a dense
+// epilogue the K tiles of an output tile may be split over several
+// workgroups (GemmArgs.ksplit, partial sums in the caller's workspace, added
+// in split order by the last workgroup of the tile): mlp_forward's down
+// projection, whose few output row tiles (hidden / 128) would otherwise
+// leave most CUs idle.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -167,10 +172,11 @@ __device__ __forceinline__ void mid_compute(f32x4 (&acc)[2][TG], const MidLoad<M
 #endif  // __HIP_DEVICE_COMPILE__
 
 // Grid: 8 * per_xcd workgroups over n_tiles x m_tiles output tiles (128
-// rows x 64 tokens). Workgroup ids are dealt round-robin to the 8 XCDs, so
-// logical workgroup f = (id % 8) * per_xcd + id / 8 takes tile (f / m_tiles,
-// f % m_tiles): the token tiles of one weight tile run side by side on one
-// XCD and read its weight through the same L2; f >= tiles exits. (8-wave workgroups whose two
+// rows x 16 TG tokens), times the K splits. Workgroup ids are dealt
+// round-robin to the 8 XCDs, so logical workgroup f = (id % 8) * per_xcd +
+// id / 8 takes token tile f % m_tiles of its weight tile and split: the
+// token tiles of one weight tile run side by side on one XCD and read its
+// weight through the same L2; f >= tiles * splits exits. (8-wave workgroups whose two
 // halves take alternate K tiles, adding their partial sums in LDS at the
 // end, measured slower: gate_up at 64 tokens, hidden 7168, 68.9 against
 // 67.2 us.)
@@ -181,17 +187,25 @@ __global__ __launch_bounds__(kMidWaves * 64, 2) void k_mid(GemmArgs args_in, int
   __shared__ __attribute__((aligned(16))) uint8_t img[2][TG * 16 * kMidRowBytes];
   GemmArgs args = args_in;
   clear_words(args.zero_ptr, args.zero_n);
+  // Dense epilogues may split K over ks workgroups per output tile; logical
+  // workgroup f takes token tile f % m_tiles of split (f / m_tiles) % ks of
+  // weight tile f / (m_tiles * ks), so the token tiles that read the same
+  // weight bytes stay neighbours.
+  const int ks = EpiTraits<EPI>::swiglu ? 1 : args.ksplit;
   const int64_t id = blockIdx.x;
   const int64_t f = (id & 7) * per_xcd + (id >> 3);
-  if (f >= tiles) return;
+  if (f >= tiles * ks) return;
   if (args.experts > 1) expert_slice(args, blockIdx.y);  // grouped GEMM: grid y walks the experts
-  const int64_t n_tile = f / m_tiles, m_tile = f - n_tile * m_tiles;
+  const int64_t m_tile = f % m_tiles, rest = f / m_tiles;
+  const int split = (int)(rest % ks);
+  const int64_t n_tile = rest / ks;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int q = lane >> 4, tl = lane & 15;
   // Valid token rows: M, or an expert's masked_m (rows past it read as
   // zeros and are not stored; a token tile wholly past it has no work).
   const int64_t M = valid_rows(args), N = args.N, K = args.K, T = K / kTileK;
+  const int64_t per = (T + ks - 1) / ks, t0 = split * per, t1 = t0 + per < T ? t0 + per : T;  // this split's K tiles
   const int64_t ngroups = N / kTileRows;
   const int64_t rg = n_tile * 8 + 2 * wave;  // this wave's first row group
   const int64_t tok0 = m_tile * 16 * TG;
@@ -229,17 +243,26 @@ __global__ __launch_bounds__(kMidWaves * 64, 2) void k_mid(GemmArgs args_in, int
   // t % 2 for K tile t + 2). (Loads two K tiles ahead, in three register
   // sets, measured slower: 242 against 176 VGPRs.)
   MidLoad<MODE> cur, nxt;
-  mid_load(cur, w, a, s, gbase, a_lane, s_lane, 0, T, lane);
-  mid_load(nxt, w, a, s, gbase, a_lane, s_lane, 1, T, lane);
+  mid_load(cur, w, a, s, gbase, a_lane, s_lane, t0, t1, lane);
+  mid_load(nxt, w, a, s, gbase, a_lane, s_lane, t0 + 1, t1, lane);
   if (puts) mid_put(img[0], cur, wave, lane);
   __syncthreads();
-  for (int64_t t = 0; t < T; ++t) {
-    const int b = (int)(t & 1);
+  for (int64_t t = t0; t < t1; ++t) {
+    const int b = (int)((t - t0) & 1);
     mid_compute<MODE, TG>(acc, cur, img[b], lane);
-    if (puts && t + 1 < T) mid_put(img[b ^ 1], nxt, wave, lane);
+    if (puts && t + 1 < t1) mid_put(img[b ^ 1], nxt, wave, lane);
     cur = nxt;
-    mid_load(nxt, w, a, s, gbase, a_lane, s_lane, t + 2, T, lane);
+    mid_load(nxt, w, a, s, gbase, a_lane, s_lane, t + 2, t1, lane);
     __syncthreads();
+  }
+
+  if constexpr (!EpiTraits<EPI>::swiglu) {
+    if (ks > 1) {
+      __shared__ uint32_t arrived;
+      if (!wg_splitk_last<2, TG, kMidWaves * 64>(acc, args.part, args.counters, ks, n_tile * m_tiles + m_tile,
+                                                 split, (int)threadIdx.x, &arrived))
+        return;
+    }
   }
 
 #pragma unroll
@@ -263,7 +286,7 @@ template <int MODE, int EPI, int TG>
 static hipError_t mid_launch_tg(const GemmArgs& a, hipStream_t s) {
   const int64_t m_tiles = (a.M + 16 * TG - 1) / (16 * TG);
   const int64_t tiles = (a.N / kTileRows + 7) / 8 * m_tiles;
-  const int64_t per_xcd = (tiles + 7) / 8;
+  const int64_t per_xcd = (tiles * (a.ksplit > 1 ? a.ksplit : 1) + 7) / 8;
   const unsigned ex = a.experts > 1 ? (unsigned)a.experts : 1u;
   k_mid<MODE, EPI, TG><<<dim3((unsigned)(8 * per_xcd), ex), kMidWaves * 64, 0, s>>>(a, m_tiles, tiles, per_xcd);
   return hipGetLastError();
@@ -274,13 +297,25 @@ static hipError_t mid_launch_tg(const GemmArgs& a, hipStream_t s) {
 // 192 tokens, hidden 7168, 97.0 / 119.9 / 121.8 us with 64-token tiles
 // against 71.2 / 98.1 / 113.9; at 64 / 256 / 512 tokens the 64-token tiles
 // win (64.4 / 152.0 / 274.4 against 71.0 / 163.2 / 293.0 us).
-template <int MODE, int EPI>
-static hipError_t mid_launch(const GemmArgs& a, hipStream_t s) {
-  const int64_t pad48 = (a.M + 47) / 48 * 48, pad64 = (a.M + 63) / 64 * 64;
-  return pad48 <= pad64 ? mid_launch_tg<MODE, EPI, 3>(a, s) : mid_launch_tg<MODE, EPI, 4>(a, s);
+static int mid_tg(int64_t M) {
+  const int64_t pad48 = (M + 47) / 48 * 48, pad64 = (M + 63) / 64 * 64;
+  return pad48 <= pad64 ? 3 : 4;
 }
 
-bool mid_supported(const GemmArgs& a) { return a.ksplit == 1; }
+template <int MODE, int EPI>
+static hipError_t mid_launch(const GemmArgs& a, hipStream_t s) {
+  return mid_tg(a.M) == 3 ? mid_launch_tg<MODE, EPI, 3>(a, s) : mid_launch_tg<MODE, EPI, 4>(a, s);
+}
+
+// Output tiles of the mid-size kernel and the floats of one tile's partial
+// sums in a K split (256 threads x 2 row groups x TG token groups x 4).
+TileShape mid_shape(int64_t M, int64_t N) {
+  const int tg = mid_tg(M);
+  return TileShape{(N / kTileRows + 7) / 8 * ((M + 16 * tg - 1) / (16 * tg)), 2048 * tg, kMidWaves};
+}
+
+// K splits run for dense epilogues of one-expert GEMMs only.
+bool mid_supported(const GemmArgs& a) { return a.ksplit == 1 || a.experts <= 1; }
 
 template <int MODE>
 static hipError_t mid_launch_m(int epi, const GemmArgs& a, hipStream_t s) {
@@ -301,6 +336,8 @@ static hipError_t mid_launch_m(int epi, const GemmArgs& a, hipStream_t s) {
 hipError_t launch_mid_gemm(int mode, int epi, const GemmArgs& a, hipStream_t s) {
   if (a.M == 0) return hipSuccess;
   if (!mid_supported(a)) return hipErrorInvalidValue;
+  if (a.ksplit > 1 && (epi != kOutF32 && epi != kOutBF16)) return hipErrorInvalidValue;
+  if (a.ksplit > 1 && (a.part == nullptr || a.counters == nullptr)) return hipErrorInvalidValue;
   return mode == kW4A4 ? mid_launch_m<kW4A4>(epi, a, s) : mid_launch_m<kW4A16>(epi, a, s);
 }
 

@@ -21,9 +21,23 @@ namespace nvfp4 {
 // where the grid has several token-group rows (down projection at 32
 // tokens, intermediate 17408: 42.9 -> 29.7 us), 2 up to 16 (4 took 28.7
 // against 23.1 us at 16 tokens and was slower at 2 and 4).
-inline int stream_groups(int mode, bool swiglu, int64_t M, int64_t N) {
+//
+// W4A16 dense above 16 tokens with a grid of more than one workgroup per CU
+// (256) at 4 groups (a W4A16 workgroup takes one token group, so the grid
+// is N / 16 / g x token groups): the fewest of 5, 7 or 8 groups that divide
+// N / 16 and fit one round. The down projection at 49-64 tokens, hidden
+// 5120 (320 row groups x 4 token groups) runs 256 workgroups of 5 groups
+// instead of 320 of 4, of which 64 CUs took two.
+inline int stream_groups(int mode, bool swiglu, int64_t M, int64_t N, int64_t experts = 1) {
   int g = mode == kW4A16 && (swiglu ? M > 8 : M > 16) ? 4 : 2;
   while (g > (swiglu ? 2 : 1) && (N / 16) % g != 0) g /= 2;
+  if (mode == kW4A16 && !swiglu && M > 16 && experts <= 1) {
+    const int64_t rg = N / 16, tg = (M + 15) / 16;
+    if (rg / g * tg > 256) {
+      for (const int h : {5, 7, 8})
+        if (rg % h == 0 && rg / h * tg <= 256) return h;
+    }
+  }
   return g;
 }
 

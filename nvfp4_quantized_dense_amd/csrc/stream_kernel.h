@@ -297,14 +297,23 @@ static hipError_t launch_nt(const GemmArgs& a, hipStream_t s) {
   if constexpr (NT == 1) {
     constexpr int kNW = MODE == kW4A16 && sw ? 4 : 8;
     if constexpr (MODE == kW4A4 && sw) {
-      if (a.M > 8 && stream_groups(MODE, sw, a.M, a.N) == 2) return launch_nt_nw<MODE, EPI, NT, 4, 2>(a, s);
+      if (a.M > 8 && stream_groups(MODE, sw, a.M, a.N, a.experts) == 2) return launch_nt_nw<MODE, EPI, NT, 4, 2>(a, s);
     }
-    switch (stream_groups(MODE, sw, a.M, a.N)) {
+    switch (stream_groups(MODE, sw, a.M, a.N, a.experts)) {
       case 1:
         if constexpr (!sw) return launch_nt_nw<MODE, EPI, NT, 8, 1>(a, s);
         break;
       case 2: return launch_nt_nw<MODE, EPI, NT, kNW, 2>(a, s);
       case 4: return launch_nt_nw<MODE, EPI, NT, kNW, 4>(a, s);
+      case 5:
+        if constexpr (MODE == kW4A16 && !sw) return launch_nt_nw<MODE, EPI, NT, kNW, 5>(a, s);
+        break;
+      case 7:
+        if constexpr (MODE == kW4A16 && !sw) return launch_nt_nw<MODE, EPI, NT, kNW, 7>(a, s);
+        break;
+      case 8:
+        if constexpr (MODE == kW4A16 && !sw) return launch_nt_nw<MODE, EPI, NT, kNW, 8>(a, s);
+        break;
     }
     return hipErrorInvalidValue;
   }

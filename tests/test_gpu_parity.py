@@ -370,6 +370,38 @@ def test_mlp_auto_dispatch(M):
     _check_mlp("w4a16", M, 512, 768, seed=M)
 
 
+# Shapes where the automatic path takes the workspace-split down projection
+# of the mid-size kernel (W4A4 from 17 tokens, W4A16 from 65 to 192, where
+# hidden / 128 x token tiles <= 256 and K splits into parts of at least 8 K
+# tiles: intermediate 6400 gives 3 splits of 9, 9 and 7 K tiles, 4096 two
+# of 8), and where the W4A16 down projection streams through 5 or 7 row
+# groups per workgroup (hidden 5120 / 7168 at 49-64 tokens: 4 groups would
+# overfill one round of workgroups).
+@pytest.mark.parametrize("mode,M,H,I", [("w4a4", 17, 2048, 6400), ("w4a4", 48, 2048, 6400),
+                                        ("w4a4", 100, 2048, 6400), ("w4a4", 200, 1024, 6400),
+                                        ("w4a4", 256, 1024, 4096), ("w4a16", 80, 1024, 4096),
+                                        ("w4a16", 150, 1024, 6400), ("w4a16", 56, 5120, 512),
+                                        ("w4a16", 64, 7168, 512)])
+def test_mlp_auto_split_down(mode, M, H, I):
+    nv.set_path(nv.PATH_AUTO)
+    _check_mlp(mode, M, H, I, seed=M + H)
+
+
+@pytest.mark.parametrize("N,M", [(5120, 56), (5120, 80), (7168, 40), (7168, 64)])
+def test_gemm_w4a16_one_round_groups(N, M):
+    """W4A16 dense GEMMs whose streaming grid takes 5, 8, 7 and 7 row groups
+    per workgroup (one round of at most 256 workgroups)."""
+    nv.set_path(nv.PATH_AUTO)
+    rng = np.random.default_rng(N + M)
+    K = 512
+    wc, ws = rand_nvfp4(rng, N, K)
+    p = nv.nvfp4_repack_weight(0, to_dev(wc), to_dev(ws))
+    alpha = np.float32(0.0173)
+    x = synth.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    y = nv.nvfp4_gemm(1, to_dev(x), None, p, N, K, scalar(alpha))
+    gemm_close(to_host(y), oracle.gemm_w4a16(x, wc, ws, alpha), f"w4a16 one-round N={N} M={M}")
+
+
 def test_mlp_decode_full_size():
     """Decode W4A4: M=1, hidden 5120, intermediate 17408, outliers; every 50th
     of the 1000 seeded inputs the decode benchmark cycles through, and the
@@ -405,8 +437,8 @@ def test_mlp_small_batch_full_size(M):
 
 
 # -- mlp_forward workspace use: split-K of the down projection (weight-
-# streaming kernel; W4A16 tiled kernel) and the decode GEMV's in-kernel
-# activation quantization
+# streaming, mid-size and W4A16 tiled kernels) and the decode GEMV's
+# in-kernel activation quantization
 #
 # Hidden 512 leaves 32 output row groups, so the streaming kernel splits
 # the down projection's K (intermediate) over several workgroups: 27 tiles
@@ -423,9 +455,8 @@ def test_mlp_small_batch_full_size(M):
                                        ("mid", 100, 512), ("mid", 64, 2048), ("mid", 200, 2048)])
 @pytest.mark.parametrize("mode", ["w4a4", "w4a16"])
 def test_mlp_split_k(mode, kpath, M, H, I):
-    """(The mid-size kernel does not split K; its cases run the forward with
-    it on the gate_up and the down projection through the dirty, reused
-    workspace all the same.)"""
+    """(The mid-size kernel splits K for the dense down projection only: 3
+    or 4 ways at these shapes, unevenly at 6912; its gate_up runs unsplit.)"""
     prev = nv.set_path(PATHS[kpath])
     try:
         w = mlp_weights(H, I, 0)
