@@ -108,7 +108,11 @@ size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 // (80: 233 against 274 us, hidden 7168; 128: 206 against 228 us, hidden
 // 5120, a tie at 7168) and loses from 144 (349 against 279 us); W4A16
 // streaming wins up to 48 (117 against 122 us) and loses at 56 (148 against
-// 124 us) to the 128-token tiled kernel.
+// 124 us) to the 128-token tiled kernel. W4A16 dense GEMMs, whose
+// streaming grids fill one round with 5, 7 or 8 row groups per workgroup
+// (stream_groups), stream up to 96 tokens: the forward at 49 / 64 / 72 / 96
+// tokens, hidden 5120, 116.5 / 118.3 / 122.2 / 123.6 us with a tiled down
+// projection against 95.3 / 96.3 / 119.7 / 121.5 streaming.
 int64_t stream_max_m(int mode, bool swiglu) { return mode == NVFP4_MODE_W4A4 ? 128 : swiglu ? 48 : 96; }
 
 // Largest tokens per expert a grouped GEMM runs as one streaming launch
