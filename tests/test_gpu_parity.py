@@ -679,6 +679,53 @@ def test_mlp_decode_graph_capture(mode):
         gemm_close(eager, r["out"], f"eager mode {mode}")
 
 
+@pytest.mark.parametrize("mode,M", [(0, 64), (0, 128), (1, 100)])
+def test_mlp_split_down_graph_replay(mode, M):
+    """The forward with its down projection K-split on the mid-size kernel
+    (hidden 2048, intermediate 6400: 3 splits), captured in a graph and
+    replayed on three inputs, eager forwards between the replays: every
+    replay equals the eager forward bit for bit (the split counters are
+    cleared by the gate_up launch and left at zero, no memset in the graph)."""
+    nv.set_path(nv.PATH_AUTO)
+    H, I = 2048, 6400
+    w = mlp_weights(H, I, 0)
+    p_gu, p_d = packed_weights(H, I, 0)
+    xs = [synth.activations(11 + k, M, H) for k in range(3)]
+    if mode == 0:
+        sc = calibrate_activation_scales(xs[0], w)
+        args = (0, to_dev(xs[0]), p_gu, scalar(sc["a_gu"]), p_d, scalar(sc["a_d"]), I)
+        gkw = dict(g1_inv=scalar(sc["g1_inv"]), g2_inv=scalar(sc["g2_inv"]))
+    else:
+        sc = None
+        args = (1, to_dev(xs[0]), p_gu, scalar(w["g_gu"]), p_d, scalar(w["g_d"]), I)
+        gkw = {}
+    xd = args[1]
+    nws = nv.mlp_workspace_bytes(mode, M, H, I)
+    ws = torch.full((nws,), 0xFF, dtype=torch.uint8, device=dev())
+    out = torch.empty((M, H), dtype=torch.float32, device=dev())
+    call = lambda: nv.mlp_forward(*args, ws=ws, out=out, **gkw)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call()  # warm-up outside the graph
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for k, x in enumerate(xs + xs[:1]):
+        xd.copy_(to_dev(x))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        y_graph = to_host(out)
+        eager = to_host(nv.mlp_forward(*args, ws=torch.full_like(ws, 0xFF), **gkw))
+        torch.cuda.synchronize()
+        assert np.array_equal(y_graph, eager), f"replay {k} differs from the eager forward"
+        if k == 0:
+            r = _decode_ref(mode, x, w, sc)
+            gemm_close(y_graph, r["out"], f"split-down graph mode {mode} M={M}")
+
+
 def test_swiglu_fused_requant_prefill_sampled_rows():
     """The fused gate_up + SwiGLU + NVFP4 kernel at the prefill shape (8192
     tokens, hidden 7168, intermediate 18432: the tiled kernel) against the
