@@ -162,20 +162,21 @@ int choose_path(int mode, int64_t M, bool swiglu) {
   return NVFP4_PATH_TILED;
 }
 
-// K splits of a dense GEMM on the mid-size kernel: as many as bring the grid
-// to about two workgroups per CU (its occupancy at 64-token tiles), at most
-// 8, every split non-empty and at least 8 K tiles long.
-int64_t mid_ways(int64_t M, int64_t N, int64_t K) {
-  const int64_t units = nvfp4::mid_shape(M, N).units, T = K / 256;
+// K splits of a dense GEMM on the mid-size kernels: as many as bring the
+// grid to about two workgroups per CU (their occupancy), at most 8, every
+// split non-empty and at least 8 K tiles long.
+int64_t mid_ways(int mode, int64_t M, int64_t N, int64_t K) {
+  const int64_t units = nvfp4::mid_shape(mode, M, N).units, T = K / 256;
   int64_t ks = std::min<int64_t>(2 * nvfp4::kTiledSlots / std::max<int64_t>(units, 1), 8);
   while (ks > 1 && ((ks - 1) * ((T + ks - 1) / ks) >= T || (T + ks - 1) / ks < 8)) --ks;
   return std::max<int64_t>(ks, 1);
 }
 
 // Path of mlp_forward's down projection (a dense GEMM that can split K
-// through the workspace): the mid-size kernel wherever it K-splits (at
-// most 256 output tiles of 128 rows x 48 or 64 tokens), W4A4 from 17
-// tokens and W4A16 from 65 to 192, else as choose_path. The W4A4 forward
+// through the workspace): the mid-size kernels wherever they K-split (at
+// most 256 output tiles of 128 rows x 48 or 64 tokens, or W4A4 x 128
+// tokens where the smaller tiles are more), W4A4 from 17 tokens and W4A16
+// from 65 to 192, else as choose_path. The W4A4 forward
 // at hidden 7168 / 5120 (same box, same run): 17 tokens 69.1 / 57.7 -> 67.3
 // / 56.4 us, 64: 109.4 / 90.1 -> 102.6 / 83.8, 96: 144.2 -> 118.6 (7168),
 // 128: 179.0 / 148.3 -> 153.6 / 114.9, 256: 258.7 / 213.8 -> 246.8 / 177.3,
@@ -186,7 +187,7 @@ int64_t mid_ways(int64_t M, int64_t N, int64_t K) {
 // 98.4 us at 49), at 256-320 the tiled kernel (174.2 against 177.2 at 256).
 int choose_path_down(int mode, int64_t M, int64_t H, int64_t I) {
   const bool mid = mode == NVFP4_MODE_W4A4 ? M >= 17 : (M >= 65 && M <= 192);
-  if (g_path == NVFP4_PATH_AUTO && mid && mid_ways(M, H, I) > 1) return NVFP4_PATH_MID;
+  if (g_path == NVFP4_PATH_AUTO && mid && mid_ways(mode, M, H, I) > 1) return NVFP4_PATH_MID;
   return choose_path(mode, M, false);
 }
 
@@ -315,8 +316,8 @@ SplitPlan split_plan(Kernel k, int mode, int64_t M, int64_t N, int64_t K, bool s
   if (k == kMid) {
     // Dense epilogues only (mid_ways).
     if (swiglu) return p;
-    const nvfp4::TileShape ts = nvfp4::mid_shape(M, N);
-    const int64_t ks = mid_ways(M, N, K);
+    const nvfp4::TileShape ts = nvfp4::mid_shape(mode, M, N);
+    const int64_t ks = mid_ways(mode, M, N, K);
     if (ks > 1) {
       p.ways = (int)ks;
       p.units = ts.units;

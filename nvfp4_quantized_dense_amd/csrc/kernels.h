@@ -109,7 +109,7 @@ struct TileShape {
 };
 TileShape stream_shape(int mode, int64_t M, int64_t N);
 TileShape tiled16_shape(int64_t M, int64_t N);
-TileShape mid_shape(int64_t M, int64_t N);
+TileShape mid_shape(int mode, int64_t M, int64_t N);  // dense epilogue, one expert
 
 // The number of K splits that brings a dense GEMM of `units` output tiles to
 // about `target` workgroups, each split keeping at least `min_tiles` tiles.

@@ -282,6 +282,193 @@ __global__ __launch_bounds__(kMidWaves * 64, 2) void k_mid(GemmArgs args_in, int
 #endif  // __HIP_DEVICE_COMPILE__
 }
 
+// ---------------------------------------------------------------------------
+// 128-token tiles (W4A4, dense epilogues): the layout of k_mid with 8 token
+// groups, the activation staged per 128-column half of a K tile so that an
+// image of 128 tokens fits 32 KB and two of them (double buffer) keep two
+// workgroups per CU; each wave puts two token groups and multiplies its two
+// weight fragments against 8 token fragments per step. It serves the K-split
+// down projection of mlp_forward where 48- or 64-token tiles would leave
+// more output tiles than two per CU and no room to split K.
+// (As the gate_up kernel it measured slower than 64-token tiles at every
+// token count: 177.3 against 151.4 us at 256 tokens, 268.9 against 260.2 at
+// 512, hidden 7168.)
+#if defined(__HIP_DEVICE_COMPILE__)
+namespace {
+constexpr int kHalfRowBytes = 256;  // one token's 128 f16 columns
+
+struct MidLoad8 {
+  u32x4 wc[2];     // this half of the wave's two weight tiles
+  uint32_t wsd[2];
+  u32x4 xc[2];     // this half of the wave's two token groups
+  uint32_t xs[2];
+};
+
+// Half h of the K range (K tile h / 2, columns 128 (h % 2)..); h >= h_end:
+// out of range (zeros, no memory access).
+__device__ __forceinline__ void mid8_load(MidLoad8& d, Rsrc w, Rsrc a, Rsrc s, const uint32_t (&gbase)[2],
+                                          const uint32_t (&a_lane)[2], const uint32_t (&s_lane)[2], int64_t h,
+                                          int64_t h_end, int lane) {
+  const bool in = h < h_end;
+  const int64_t t = h >> 1;
+  const int c = (int)(h & 1);
+  const uint32_t tw = in ? (uint32_t)(t * kTileBytes) : kOutOfRange;
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    d.wc[g] = bload16_nt(w, tw + 1024 * c + 16 * lane, gbase[g]);
+    d.wsd[g] = bload4_nt(w, tw + kTileCodeBytes + 4 * lane, gbase[g]);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    d.xc[i] = bload16(a, in ? a_lane[i] + (uint32_t)(t * 128 + 64 * c) : kOutOfRange);
+    d.xs[i] = bload2(s, in ? s_lane[i] + (uint32_t)(t * 16 + 8 * c) : kOutOfRange);
+  }
+}
+
+__device__ __forceinline__ void mid8_put(uint8_t* img, const MidLoad8& d, int wave, int lane) {
+  const int q = lane >> 4, tl = lane & 15;
+  const int key = mid_key(tl);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    uint8_t* row = img + (16 * (2 * wave + i) + tl) * kHalfRowBytes;
+    const f16x2 sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d.xs[i], 1.0f, false);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const _Float16 sv = (u >> 1) ? sc.y : sc.x;
+      *reinterpret_cast<f16x8*>(row + 16 * ((4 * q + u) ^ key)) = deq8_f16(d.xc[i][u], sv);
+    }
+  }
+}
+
+__device__ __forceinline__ void mid8_compute(f32x4 (&acc)[2][8], const MidLoad8& d, const uint8_t* img, int c,
+                                             int lane) {
+  const int q = lane >> 4, tl = lane & 15;
+  const int key = mid_key(tl);
+  _Float16 ws[2][2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const f16x2 v = c ? __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d.wsd[g], 1.0f, true)
+                      : __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(d.wsd[g], 1.0f, false);
+    ws[g][0] = v.x; ws[g][1] = v.y;
+  }
+  const uint8_t* row = img + tl * kHalfRowBytes;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int off = 16 * ((4 * q + u) ^ key);
+    f16x8 B[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) B[j] = *reinterpret_cast<const f16x8*>(row + j * 16 * kHalfRowBytes + off);
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const f16x8 A = deq8_f16(d.wc[g][u], ws[g][u >> 1]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[g][j] = mfma16x16x32(A, B[j], acc[g][j]);
+    }
+  }
+}
+}  // namespace
+#endif  // __HIP_DEVICE_COMPILE__
+
+template <int EPI>
+__global__ __launch_bounds__(kMidWaves * 64, 2) void k_mid8(GemmArgs args_in, int64_t m_tiles, int64_t tiles,
+                                                            int64_t per_xcd) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __shared__ __attribute__((aligned(16))) uint8_t img[2][128 * kHalfRowBytes];
+  GemmArgs args = args_in;
+  clear_words(args.zero_ptr, args.zero_n);
+  const int ks = EpiTraits<EPI>::swiglu ? 1 : args.ksplit;
+  const int64_t id = blockIdx.x;
+  const int64_t f = (id & 7) * per_xcd + (id >> 3);
+  if (f >= tiles * ks) return;
+  if (args.experts > 1) expert_slice(args, blockIdx.y);
+  const int64_t m_tile = f % m_tiles, rest = f / m_tiles;
+  const int split = (int)(rest % ks);
+  const int64_t n_tile = rest / ks;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int q = lane >> 4, tl = lane & 15;
+  const int64_t M = valid_rows(args), N = args.N, K = args.K, T = K / kTileK;
+  const int64_t per = (T + ks - 1) / ks, t0 = split * per, t1 = t0 + per < T ? t0 + per : T;
+  const int64_t ngroups = N / kTileRows;
+  const int64_t rg = n_tile * 8 + 2 * wave;
+  const int64_t tok0 = m_tile * 128;
+  if (tok0 >= M) return;
+
+  const Rsrc w = make_rsrc(args.w, (uint32_t)(ngroups * T * kTileBytes));
+  const Rsrc a = make_rsrc(args.a, (uint32_t)(M * (K / 2)));
+  const Rsrc s = make_rsrc(args.a_scales, (uint32_t)(M * (K / 16)));
+  uint32_t gbase[2];
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    const int64_t grp = rg + g < ngroups ? rg + g : ngroups - 1;
+    gbase[g] = __builtin_amdgcn_readfirstlane((uint32_t)(grp * T * kTileBytes));
+  }
+  uint32_t a_lane[2], s_lane[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int64_t trow = tok0 + 16 * (2 * wave + i) + tl;
+    a_lane[i] = (uint32_t)(trow * (K / 2) + 16 * q);
+    s_lane[i] = (uint32_t)(trow * (K / 16) + 2 * q);
+  }
+  const float alpha = uniform_now(args.alpha);
+  const float g2i = EPI == kSwigluNvfp4 ? uniform_now(args.g2_inv) : 0.0f;
+
+  f32x4 acc[2][8];
+#pragma unroll
+  for (int g = 0; g < 2; ++g)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[g][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int64_t h0 = 2 * t0, h1 = 2 * t1;
+  MidLoad8 cur, nxt;
+  mid8_load(cur, w, a, s, gbase, a_lane, s_lane, h0, h1, lane);
+  mid8_load(nxt, w, a, s, gbase, a_lane, s_lane, h0 + 1, h1, lane);
+  mid8_put(img[0], cur, wave, lane);
+  __syncthreads();
+  for (int64_t h = h0; h < h1; ++h) {
+    const int b = (int)((h - h0) & 1);
+    mid8_compute(acc, cur, img[b], (int)(h & 1), lane);
+    if (h + 1 < h1) mid8_put(img[b ^ 1], nxt, wave, lane);
+    cur = nxt;
+    mid8_load(nxt, w, a, s, gbase, a_lane, s_lane, h + 2, h1, lane);
+    __syncthreads();
+  }
+
+  if constexpr (!EpiTraits<EPI>::swiglu) {
+    if (ks > 1) {
+      __shared__ uint32_t arrived;
+      if (!wg_splitk_last<2, 8, kMidWaves * 64>(acc, args.part, args.counters, ks, n_tile * m_tiles + m_tile,
+                                                split, (int)threadIdx.x, &arrived))
+        return;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int64_t token = tok0 + 16 * j + tl;
+    const bool tv = token < M;
+    const float at = row_alpha(alpha, args.row_scale, tv, token);
+    if constexpr (EpiTraits<EPI>::swiglu) {
+      store_swiglu<EPI>(acc[0][j], acc[1][j], at, g2i, tv && rg < ngroups, token, (rg >> 1) * kTileRows, lane,
+                        N / 2, args.out, args.out_scales, args.h_prescale);
+    } else {
+#pragma unroll
+      for (int g = 0; g < 2; ++g)
+        store_dense<EPI>(acc[g][j], at, tv && rg + g < ngroups, token, (rg + g) * kTileRows + 4 * q, N, args.out);
+    }
+  }
+#endif  // __HIP_DEVICE_COMPILE__
+}
+
+template <int EPI>
+static hipError_t mid8_launch(const GemmArgs& a, hipStream_t s) {
+  const int64_t m_tiles = (a.M + 127) / 128;
+  const int64_t tiles = (a.N / kTileRows + 7) / 8 * m_tiles;
+  const int64_t per_xcd = (tiles * (a.ksplit > 1 ? a.ksplit : 1) + 7) / 8;
+  const unsigned ex = a.experts > 1 ? (unsigned)a.experts : 1u;
+  k_mid8<EPI><<<dim3((unsigned)(8 * per_xcd), ex), kMidWaves * 64, 0, s>>>(a, m_tiles, tiles, per_xcd);
+  return hipGetLastError();
+}
+
 template <int MODE, int EPI, int TG>
 static hipError_t mid_launch_tg(const GemmArgs& a, hipStream_t s) {
   const int64_t m_tiles = (a.M + 16 * TG - 1) / (16 * TG);
@@ -297,20 +484,36 @@ static hipError_t mid_launch_tg(const GemmArgs& a, hipStream_t s) {
 // 192 tokens, hidden 7168, 97.0 / 119.9 / 121.8 us with 64-token tiles
 // against 71.2 / 98.1 / 113.9; at 64 / 256 / 512 tokens the 64-token tiles
 // win (64.4 / 152.0 / 274.4 against 71.0 / 163.2 / 293.0 us).
-static int mid_tg(int64_t M) {
+// Token groups per tile: 3 or 4 as above, except for one-expert W4A4 GEMMs
+// with a dense epilogue whose 48- or 64-token grid has more than 256 tiles
+// (two per CU, so no room for a K split): 8 (k_mid8). The forward at hidden
+// 7168 / 5120 (same box, same run): 257 tokens 306.6 -> 274.6 us (7168),
+// 320: 329.6 -> 294.2 (7168), 384: 357.1 / 262.6 -> 326.6 / 233.7, 512:
+// 424.9 / 314.2 -> 422.0 / 299.1; where the smaller tiles still split, they
+// win (257 tokens at 5120: 187.8 against 198.8 us).
+static int mid_tg(int mode, bool dense, int64_t M, int64_t N, int experts) {
   const int64_t pad48 = (M + 47) / 48 * 48, pad64 = (M + 63) / 64 * 64;
-  return pad48 <= pad64 ? 3 : 4;
+  const int tg = pad48 <= pad64 ? 3 : 4;
+  if (mode == kW4A4 && dense && experts <= 1 &&
+      (N / kTileRows + 7) / 8 * ((M + 16 * tg - 1) / (16 * tg)) > 256)
+    return 8;
+  return tg;
 }
 
 template <int MODE, int EPI>
 static hipError_t mid_launch(const GemmArgs& a, hipStream_t s) {
-  return mid_tg(a.M) == 3 ? mid_launch_tg<MODE, EPI, 3>(a, s) : mid_launch_tg<MODE, EPI, 4>(a, s);
+  const int tg = mid_tg(MODE, !EpiTraits<EPI>::swiglu, a.M, a.N, a.experts);
+  if constexpr (MODE == kW4A4 && !EpiTraits<EPI>::swiglu) {
+    if (tg == 8) return mid8_launch<EPI>(a, s);
+  }
+  return tg == 3 ? mid_launch_tg<MODE, EPI, 3>(a, s) : mid_launch_tg<MODE, EPI, 4>(a, s);
 }
 
-// Output tiles of the mid-size kernel and the floats of one tile's partial
-// sums in a K split (256 threads x 2 row groups x TG token groups x 4).
-TileShape mid_shape(int64_t M, int64_t N) {
-  const int tg = mid_tg(M);
+// Output tiles of a one-expert dense GEMM on the mid-size kernels and the
+// floats of one tile's partial sums in a K split (256 threads x 2 row
+// groups x TG token groups x 4).
+TileShape mid_shape(int mode, int64_t M, int64_t N) {
+  const int tg = mid_tg(mode, true, M, N, 1);
   return TileShape{(N / kTileRows + 7) / 8 * ((M + 16 * tg - 1) / (16 * tg)), 2048 * tg, kMidWaves};
 }
 

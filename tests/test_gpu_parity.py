@@ -382,12 +382,38 @@ def test_mlp_auto_dispatch(M):
 # overfill one round of workgroups).
 @pytest.mark.parametrize("mode,M,H,I", [("w4a4", 17, 2048, 6400), ("w4a4", 48, 2048, 6400),
                                         ("w4a4", 100, 2048, 6400), ("w4a4", 200, 1024, 6400),
-                                        ("w4a4", 256, 1024, 4096), ("w4a16", 80, 1024, 4096),
+                                        ("w4a4", 256, 1024, 4096), ("w4a4", 300, 1024, 4096),
+                                        ("w4a4", 400, 2048, 6400), ("w4a4", 300, 7168, 4096),
+                                        ("w4a16", 80, 1024, 4096),
                                         ("w4a16", 150, 1024, 6400), ("w4a16", 56, 5120, 512),
                                         ("w4a16", 64, 7168, 512)])
 def test_mlp_auto_split_down(mode, M, H, I):
+    """(At hidden 7168 and 300 tokens the 64-token grid of the W4A4 down
+    projection has 280 tiles, so it takes 128-token tiles, split 2 ways;
+    above 256 tokens the oracle checks 48 sampled rows, the ragged last
+    tile among them.)"""
     nv.set_path(nv.PATH_AUTO)
-    _check_mlp(mode, M, H, I, seed=M + H)
+    rows = None if M <= 256 else np.unique(np.concatenate([np.arange(16), np.arange(M - 16, M),
+                                                           np.random.default_rng(M).choice(M, 16, replace=False)]))
+    _check_mlp(mode, M, H, I, seed=M + H, rows=rows)
+
+
+def test_gemm_w4a4_mid_128_token_tiles():
+    """A one-expert dense W4A4 GEMM under NVFP4_PATH_MID whose 64-token grid
+    would exceed 256 tiles (7168 rows, 300 tokens) runs the 128-token
+    kernel, unsplit (the standalone entry has no workspace)."""
+    prev = nv.set_path(PATHS["mid"])
+    try:
+        rng = np.random.default_rng(300)
+        M, N, K = 300, 7168, 512
+        wc, ws = rand_nvfp4(rng, N, K)
+        p = nv.nvfp4_repack_weight(0, to_dev(wc), to_dev(ws))
+        alpha = np.float32(0.0173)
+        ac, as_ = rand_nvfp4(rng, M, K)
+        y = nv.nvfp4_gemm(0, to_dev(ac), to_dev(as_), p, N, K, scalar(alpha))
+        gemm_close(to_host(y), oracle.gemm_w4a4(ac, as_, wc, ws, alpha), "mid 128-token tiles")
+    finally:
+        nv.set_path(prev)
 
 
 @pytest.mark.parametrize("N,M", [(5120, 56), (5120, 80), (7168, 40), (7168, 64)])
@@ -455,11 +481,13 @@ def test_mlp_small_batch_full_size(M):
 @pytest.mark.parametrize("I", [6912, 8192])
 @pytest.mark.parametrize("kpath,M,H", [("gemv", 1, 512), ("gemv", 2, 512), ("stream", 3, 512), ("stream", 16, 512),
                                        ("stream", 40, 512), ("tiled", 200, 512), ("mid", 64, 512),
-                                       ("mid", 100, 512), ("mid", 64, 2048), ("mid", 200, 2048)])
+                                       ("mid", 100, 512), ("mid", 64, 2048), ("mid", 200, 2048),
+                                       ("mid", 300, 512)])
 @pytest.mark.parametrize("mode", ["w4a4", "w4a16"])
 def test_mlp_split_k(mode, kpath, M, H, I):
-    """(The mid-size kernel splits K for the dense down projection only: 3
-    or 4 ways at these shapes, unevenly at 6912; its gate_up runs unsplit.)"""
+    """(The mid-size kernels split K for the dense down projection only: 3
+    or 4 ways at these shapes, unevenly at 6912, on 128-token tiles at 300
+    tokens in W4A4; the gate_up runs unsplit.)"""
     prev = nv.set_path(PATHS[kpath])
     try:
         w = mlp_weights(H, I, 0)
