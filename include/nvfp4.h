@@ -89,7 +89,8 @@ extern "C" {
                                 paths run only for operands of 2^31 bytes or more (any M; no
                                 split-K; the grouped GEMM treats it as NVFP4_PATH_TILED) */
 #define NVFP4_PATH_MID 5     /* 128 weight rows x 48 or 64 tokens per workgroup (whichever pads M
-                                less; 48 on a tie), the activation brought into LDS once per
+                                less; 48 on a tie; 128 for one-expert W4A4 dense GEMMs whose grid
+                                would exceed 256 tiles), the activation brought into LDS once per
                                 workgroup (any M; chosen for the W4A4 SwiGLU GEMMs of 33 to 512
                                 tokens, the W4A16 SwiGLU GEMMs of 33 to 64 tokens, the W4A4
                                 grouped GEMMs of 64 to 512 tokens per expert, and mlp_forward's
