@@ -158,6 +158,17 @@ def test_mlp_per_token_auto(M):
     _check_mlp_per_token(M, 512, 768, seed=M)
 
 
+@pytest.mark.parametrize("M,H,I", [(64, 2048, 6400), (300, 7168, 4096)])
+def test_mlp_per_token_split_down(M, H, I):
+    """The per-token scales through the K-split down projection of the
+    mid-size kernels: 64-token tiles split 3 ways (64 tokens), 128-token
+    tiles split 2 ways (300 tokens, hidden 7168; 48 sampled rows)."""
+    nv.set_path(nv.PATH_AUTO)
+    rows = None if M <= 64 else np.unique(np.concatenate([np.arange(16), np.arange(M - 16, M),
+                                                           np.random.default_rng(M).choice(M, 16, replace=False)]))
+    _check_mlp_per_token(M, H, I, seed=M + 1, rows=rows, calib_rows=16)
+
+
 @pytest.mark.parametrize("M", [1, 16])
 def test_mlp_per_token_decode_full_size(M):
     """Hidden 5120, intermediate 17408 (with outliers), through the GEMV path."""
