@@ -69,6 +69,38 @@ def test_packed_and_workspace_sizes():
             assert nv.mlp_workspace_bytes(mode, M, 7168, 18432) >= tail(7168, 18432) + M * 7168 // 2
 
 
+def test_workspace_holds_split_down_partials():
+    """The forward's workspace holds the K-split partial tiles and counters of
+    its down projection on the mid-size kernels (host sizing only). Restated
+    plan: tiles of 128 rows x 48, 64 or (one-expert W4A4 dense grids of more
+    than 256 such tiles) 128 tokens; splits = min(8, 512 / tiles), reduced
+    until every split is non-empty and at least 8 K tiles long; a partial
+    tile is 256 threads x 2 row groups x TG token groups x 4 floats."""
+    def a256(v):
+        return (v + 255) // 256 * 256
+
+    def split_bytes(mode, M, H, I):
+        tg = 3 if (M + 47) // 48 * 48 <= (M + 63) // 64 * 64 else 4
+        rows = (H // 16 + 7) // 8
+        if mode == nv.MODE_W4A4 and rows * -(-M // (16 * tg)) > 256:
+            tg = 8
+        units, T = rows * -(-M // (16 * tg)), I // 256
+        ks = min(2 * 256 // units, 8)
+        while ks > 1 and ((ks - 1) * -(-T // ks) >= T or -(-T // ks) < 8):
+            ks -= 1
+        return 0 if ks < 2 else a256(units * ks * 2048 * tg * 4) + a256(units * 4)
+
+    for mode in (nv.MODE_W4A4, nv.MODE_W4A16):
+        for M, H, I in [(17, 7168, 18432), (64, 7168, 18432), (128, 5120, 17408), (300, 7168, 18432),
+                        (384, 5120, 17408), (100, 2048, 6400)]:
+            act = (a256(M * H // 2) + a256(M * H // 16) + a256(M * I // 2) + a256(M * I // 16)
+                   if mode == nv.MODE_W4A4 else a256(M * I * 2))
+            need = act + split_bytes(mode, M, H, I) + (4 << 20)
+            assert nv.mlp_workspace_bytes(mode, M, H, I) >= need, (mode, M, H, I)
+    # the 8-way split of 56 tiles at 64 tokens, hidden 7168: 14.7 MB of partials
+    assert split_bytes(nv.MODE_W4A4, 64, 7168, 18432) == a256(56 * 8 * 8192 * 4) + a256(56 * 4)
+
+
 def test_workspace_status_address():
     lib = nv.lib()
     base = 0x7F0000000000
