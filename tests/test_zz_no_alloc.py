@@ -44,12 +44,14 @@ def _calls(mode, x, w, sc, p_gu, p_d, I):
 
 
 # (mode, H, I, first M, second M): decode-size shapes on the single-launch
-# decode and the streaming kernels; 256 tokens on the tiled kernel with its
-# split-K down projection, at the scratch limit of hidden 7168.
+# decode and the streaming kernels; 64, 256 and 300 tokens with the down
+# projection K-split on the mid-size kernels (8, 2 and 3 ways; 128-token
+# tiles at 300), its partial tiles in the scratch.
 CASES = [
     (0, 5120, 17408, 16, 1),
     (0, 7168, 18432, 64, 1),
     (0, 7168, 18432, 256, 3),
+    (0, 7168, 18432, 300, 17),
     (1, 5120, 17408, 768, 48),
     (1, 5120, 17408, 64, 16),
     (1, 5120, 17408, 16, 1),
